@@ -1,0 +1,44 @@
+"""CPU oracle for the Spense hybrid sparse-dense linear layer.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import this
+package: only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline``
+leg of ``bench.py`` use it.  It shares no code with the HIP library (no
+kernels, headers, tables or helpers); the two meet only through the seeded
+inputs drawn by ``synth``.
+
+Every function here is plain NumPy in float64 (integer work on bit patterns),
+written from the definitions on the pages:
+
+  * "SpenseGPT: Practical One-shot Pruning Enabling Sparse and Dense GEMMs for
+    LLM Inference" (gist.science explainer), Technical Summary 2.A "The Spense
+    Format": each weight matrix is split into a contiguous dense region that
+    keeps its weights and a contiguous 2:4 region; the input-split variant runs
+    the first part of the input through the sparse GEMM and the second through
+    the dense GEMM and accumulates both into one output.
+  * same page, Technical Summary 2.B "Dense Index Selection Strategies":
+    SpenseGPT keeps the last p% of indices dense; SpenseGPT+ keeps a selected
+    index set dense and permutes it into the contiguous dense block.
+  * same page, Technical Summary 1 "Problem Statement" (and the SlideSparse
+    explainer's Technical summary 1): 2:4 means at most two nonzeros in every
+    four consecutive weights.
+
+Parity status: every function is pinned by ``tests/test_oracle.py`` (closed
+forms, exhaustive brute force on tiny inputs, library routines for the
+special cases).  No function is "parity unpinned".
+"""
+
+from .spense import (  # noqa: F401
+    DT_BF16,
+    DT_F32,
+    DT_FP8,
+    DenseSetError,
+    Packed,
+    decode_values,
+    decompress,
+    dense_linear_ref,
+    linear_ref,
+    magnitude_key,
+    pack,
+    resolve_dense_set,
+    unpack_bits,
+)

@@ -1,0 +1,253 @@
+"""Plain NumPy oracle of the Spense linear layer (test infrastructure only).
+
+Notation: W[N,K] weights, X[M,K] activations, D the dense column set with
+K_d = |D| columns, K_s = K - K_d sparse columns, pi the column order
+[sparse columns ascending | dense columns ascending], X' = X[:, pi].
+
+Sources (all on the SpenseGPT gist.science explainer unless noted):
+  * Technical Summary 2.A "The Spense Format": one contiguous dense region
+    plus one contiguous 2:4 region; input-split accumulates the sparse-GEMM and
+    dense-GEMM results into the same output.
+  * Technical Summary 2.B: SpenseGPT keeps the last p% of indices dense;
+    SpenseGPT+ chooses an index set and moves it into the contiguous dense
+    block by a permutation, which leaves the product unchanged.
+  * Technical Summary 1 (and SlideSparse explainer, Technical summary 1):
+    a 2:4 group of four consecutive weights holds at most two nonzeros.
+Readings where the pages are silent (tie-break, metadata encoding, fp8
+magnitude domain, fraction rounding) are the ones listed in the design notes:
+magnitude = stored bit pattern with the sign cleared, equal magnitudes go to
+the lower in-group position, the nibble for a group is i0 | i1 << 2 with
+i0 < i1, eight groups per uint32 word starting at the low nibble, and
+K_d = round-half-away(p * K).
+"""
+
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass
+from typing import Optional
+
+import numpy as np
+
+DT_F32 = 0
+DT_BF16 = 1
+DT_FP8 = 2
+
+
+class DenseSetError(ValueError):
+    """Raised for a dense set or fraction the format cannot represent."""
+
+
+# ---------------------------------------------------------------------------
+# a1: dense-set resolution  (Technical Summary 2.A / 2.B)
+# ---------------------------------------------------------------------------
+def resolve_dense_set(K: int, dense_cols=None, dense_fraction: Optional[float] = None):
+    """Return (pi, K_s, K_d).
+
+    With ``dense_cols`` the given set is the dense region (SpenseGPT+ style:
+    arbitrary indices, moved into one contiguous block).  Otherwise the dense
+    region is the last K_d = round(p*K) indices (SpenseGPT: the last p%).
+    pi lists the sparse indices ascending, then the dense indices ascending.
+    The sparse region must hold whole groups of four.
+    """
+    if K <= 0:
+        raise DenseSetError("K must be positive")
+    if dense_cols is not None:
+        D = np.asarray(dense_cols, dtype=np.int64).ravel()
+        if D.size and (D.min() < 0 or D.max() >= K):
+            raise DenseSetError("dense column out of range")
+        if np.unique(D).size != D.size:
+            raise DenseSetError("duplicate dense column")
+        D = np.sort(D)
+    else:
+        if dense_fraction is None:
+            raise DenseSetError("need dense_cols or dense_fraction")
+        p = float(dense_fraction)
+        if not (0.0 <= p <= 1.0):
+            raise DenseSetError("dense_fraction outside [0, 1]")
+        K_d = int(math.floor(p * K + 0.5))
+        D = np.arange(K - K_d, K, dtype=np.int64)
+    K_d = int(D.size)
+    K_s = K - K_d
+    if K_s % 4 != 0:
+        raise DenseSetError("sparse region length must be a multiple of 4")
+    is_dense = np.zeros(K, dtype=bool)
+    is_dense[D] = True
+    sparse = np.nonzero(~is_dense)[0]
+    pi = np.concatenate([sparse, D]).astype(np.int64)
+    return pi, K_s, K_d
+
+
+# ---------------------------------------------------------------------------
+# element encodings
+# ---------------------------------------------------------------------------
+def magnitude_key(bits: np.ndarray, dtype: int) -> np.ndarray:
+    """Magnitude order key: the stored bit pattern with its sign bit cleared.
+
+    For IEEE-style encodings (fp32, bf16, e4m3fn) this unsigned integer orders
+    finite magnitudes exactly as their values do; +0 and -0 compare equal.
+    """
+    if dtype == DT_F32:
+        u = np.ascontiguousarray(bits, dtype=np.float32).view(np.uint32)
+        return (u & np.uint32(0x7FFFFFFF)).astype(np.int64)
+    if dtype == DT_BF16:
+        return (np.asarray(bits, dtype=np.uint16) & np.uint16(0x7FFF)).astype(np.int64)
+    if dtype == DT_FP8:
+        return (np.asarray(bits, dtype=np.uint8) & np.uint8(0x7F)).astype(np.int64)
+    raise ValueError(f"unknown dtype {dtype}")
+
+
+def _e4m3_value(code: int) -> float:
+    """OCP e4m3fn: sign, 4-bit exponent (bias 7), 3-bit mantissa; S.1111.111 is NaN."""
+    s = -1.0 if code & 0x80 else 1.0
+    e = (code >> 3) & 0xF
+    m = code & 0x7
+    if e == 0xF and m == 0x7:
+        return float("nan")
+    if e == 0:
+        return s * m * 2.0 ** -9
+    return s * (1.0 + m / 8.0) * 2.0 ** (e - 7)
+
+
+_E4M3_TABLE = np.array([_e4m3_value(c) for c in range(256)], dtype=np.float64)
+
+
+def decode_values(bits: np.ndarray, dtype: int) -> np.ndarray:
+    """Stored bits -> float64 values."""
+    if dtype == DT_F32:
+        return np.asarray(bits, dtype=np.float32).astype(np.float64)
+    if dtype == DT_BF16:
+        u = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+        with np.errstate(invalid="ignore"):
+            return u.view(np.float32).astype(np.float64)
+    if dtype == DT_FP8:
+        return _E4M3_TABLE[np.asarray(bits, dtype=np.uint8)]
+    raise ValueError(f"unknown dtype {dtype}")
+
+
+def _storage_dtype(dtype: int):
+    return {DT_F32: np.float32, DT_BF16: np.uint16, DT_FP8: np.uint8}[dtype]
+
+
+# ---------------------------------------------------------------------------
+# a2 + a3: 2:4 magnitude selection and compression, dense block copy
+# ---------------------------------------------------------------------------
+@dataclass
+class Packed:
+    """Canonical packed form of one weight matrix.
+
+    vals  [N, K_s/2]          kept values (bit copies), two per group, lower position first
+    meta  [N, ceil(K_s/32)]   uint32; group g's nibble (i0 | i1<<2) at bits 4*(g%8) of word g//8
+    mask  [N, K_s]            uint8 0/1, 1 on kept slots (columns in pi order)
+    dense [N, K_d]            bit copies of W[:, pi[K_s:]]
+    pi    [K]                 column order
+    """
+
+    vals: np.ndarray
+    meta: np.ndarray
+    mask: np.ndarray
+    dense: np.ndarray
+    pi: np.ndarray
+    K_s: int
+    K_d: int
+    dtype: int
+
+
+def pack(W: np.ndarray, dtype: int, pi: np.ndarray, K_s: int) -> Packed:
+    """Choose the 2:4 mask by magnitude and compress the sparse region.
+
+    Group g of row n holds the four sparse-region columns pi[4g..4g+3].  The two
+    slots with the largest magnitude key are kept; among equal keys the lower
+    slot wins (a stable sort of the negated keys realises exactly this order).
+    """
+    W = np.asarray(W)
+    N, K = W.shape
+    if K_s % 4 != 0:
+        raise DenseSetError("sparse region length must be a multiple of 4")
+    G = K_s // 4
+    pi = np.asarray(pi, dtype=np.int64)
+    Ws = W[:, pi[:K_s]].reshape(N, G, 4)
+    keys = magnitude_key(Ws, dtype)
+    order = np.argsort(-keys, axis=2, kind="stable")[:, :, :2]
+    i0 = order.min(axis=2)
+    i1 = order.max(axis=2)
+    mask = np.zeros((N, G, 4), dtype=np.uint8)
+    np.put_along_axis(mask, i0[:, :, None], 1, axis=2)
+    np.put_along_axis(mask, i1[:, :, None], 1, axis=2)
+    v0 = np.take_along_axis(Ws, i0[:, :, None], axis=2)[:, :, 0]
+    v1 = np.take_along_axis(Ws, i1[:, :, None], axis=2)[:, :, 0]
+    vals = np.empty((N, 2 * G), dtype=W.dtype)
+    vals[:, 0::2] = v0
+    vals[:, 1::2] = v1
+    nib = (i0 | (i1 << 2)).astype(np.uint64)
+    n_words = (G + 7) // 8
+    meta = np.zeros((N, n_words), dtype=np.uint64)
+    for j in range(8):
+        part = nib[:, j::8]
+        meta[:, : part.shape[1]] |= part << np.uint64(4 * j)
+    dense = np.ascontiguousarray(W[:, pi[K_s:]])
+    return Packed(vals=vals, meta=meta.astype(np.uint32), mask=mask.reshape(N, K_s),
+                  dense=dense, pi=pi, K_s=K_s, K_d=K - K_s, dtype=dtype)
+
+
+def unpack_bits(p: Packed) -> np.ndarray:
+    """Rebuild W with pruned positions set to (+0) from vals/meta/dense, natural column order."""
+    N = p.vals.shape[0]
+    K = p.pi.size
+    G = p.K_s // 4
+    out = np.zeros((N, K), dtype=_storage_dtype(p.dtype))
+    if G:
+        g = np.arange(G)
+        nib = (p.meta[:, g // 8].astype(np.uint64) >> (4 * (g % 8)).astype(np.uint64)) & np.uint64(0xF)
+        i0 = (nib & np.uint64(3)).astype(np.int64)
+        i1 = (nib >> np.uint64(2)).astype(np.int64)
+        rows = np.arange(N)[:, None]
+        col0 = p.pi[4 * g[None, :] + i0]
+        col1 = p.pi[4 * g[None, :] + i1]
+        out[rows, col0] = p.vals[:, 0::2]
+        out[rows, col1] = p.vals[:, 1::2]
+    if p.K_d:
+        out[:, p.pi[p.K_s:]] = p.dense
+    return out
+
+
+def decompress(p: Packed, scales=None) -> np.ndarray:
+    """Values of the pruned weight matrix in natural column order, float64 (scale not applied)."""
+    return decode_values(unpack_bits(p), p.dtype)
+
+
+# ---------------------------------------------------------------------------
+# a4..a7: the layer output  Y = s * (X' . W_sparse^T + X' . W_dense^T)
+# ---------------------------------------------------------------------------
+def linear_ref(X_bits: np.ndarray, xdtype: int, p: Packed, scales=None):
+    """Exact layer output in float64 and its error scale.
+
+    Since X'[:, j] = X[:, pi[j]] and the packed weights decompress to the same
+    columns pi[j], the sparse product plus the dense product equals X times the
+    decompressed (pruned) weight matrix in natural order:
+        Y[m, n] = s[n] * sum_k X[m, k] * Wp[n, k]
+        B[m, n] = s[n] * sum_k |X[m, k] * Wp[n, k]|
+    with s = 1 for non-fp8 weights.  Returns (Y, B), both [M, N] float64.
+    """
+    Wp = decompress(p)
+    X = decode_values(X_bits, xdtype)
+    Y = X @ Wp.T
+    B = np.abs(X) @ np.abs(Wp).T
+    if scales is not None:
+        s = np.asarray(scales, dtype=np.float32).astype(np.float64)
+        Y = Y * s[None, :]
+        B = B * s[None, :]
+    return Y, B
+
+
+def dense_linear_ref(X_bits: np.ndarray, xdtype: int, W_bits: np.ndarray, wdtype: int, scales=None):
+    """All-dense comparator Y = X . (s o W)^T of the unpruned weights, with its error scale."""
+    W = decode_values(W_bits, wdtype)
+    X = decode_values(X_bits, xdtype)
+    Y = X @ W.T
+    B = np.abs(X) @ np.abs(W).T
+    if scales is not None:
+        s = np.asarray(scales, dtype=np.float32).astype(np.float64)
+        Y = Y * s[None, :]
+        B = B * s[None, :]
+    return Y, B

@@ -1,0 +1,357 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each test fixes the oracle to an outside fact: a hand-worked example, a
+library routine (torch's e4m3/bf16 casts, torch's float64 GEMM), an
+independent characterisation (pairwise dominance for the 2:4 choice), exact
+integer brute force, or an invariant the pages state (2:4 groups hold at most
+two nonzeros; permuting indices into the dense block leaves the output
+unchanged).
+"""
+
+import itertools
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import DT_BF16, DT_F32, DT_FP8
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# --------------------------------------------------------------------------
+# independent helpers (not the oracle's code paths)
+# --------------------------------------------------------------------------
+def dominance_pair(keys):
+    """The unique kept pair by pairwise dominance: P is valid iff every i in P
+    beats every j outside P (larger key, or equal key and lower position)."""
+    valid = []
+    for P in itertools.combinations(range(4), 2):
+        ok = True
+        for i in P:
+            for j in range(4):
+                if j in P:
+                    continue
+                if not (keys[i] > keys[j] or (keys[i] == keys[j] and i < j)):
+                    ok = False
+        if ok:
+            valid.append(P)
+    assert len(valid) == 1, (keys, valid)
+    return valid[0]
+
+
+def prune_python(Wvals, keys, pi, K_s):
+    """Pruned weight values in natural order, by plain loops."""
+    N = len(Wvals)
+    out = [[float(v) for v in row] for row in Wvals]
+    for n in range(N):
+        for g in range(K_s // 4):
+            cols = [int(pi[4 * g + t]) for t in range(4)]
+            kk = [int(keys[n][c]) for c in cols]
+            keep = sorted(range(4), key=lambda t: (-kk[t], t))[:2]
+            for t in range(4):
+                if t not in keep:
+                    out[n][cols[t]] = 0.0
+    return out
+
+
+def torch_e4m3_values():
+    return torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+# --------------------------------------------------------------------------
+# element encodings
+# --------------------------------------------------------------------------
+def test_e4m3_decode_matches_torch_all_codes():
+    ref = torch_e4m3_values()
+    got = oracle.decode_values(np.arange(256, dtype=np.uint8), DT_FP8)
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(got))
+    assert np.array_equal(ref[~nan], got[~nan])
+    assert np.array_equal(np.signbit(ref[~nan]), np.signbit(got[~nan]))
+    # closed forms: largest finite, smallest subnormal, smallest normal, one
+    assert got[0x7E] == 448.0 and got[0x01] == 2.0 ** -9 and got[0x08] == 2.0 ** -6 and got[0x38] == 1.0
+    assert np.isnan(got[0x7F]) and np.isnan(got[0xFF])
+
+
+def test_bf16_decode_matches_torch():
+    bits = np.arange(0, 65536, 7, dtype=np.uint32).astype(np.uint16)
+    ref = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
+    got = oracle.decode_values(bits, DT_BF16)
+    nan = np.isnan(ref)
+    assert np.array_equal(nan, np.isnan(got))
+    assert np.array_equal(ref[~nan], got[~nan])
+
+
+def test_synth_e4m3_encoder_matches_torch_cast():
+    rng = np.random.default_rng(5)
+    vals = np.concatenate([
+        rng.normal(0, 50, 20000), rng.normal(0, 0.01, 20000), rng.uniform(-448, 448, 20000),
+        torch_e4m3_values()[np.isfinite(torch_e4m3_values())],
+    ])
+    # exact midpoints between neighbouring codes exercise ties-to-even
+    fin = np.sort(np.unique(np.abs(torch_e4m3_values()[np.isfinite(torch_e4m3_values())])))
+    mids = (fin[1:] + fin[:-1]) / 2
+    vals = np.concatenate([vals, mids, -mids, [0.0, -0.0, 448.0, -448.0]])
+    vals = np.clip(vals, -448, 448)
+    ref = torch.from_numpy(vals).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = synth.e4m3_encode(vals)
+    assert np.array_equal(ref, got)
+    # saturation: beyond the largest finite value the encoder clamps to 448
+    assert synth.e4m3_encode(np.array([1e6, -500.0])).tolist() == [0x7E, 0xFE]
+
+
+def test_synth_bf16_encoder_matches_torch_cast():
+    rng = np.random.default_rng(6)
+    v = np.concatenate([rng.normal(0, 1, 50000), rng.normal(0, 1e-30, 1000), [0.0, -0.0, 1.0, 3.0e38]])
+    f32 = v.astype(np.float32)
+    ref = torch.from_numpy(f32).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(ref, synth.bf16_encode(v))
+
+
+# --------------------------------------------------------------------------
+# a1: dense-set resolution
+# --------------------------------------------------------------------------
+def test_dense_set_tail_and_rounding():
+    pi, K_s, K_d = oracle.resolve_dense_set(5120, dense_fraction=0.25)
+    assert (K_s, K_d) == (3840, 1280)
+    assert np.array_equal(pi, np.arange(5120))
+    for K, p, kd in ((100, 0.125, 13), (100, 0.12, 12), (8, 0.5, 4), (12, 1 / 3, 4), (16, 0.0, 0), (16, 1.0, 16)):
+        if (K - kd) % 4:
+            with pytest.raises(oracle.DenseSetError):
+                oracle.resolve_dense_set(K, dense_fraction=p)
+        else:
+            assert oracle.resolve_dense_set(K, dense_fraction=p)[2] == kd
+
+
+def test_dense_set_explicit():
+    pi, K_s, K_d = oracle.resolve_dense_set(12, dense_cols=[11, 2, 7, 0])
+    assert (K_s, K_d) == (8, 4)
+    assert pi.tolist() == [1, 3, 4, 5, 6, 8, 9, 10, 0, 2, 7, 11]
+    with pytest.raises(oracle.DenseSetError):
+        oracle.resolve_dense_set(12, dense_cols=[1, 1, 2, 3])
+    with pytest.raises(oracle.DenseSetError):
+        oracle.resolve_dense_set(12, dense_cols=[12, 1, 2, 3])
+    with pytest.raises(oracle.DenseSetError):
+        oracle.resolve_dense_set(12, dense_cols=[1, 2])
+    with pytest.raises(oracle.DenseSetError):
+        oracle.resolve_dense_set(12, dense_fraction=1.5)
+
+
+# --------------------------------------------------------------------------
+# hand-worked examples
+# --------------------------------------------------------------------------
+def _golden_cases():
+    with open(os.path.join(GOLDEN, "hand_worked.json")) as f:
+        return json.load(f)["cases"]
+
+
+@pytest.mark.parametrize("case", _golden_cases(), ids=lambda c: c["name"])
+def test_hand_worked(case):
+    K = case["K"]
+    if "dense_cols" in case:
+        pi, K_s, K_d = oracle.resolve_dense_set(K, dense_cols=case["dense_cols"])
+    else:
+        pi, K_s, K_d = oracle.resolve_dense_set(K, dense_fraction=case["dense_fraction"])
+    e = case["expect"]
+    assert pi.tolist() == e["pi"] and K_s == e["K_s"]
+    if case["dtype"] == "f32":
+        W = np.array(case["W"], dtype=np.float32)
+        p = oracle.pack(W, DT_F32, pi, K_s)
+        assert np.array_equal(p.vals, np.array(e["vals"], dtype=np.float32))
+        assert np.array_equal(np.signbit(p.vals), np.signbit(np.array(e["vals"], dtype=np.float32)))
+        assert np.array_equal(p.dense, np.array(e["dense"], dtype=np.float32).reshape(p.dense.shape))
+        X = np.array(case["X"], dtype=np.float32)
+        Y, _ = oracle.linear_ref(X, DT_F32, p)
+    else:
+        W = np.array(case["W_codes"], dtype=np.uint8)
+        p = oracle.pack(W, DT_FP8, pi, K_s)
+        assert p.vals.tolist() == e["vals_codes"]
+        assert p.dense.reshape(-1).tolist() == [c for row in e["dense_codes"] for c in row]
+        X = synth.bf16_encode(np.array(case["X"], dtype=np.float64))
+        Y, _ = oracle.linear_ref(X, DT_BF16, p, scales=np.array(case["scales"], dtype=np.float32))
+    assert p.meta.tolist() == e["meta"]
+    assert p.mask.tolist() == e["mask"]
+    assert np.array_equal(Y, np.array(e["Y"], dtype=np.float64))
+
+
+# --------------------------------------------------------------------------
+# a2: the 2:4 choice, exhaustively
+# --------------------------------------------------------------------------
+def _check_groups(W, dtype):
+    """W[n, 4]: one group per row; compare oracle's choice with dominance."""
+    pi = np.arange(4)
+    p = oracle.pack(W, dtype, pi, 4)
+    keys = oracle.magnitude_key(W, dtype)
+    nib = p.meta[:, 0] & 0xF
+    for n in range(W.shape[0]):
+        i0, i1 = dominance_pair(keys[n].tolist())
+        assert int(nib[n]) == (i0 | (i1 << 2)), (W[n], keys[n])
+        assert p.mask[n].tolist() == [1 if t in (i0, i1) else 0 for t in range(4)]
+
+
+def test_tie_break_exhaustive_small_ints():
+    groups = np.array(list(itertools.product(range(-4, 5), repeat=4)), dtype=np.float64)
+    groups[groups == 0] = 0.0
+    _check_groups(groups.astype(np.float32), DT_F32)
+    _check_groups(synth.bf16_encode(groups * 0.375), DT_BF16)
+    _check_groups(synth.e4m3_encode(groups * 2.0), DT_FP8)
+    # signed zeros in every position: -0 and +0 are equal magnitudes
+    z = np.array(list(itertools.product([0.0, -0.0, 1.0, -1.0], repeat=4)), dtype=np.float32)
+    _check_groups(z, DT_F32)
+
+
+def test_tie_break_all_e4m3_code_pairs():
+    a, b = np.meshgrid(np.arange(256), np.arange(256), indexing="ij")
+    a = a.ravel().astype(np.uint8)
+    b = b.ravel().astype(np.uint8)
+    for patt in ((a, b, b, a), (a, a, b, b), (b, a, a, b)):
+        W = np.stack(patt, axis=1)
+        p = oracle.pack(W, DT_FP8, np.arange(4), 4)
+        keys = oracle.magnitude_key(W, DT_FP8)
+        # vectorised dominance: count for each candidate pair whether it dominates
+        nib = (p.meta[:, 0] & 0xF).astype(np.int64)
+        sel = np.zeros(W.shape[0], dtype=np.int64) - 1
+        for P in itertools.combinations(range(4), 2):
+            ok = np.ones(W.shape[0], dtype=bool)
+            for i in P:
+                for j in range(4):
+                    if j in P:
+                        continue
+                    ok &= (keys[:, i] > keys[:, j]) | ((keys[:, i] == keys[:, j]) & (i < j))
+            assert not np.any(ok & (sel >= 0))
+            sel[ok] = P[0] | (P[1] << 2)
+        assert np.all(sel >= 0)
+        assert np.array_equal(sel, nib)
+
+
+# --------------------------------------------------------------------------
+# invariants on random weights
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", [DT_F32, DT_BF16, DT_FP8])
+def test_two_of_four_and_round_trip(dtype):
+    rng = np.random.default_rng(11)
+    N, K = 24, 96
+    W, s = synth.make_weight(N, K, dtype, rng)
+    for D in (synth.tail_dense_set(K, 32), synth.random_dense_set(K, 20, 3), np.array([], dtype=np.int32)):
+        pi, K_s, K_d = oracle.resolve_dense_set(K, dense_cols=D)
+        p = oracle.pack(W, dtype, pi, K_s)
+        # exactly two kept slots per group
+        assert np.all(p.mask.reshape(N, -1, 4).sum(axis=2) == 2)
+        Wr = oracle.unpack_bits(p)
+        # pruned matrix: at most two nonzeros per group of the sparse region
+        vals = oracle.decode_values(Wr, dtype)
+        nz = (vals[:, pi[:K_s]] != 0).reshape(N, -1, 4).sum(axis=2)
+        assert np.all(nz <= 2)
+        # round trip against the mask applied to W (computed here, not by unpack)
+        keep = np.ones((N, K), dtype=bool)
+        keep[:, pi[:K_s]] = p.mask.astype(bool)
+        zero = np.zeros((), dtype=W.dtype)
+        expect = np.where(keep, W, zero)
+        assert np.array_equal(expect.view(np.uint8), Wr.view(np.uint8))
+        # idempotence: packing the pruned matrix gives the same packed form
+        p2 = oracle.pack(Wr, dtype, pi, K_s)
+        assert np.array_equal(p2.meta, p.meta) and np.array_equal(p2.mask, p.mask)
+
+
+# --------------------------------------------------------------------------
+# special cases that reduce to a library GEMM
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype", [DT_F32, DT_BF16, DT_FP8])
+def test_fraction_one_is_dense_gemm(dtype):
+    rng = np.random.default_rng(12)
+    N, K, M = 40, 64, 3
+    W, s = synth.make_weight(N, K, dtype, rng)
+    X = synth.make_x(M, K, DT_F32 if dtype == DT_F32 else DT_BF16, rng)
+    xdt = DT_F32 if dtype == DT_F32 else DT_BF16
+    pi, K_s, K_d = oracle.resolve_dense_set(K, dense_fraction=1.0)
+    assert K_s == 0
+    p = oracle.pack(W, dtype, pi, K_s)
+    Y, B = oracle.linear_ref(X, xdt, p, s)
+    Wt = torch.from_numpy(oracle.decode_values(W, dtype))
+    if s is not None:
+        Wt = Wt * torch.from_numpy(s.astype(np.float64))[:, None]
+    ref = torch.nn.functional.linear(torch.from_numpy(oracle.decode_values(X, xdt)), Wt).numpy()
+    assert np.all(np.abs(Y - ref) <= 1e-12 * B + 1e-300)
+    Yd, _ = oracle.dense_linear_ref(X, xdt, W, dtype, s)
+    assert np.all(np.abs(Yd - ref) <= 1e-12 * B + 1e-300)
+
+
+@pytest.mark.parametrize("dtype", [DT_F32, DT_FP8])
+def test_fraction_zero_is_pure_two_four(dtype):
+    rng = np.random.default_rng(13)
+    N, K, M = 16, 64, 2
+    W, s = synth.make_weight(N, K, dtype, rng)
+    xdt = DT_F32 if dtype == DT_F32 else DT_BF16
+    X = synth.make_x(M, K, xdt, rng)
+    pi, K_s, K_d = oracle.resolve_dense_set(K, dense_fraction=0.0)
+    p = oracle.pack(W, dtype, pi, K_s)
+    Y, B = oracle.linear_ref(X, xdt, p, s)
+    keys = oracle.magnitude_key(W, dtype)
+    Wp = torch.tensor(prune_python(oracle.decode_values(W, dtype).tolist(), keys.tolist(), pi, K_s), dtype=torch.float64)
+    if s is not None:
+        Wp = Wp * torch.from_numpy(s.astype(np.float64))[:, None]
+    ref = torch.nn.functional.linear(torch.from_numpy(oracle.decode_values(X, xdt)), Wp).numpy()
+    assert np.all(np.abs(Y - ref) <= 1e-12 * B + 1e-300)
+
+
+# --------------------------------------------------------------------------
+# exact brute force over every dense set of a tiny layer
+# --------------------------------------------------------------------------
+def test_brute_force_every_dense_set_8x16():
+    rng = np.random.default_rng(14)
+    N, K, M = 8, 16, 2
+    W = rng.integers(-6, 7, size=(N, K)).astype(np.float32)
+    X = rng.integers(-5, 6, size=(M, K)).astype(np.float32)
+    keys = oracle.magnitude_key(W, DT_F32).tolist()
+    Wl = W.astype(np.float64).tolist()
+    Xl = X.astype(np.float64).tolist()
+    count = 0
+    for kd in (0, 4, 8, 12, 16):
+        for D in itertools.combinations(range(K), kd):
+            pi, K_s, K_d = oracle.resolve_dense_set(K, dense_cols=list(D))
+            p = oracle.pack(W, DT_F32, pi, K_s)
+            Y, _ = oracle.linear_ref(X, DT_F32, p)
+            Wp = prune_python(Wl, keys, pi, K_s)
+            for m in range(M):
+                for n in range(N):
+                    acc = 0.0
+                    for k in range(K):
+                        acc += Xl[m][k] * Wp[n][k]
+                    assert Y[m, n] == acc
+            count += 1
+    assert count == 1 + 1820 + 12870 + 1820 + 1
+
+
+# --------------------------------------------------------------------------
+# permutation into the dense block leaves the output unchanged
+# --------------------------------------------------------------------------
+def test_gather_equals_contiguous_tail():
+    rng = np.random.default_rng(15)
+    N, K, M = 32, 128, 4
+    W = rng.integers(-8, 9, size=(N, K)).astype(np.float32)
+    X = rng.integers(-4, 5, size=(M, K)).astype(np.float32)
+    D = synth.random_dense_set(K, 32, 7)
+    pi, K_s, K_d = oracle.resolve_dense_set(K, dense_cols=D)
+    Y1, _ = oracle.linear_ref(X, DT_F32, oracle.pack(W, DT_F32, pi, K_s))
+    pi2, K_s2, _ = oracle.resolve_dense_set(K, dense_fraction=K_d / K)
+    Y2, _ = oracle.linear_ref(X[:, pi], DT_F32, oracle.pack(W[:, pi], DT_F32, pi2, K_s2))
+    assert np.array_equal(Y1, Y2)
+
+
+def test_scale_is_per_output_channel():
+    rng = np.random.default_rng(16)
+    N, K, M = 8, 32, 2
+    W, s = synth.make_weight(N, K, DT_FP8, rng)
+    X = synth.make_x(M, K, DT_BF16, rng)
+    pi, K_s, _ = oracle.resolve_dense_set(K, dense_fraction=0.25)
+    p = oracle.pack(W, DT_FP8, pi, K_s)
+    Y, _ = oracle.linear_ref(X, DT_BF16, p, s)
+    Y1, _ = oracle.linear_ref(X, DT_BF16, p, None)
+    assert np.array_equal(Y, Y1 * s.astype(np.float64)[None, :])
+    # the scale is max|w|/448 of the unpruned row: every row holds a +-448 code
+    assert np.all(np.max(oracle.magnitude_key(W, DT_FP8), axis=1) == 0x7E)
