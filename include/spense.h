@@ -1,0 +1,172 @@
+/*
+ * spense.h - C interface of the Spense hybrid sparse-dense linear layer on
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The layer (SpenseGPT gist.science explainer, Technical Summary 2.A "The
+ * Spense Format"): the input dimension K of a weight matrix W[N,K] is split
+ * into a contiguous 2:4 semi-structured region and a contiguous dense region,
+ * and the input-split form accumulates both products into one output,
+ *
+ *     Y[M,N] = X'[:, :K_s] . W_sparse^T + X'[:, K_s:] . W_dense^T,
+ *
+ * where X' = X[:, pi] and pi lists the sparse columns ascending, then the
+ * dense columns ascending.  Which columns stay dense (Technical Summary 2.B
+ * "Dense Index Selection Strategies"): the last p% of K (SpenseGPT), or any
+ * chosen set moved into the dense block by that permutation (SpenseGPT+).
+ * 2:4 means at most two nonzeros in every four consecutive weights (Technical
+ * Summary 1 "Problem Statement"); here exactly two slots per group are kept,
+ * the two with the largest magnitude, the lower position winning ties.
+ *
+ * General rules for every entry point:
+ *   - All arguments are validated on the host before any HIP call or launch;
+ *     a rejected call returns SPENSE_EINVAL / SPENSE_EUNSUPPORTED and has no
+ *     side effect.
+ *   - "device pointer" means memory the HIP runtime can access from the GPU
+ *     current at the call (hipMalloc / torch CUDA tensors).  "host pointer" is
+ *     ordinary CPU memory.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *   - Matrices are row-major; leading dimensions are in elements.
+ *   - A HIP runtime failure returns SPENSE_EHIP; spense_last_hip_error()
+ *     then returns the hipError_t value.  Faults inside a kernel surface at the
+ *     caller's next synchronisation, as for any HIP launch.
+ *   - The library is not thread-safe per handle: at most one spense_linear may
+ *     be in flight on a handle at a time (its split-K workspace is shared).
+ */
+#ifndef SPENSE_H
+#define SPENSE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SPENSE_ABI_VERSION 1
+
+/* Element types.  The numbering is fixed. */
+typedef enum spense_dtype {
+  SPENSE_F32 = 0,      /* IEEE binary32 */
+  SPENSE_BF16 = 1,     /* bfloat16 */
+  SPENSE_FP8_E4M3 = 2  /* OCP e4m3fn: bias 7, largest finite 448, no infinities */
+} spense_dtype;
+
+typedef enum spense_status {
+  SPENSE_OK = 0,
+  SPENSE_EINVAL = -1,       /* bad argument (null pointer, size, dense set, ...) */
+  SPENSE_EUNSUPPORTED = -2, /* valid but unsupported combination of types */
+  SPENSE_ENOMEM = -3,       /* device or host allocation failed */
+  SPENSE_EHIP = -4          /* a HIP runtime call failed */
+} spense_status;
+
+typedef struct spense_layer* spense_handle;
+
+typedef struct spense_layer_info {
+  int64_t N, K;           /* weight shape */
+  int64_t K_s, K_d;       /* sparse / dense region lengths, K_s + K_d = K, K_s % 4 == 0 */
+  int32_t wdtype;         /* spense_dtype of the stored weights */
+  int32_t gather;         /* 1 when spense_linear gathers activation columns (pi not the identity
+                             on a 128-aligned split), 0 when X is read in place */
+  int64_t weight_bytes;   /* bytes the method must stream per call: kept values + 2-bit indices
+                             + dense block = N*(K_s/2*b + K_s/8 + K_d*b), b = element bytes */
+  int64_t device_bytes;   /* bytes of the device-resident packed form, padding included */
+} spense_layer_info;
+
+/*
+ * spense_pack - choose the 2:4 mask and build the packed layer (once per weight).
+ *
+ * Defined by Technical Summary 2.A / 2.B of the SpenseGPT explainer: the dense
+ * set is either `dense_cols` (SpenseGPT+ style, any columns, order irrelevant)
+ * or, when dense_cols is NULL, the last K_d = round(dense_fraction*K) columns
+ * (SpenseGPT style, rounding half away from zero).  In every group of four
+ * consecutive sparse-region columns (in pi order) the two entries with the
+ * largest magnitude are kept, magnitude being the stored bit pattern with the
+ * sign bit cleared; the lower in-group position wins ties.
+ *
+ *   W          device pointer, [N, ldw] elements of `wdtype`; only [N, K] is read.
+ *   wdtype     SPENSE_F32, SPENSE_BF16 or SPENSE_FP8_E4M3.
+ *   N, K       N >= 1, K >= 1; ldw >= K.
+ *   scales     device pointer, [N] float32 per-output-channel dequantisation scales;
+ *              required (non-NULL) iff wdtype == SPENSE_FP8_E4M3, must be NULL otherwise.
+ *              Y[m,n] is multiplied by scales[n].
+ *   dense_cols host pointer to n_dense distinct int32 column indices in [0, K), or NULL.
+ *   n_dense    number of entries in dense_cols (ignored when dense_cols is NULL).
+ *   dense_fraction  used only when dense_cols is NULL; must lie in [0, 1].
+ *   stream     stream the packing kernels run on.
+ *   out        receives the new handle.
+ *
+ * K - K_d must be a multiple of 4 (SPENSE_EINVAL otherwise).  The call returns
+ * after the packed form is complete (it synchronises `stream`), so W and
+ * scales may be freed or overwritten once it returns.  The handle owns every
+ * buffer it holds; release it with spense_free.
+ */
+int spense_pack(const void* W, int32_t wdtype, int64_t N, int64_t K, int64_t ldw, const float* scales,
+                const int32_t* dense_cols, int64_t n_dense, double dense_fraction, void* stream,
+                spense_handle* out);
+
+/*
+ * spense_linear - Y = X . W_pruned^T (times the per-channel scales), the layer forward.
+ *
+ * Input-split execution (Technical Summary 2.A): the sparse region runs on the
+ * structured-sparse SMFMAC matrix instructions, the dense region on dense MFMA,
+ * both accumulating into the same fp32 accumulators; when the dense set is not
+ * a 128-aligned tail the activation columns are gathered through pi in the
+ * same kernel.  Accumulation is fp32; products of bf16 activations with bf16
+ * or e4m3 weights are exact.
+ *
+ *   h          handle from spense_pack.
+ *   X          device pointer, [M, ldx] elements of `xdtype`, ldx >= K.
+ *              xdtype must be SPENSE_F32 for fp32 weights and SPENSE_BF16 otherwise.
+ *   M          number of activation rows, M >= 1.
+ *   Y          device pointer, [M, ldy] elements of `ydtype`, ldy >= N; only [M, N] is written.
+ *   ydtype     SPENSE_F32 (fp32 accumulators as they are) or SPENSE_BF16 (round to nearest even).
+ *
+ * Asynchronous on `stream`.  Deterministic: repeated calls give bitwise equal
+ * Y (split-K partial sums are added in a fixed order).  The first call at a
+ * larger M than before may allocate a larger split-K workspace (hipMalloc).
+ */
+int spense_linear(spense_handle h, const void* X, int32_t xdtype, int64_t M, int64_t ldx, void* Y, int32_t ydtype,
+                  int64_t ldy, void* stream);
+
+/*
+ * spense_linear_splits - spense_linear with the split-K factor forced (tuning and tests).
+ * splits == 0 picks automatically; otherwise 1 <= splits <= number of 128-column steps.
+ */
+int spense_linear_splits(spense_handle h, const void* X, int32_t xdtype, int64_t M, int64_t ldx, void* Y,
+                         int32_t ydtype, int64_t ldy, int32_t splits, void* stream);
+
+/* spense_info - sizes of a packed layer (host-side, no synchronisation). */
+int spense_info(spense_handle h, spense_layer_info* info);
+
+/*
+ * spense_export - write the packed layer in its canonical form (for bit-exact checks).
+ *
+ *   vals   device pointer, [N, K_s/2] elements of wdtype: the two kept values of each
+ *          group, lower position first.
+ *   meta   device pointer, [N, ceil(K_s/32)] uint32: group g's nibble (i0 | i1 << 2),
+ *          i0 < i1 its kept in-group positions, sits at bits 4*(g%8) of word g/8;
+ *          unused nibbles are 0.
+ *   mask   device pointer, [N, K_s] uint8: 1 on kept slots (columns in pi order).
+ *   dense  device pointer, [N, K_d] elements of wdtype: W[:, pi[K_s:]].
+ *   pi     host pointer, [K] int32 column order.
+ * Any pointer may be NULL to skip that part.  Synchronises `stream` before returning.
+ */
+int spense_export(spense_handle h, void* vals, uint32_t* meta, uint8_t* mask, void* dense, int32_t* pi,
+                  void* stream);
+
+/* spense_free - release the handle and its device buffers (no launch may still use it). */
+int spense_free(spense_handle h);
+
+/* Human-readable text for a status code (static storage). */
+const char* spense_strerror(int status);
+
+/* hipError_t value of the most recent SPENSE_EHIP on the calling thread (0 if none). */
+int spense_last_hip_error(void);
+
+/* SPENSE_ABI_VERSION of the loaded library. */
+int spense_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPENSE_H */

@@ -19,6 +19,9 @@ fp8 -> ``np.uint8`` codes.
 
 from __future__ import annotations
 
+import os
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 
 # dtype tags; the numbering is the one the C interface uses
@@ -43,39 +46,46 @@ def bf16_encode(x) -> np.ndarray:
 def e4m3_encode(x) -> np.ndarray:
     """float array -> OCP e4m3fn codes (uint8): round to nearest even, saturate at 448.
 
-    Works in float64: the quantum of the binade holding |x| is
-    2^(max(e, -6) - 3) (e = floor(log2 |x|), subnormal quantum 2^-9), so
-    |x| / quantum is rounded with ``np.rint`` (ties to even) and the rounded
-    magnitude is then split into exponent and 3-bit mantissa fields.
+    Exact on the float64 bit pattern.  For |x| >= 2^-6 (normal e4m3) the 52-bit
+    fraction is rounded to 3 bits (ties to even) by integer addition, the
+    carry stepping into the exponent when the fraction rounds up; the biased
+    float64 exponent then maps to the e4m3 exponent by subtracting 1023 - 7.
+    Below 2^-6 the subnormal code is rint(|x| * 2^9).
     """
-    a64 = np.asarray(x, dtype=np.float64)
-    sign = np.signbit(a64).astype(np.uint8) << 7
-    a = np.minimum(np.abs(a64), 448.0)
-    _, E = np.frexp(a)  # a = m * 2^E, m in [0.5, 1)
-    e = np.maximum(E.astype(np.int64) - 1, -6)
-    q = np.ldexp(1.0, e - 3)
-    r = np.rint(a / q) * q  # representable e4m3 magnitude (may step into the next binade)
-    r = np.minimum(r, 448.0)
-    _, Er = np.frexp(r)
-    er = Er.astype(np.int64) - 1
-    normal = r >= 2.0 ** -6
-    er_n = np.where(normal, er, 0)
-    mant_n = np.rint((r / np.ldexp(1.0, er_n) - 1.0) * 8.0).astype(np.int64)
-    code_n = ((er_n + 7) << 3) | mant_n
-    code_s = np.rint(r / 2.0 ** -9).astype(np.int64)
-    code = np.where(normal, code_n, code_s).astype(np.uint8)
-    return code | sign
+    a = np.minimum(np.abs(np.asarray(x, dtype=np.float64)), 448.0)
+    sign = (np.signbit(np.asarray(x, dtype=np.float64)).astype(np.uint8) << 7).astype(np.uint8)
+    u = a.view(np.uint64)
+    lsb = (u >> np.uint64(49)) & np.uint64(1)
+    rounded = (u + np.uint64((1 << 48) - 1) + lsb) >> np.uint64(49)
+    normal = a >= 2.0 ** -6
+    code_n = rounded.astype(np.int64) - ((1023 - 7) << 3)
+    code_s = np.rint(a * 512.0).astype(np.int64)
+    code = np.where(normal, code_n, code_s)
+    return np.minimum(code, 0x7E).astype(np.uint8) | sign
 
 
 def _draw_normal(rng: np.random.Generator, rows: int, cols: int, std: float) -> np.ndarray:
     return rng.normal(0.0, std, size=(rows, cols))
 
 
+def _encode_rows(w: np.ndarray, dtype: int, out: np.ndarray, scales, r0: int, r1: int) -> None:
+    if dtype == DT_F32:
+        out[r0:r1] = w.astype(np.float32)
+    elif dtype == DT_BF16:
+        out[r0:r1] = bf16_encode(w)
+    else:
+        s = (np.max(np.abs(w), axis=1) / 448.0).astype(np.float32)
+        s = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
+        scales[r0:r1] = s
+        out[r0:r1] = e4m3_encode(w / s.astype(np.float64)[:, None])
+
+
 def make_weight(N: int, K: int, dtype: int, rng: np.random.Generator):
     """Draw W[N,K] ~ N(0, 0.02) and encode it.  Returns (bits, scales-or-None).
 
-    Rows are drawn in chunks; PCG64 normal draws fill row-major, so the result
-    equals one (N, K) draw.
+    Rows are drawn in chunks, in order, from the one generator (PCG64 normal
+    draws fill row-major, so the result equals one (N, K) draw); the encoding
+    of finished chunks runs on worker threads while later chunks are drawn.
     """
     if dtype == DT_F32:
         out = np.empty((N, K), np.float32)
@@ -83,22 +93,22 @@ def make_weight(N: int, K: int, dtype: int, rng: np.random.Generator):
         out = np.empty((N, K), np.uint16)
     elif dtype == DT_FP8:
         out = np.empty((N, K), np.uint8)
-        scales = np.empty((N,), np.float32)
     else:
         raise ValueError(f"unknown dtype {dtype}")
-    for r0 in range(0, N, _ROW_CHUNK):
-        r1 = min(N, r0 + _ROW_CHUNK)
-        w = _draw_normal(rng, r1 - r0, K, 0.02)
-        if dtype == DT_F32:
-            out[r0:r1] = w.astype(np.float32)
-        elif dtype == DT_BF16:
-            out[r0:r1] = bf16_encode(w)
-        else:
-            s = (np.max(np.abs(w), axis=1) / 448.0).astype(np.float32)
-            s = np.where(s > 0, s, np.float32(1.0)).astype(np.float32)
-            scales[r0:r1] = s
-            out[r0:r1] = e4m3_encode(w / s.astype(np.float64)[:, None])
-    return out, (scales if dtype == DT_FP8 else None)
+    scales = np.empty((N,), np.float32) if dtype == DT_FP8 else None
+    workers = max(1, min(8, os.cpu_count() or 1))
+    with ThreadPoolExecutor(max_workers=workers) as pool:
+        futs = []
+        for r0 in range(0, N, _ROW_CHUNK):
+            r1 = min(N, r0 + _ROW_CHUNK)
+            w = _draw_normal(rng, r1 - r0, K, 0.02)
+            futs.append(pool.submit(_encode_rows, w, dtype, out, scales, r0, r1))
+            # bound the number of drawn-but-unencoded chunks held in memory
+            while len(futs) > 2 * workers:
+                futs.pop(0).result()
+        for f in futs:
+            f.result()
+    return out, scales
 
 
 def make_x(M: int, K: int, dtype: int, rng: np.random.Generator) -> np.ndarray:

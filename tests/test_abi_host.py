@@ -1,0 +1,87 @@
+"""Host-side checks of the C interface: the library loads, exports every
+function ``include/spense.h`` declares, and rejects bad arguments on the host
+before any HIP call (so these run without a GPU)."""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import sparse_dense_gemm_amd as sdg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE_PTR = 1 << 20  # never dereferenced: validation fails before any HIP call
+
+
+def header_functions():
+    names = set()
+    for fn in os.listdir(os.path.join(ROOT, "include")):
+        if not fn.endswith(".h"):
+            continue
+        src = open(os.path.join(ROOT, "include", fn)).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(spense_[a-z0-9_]+)\s*\(", src, re.M):
+            names.add(m.group(1))
+    return sorted(names)
+
+
+def test_library_exports_every_declared_function():
+    names = header_functions()
+    assert {"spense_pack", "spense_linear", "spense_free", "spense_export", "spense_info"} <= set(names)
+    lib = ctypes.CDLL(sdg.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_abi_version_and_strerror():
+    assert sdg.spense_abi_version() == 1
+    lib = sdg._lib()
+    for code in (0, -1, -2, -3, -4):
+        assert lib.spense_strerror(code)
+    assert lib.spense_strerror(12345) == b"unknown status"
+
+
+def _pack(W=FAKE_PTR, wdt=sdg.DT_FP8, N=64, K=128, ldw=None, scales=FAKE_PTR, cols=None, frac=0.25):
+    lib = sdg._lib()
+    h = ctypes.c_void_p()
+    cols_ptr, n = None, 0
+    keep = None
+    if cols is not None:
+        keep = np.ascontiguousarray(np.asarray(cols, dtype=np.int32))
+        cols_ptr, n = (keep.ctypes.data if keep.size else np.zeros(1, np.int32).ctypes.data), keep.size
+    st = lib.spense_pack(W, wdt, N, K, K if ldw is None else ldw, scales, cols_ptr, n, frac, None, ctypes.byref(h))
+    return st, h.value
+
+
+@pytest.mark.parametrize("kw", [
+    dict(W=None),                               # null weights
+    dict(wdt=7),                                # unknown dtype
+    dict(N=0), dict(K=0), dict(ldw=100),        # sizes
+    dict(scales=None),                          # e4m3 needs scales
+    dict(wdt=sdg.DT_BF16),                      # bf16 must not get scales
+    dict(frac=1.5), dict(frac=-0.1), dict(frac=float("nan")),
+    dict(K=130, frac=0.0),                      # K_s % 4 != 0
+    dict(cols=[1, 2, 3]),                       # K - 3 not a multiple of 4
+    dict(cols=[1, 1, 2, 3]),                    # duplicate
+    dict(cols=[-1, 1, 2, 3]), dict(cols=[128, 1, 2, 3]),  # out of range
+])
+def test_pack_rejects_bad_arguments(kw):
+    st, h = _pack(**kw)
+    assert st == sdg.SPENSE_EINVAL and not h
+
+
+def test_linear_rejects_bad_arguments():
+    lib = sdg._lib()
+    assert lib.spense_linear(None, FAKE_PTR, sdg.DT_BF16, 1, 128, FAKE_PTR, sdg.DT_F32, 64, None) == sdg.SPENSE_EINVAL
+    assert lib.spense_free(None) == sdg.SPENSE_EINVAL
+    assert lib.spense_info(None, None) == sdg.SPENSE_EINVAL
+    assert lib.spense_export(None, None, None, None, None, None, None) == sdg.SPENSE_EINVAL
+
+
+def test_binding_fails_loudly_without_library(monkeypatch):
+    monkeypatch.setattr(sdg, "_lib_handle", None)
+    monkeypatch.setattr(sdg, "LIB_PATH", "/nonexistent/libspense.so")
+    with pytest.raises(RuntimeError, match="not built"):
+        sdg.spense_abi_version()

@@ -1,0 +1,240 @@
+"""Parity of the HIP library (called through its C interface) with the oracle.
+
+* spense_pack: canonical export equals the oracle's packed form bit for bit.
+* spense_linear: every element within 1e-3 * sum_k |x_k w_k| of the oracle's
+  float64 result, compared on the fp32 output before any cast.
+Full workloads run at their real shapes; the oracle checks all rows for the
+single-layer workloads and a spread sample of row tiles (and of activation
+rows at M >= 256) for the large layer sets.
+"""
+
+import functools
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sparse_dense_gemm_amd as sdg
+import synth
+from synth import DT_BF16, DT_F32, DT_FP8
+
+from spense_gpu_util import (assert_pack_equal, export, linear_dev, log, oracle_pack_rows, pack_dev, to_dev,
+                             tol_ratio)
+
+pytestmark = pytest.mark.gpu
+
+WL = synth.WORKLOADS
+
+
+def _cases():
+    cases = []
+    for key, w in WL.items():
+        for spec in w.layers:
+            cases.append((spec.layer_index, spec.wdtype, key, spec.name))
+    # group equal layers (same seeds, same W) next to each other so inputs are reused
+    cases.sort(key=lambda c: (c[2].startswith("layer32b"), c[0], c[1], c[2]))
+    return [(c[2], c[3]) for c in cases]
+
+
+@functools.lru_cache(maxsize=1)
+def _weights(N, K, wdtype, layer_index, single):
+    spec = synth.LayerSpec("w", N, K, 0, wdtype, DT_F32 if wdtype == DT_F32 else DT_BF16, "tail", layer_index)
+    W, s, _, _ = synth.layer_inputs(spec, 1, single_stream=single)
+    return W, s
+
+
+def _sample_rows(N, big):
+    if not big:
+        return None
+    NT = (N + 15) // 16
+    tiles = np.unique(np.concatenate([np.linspace(0, NT - 1, 24).astype(np.int64), [0, NT - 1]]))
+    rows = np.concatenate([np.arange(16 * t, min(N, 16 * t + 16)) for t in tiles])
+    return rows
+
+
+@pytest.mark.parametrize("key,lname", _cases())
+def test_workload_parity(key, lname):
+    w = WL[key]
+    spec = next(s for s in w.layers if s.name == lname)
+    Mmax = max(w.Ms)
+    log(f"[parity] {key}/{lname} N={spec.N} K={spec.K} K_d={spec.K_d} wdtype={spec.wdtype} Ms={w.Ms}")
+    W, s = _weights(spec.N, spec.K, spec.wdtype, spec.layer_index, w.single_stream)
+    _, _, X, D = synth.layer_inputs(synth.LayerSpec(spec.name, 1, spec.K, spec.K_d, spec.wdtype, spec.xdtype,
+                                                    spec.dense, spec.layer_index), Mmax, single_stream=False)
+    if w.single_stream:
+        _, _, X, D = synth.layer_inputs(spec, Mmax, single_stream=True)
+    big = spec.N * spec.K > 40_000_000
+    rows = _sample_rows(spec.N, big)
+    Wd = to_dev(W, spec.wdtype)
+    sd = to_dev(s, DT_F32) if s is not None else None
+    h = pack_dev(Wd, spec.wdtype, sd, dense_cols=D)
+    try:
+        ref = oracle_pack_rows(W, spec.wdtype, D, rows)
+        got = export(h, spec.wdtype, rows)
+        assert_pack_equal(got, ref)
+        log(f"  pack bit-exact ({'all' if rows is None else len(rows)} rows)")
+        Xd = to_dev(X, spec.xdtype)
+        s_rows = None if s is None else (s if rows is None else s[rows])
+        for M in w.Ms:
+            Y = linear_dev(h, Xd[:M], spec.N).cpu().numpy()
+            mrows = np.arange(M) if M <= 128 else np.unique(np.concatenate(
+                [np.random.default_rng(M).choice(M, 62, replace=False), [0, M - 1]]))
+            Yref, B = oracle.linear_ref(X[mrows], spec.xdtype, ref, s_rows)
+            Yg = Y[mrows] if rows is None else Y[mrows][:, rows]
+            r = tol_ratio(Yg, Yref, B)
+            log(f"  M={M}: max err / (1e-3 * sum|xw|) = {r:.3e}")
+            assert r <= 1.0
+    finally:
+        sdg.spense_free(h)
+
+
+# ---------------------------------------------------------------------------
+# edge cases on small shapes
+# ---------------------------------------------------------------------------
+def _small(N, K, wdtype, seed):
+    rng = np.random.default_rng(seed)
+    W, s = synth.make_weight(N, K, wdtype, rng)
+    return W, s
+
+
+EDGE = [
+    # (N, K, wdtype, dense spec, Ms, splits)
+    (50, 200, DT_FP8, ("frac", 0.26), (1, 3, 17), (0, 1, 2)),       # ragged rows, K_s = 148 (not 128-aligned)
+    (64, 384, DT_FP8, ("rand", 96), (1, 16, 33, 65), (0, 1, 3)),   # gather path, several m-tiles
+    (48, 256, DT_BF16, ("frac", 0.25), (2, 31, 64, 100), (0, 1, 2)),
+    (40, 320, DT_BF16, ("rand", 80), (5,), (0, 2)),
+    (32, 256, DT_FP8, ("frac", 0.0), (1, 8), (0, 2)),                # pure 2:4
+    (32, 256, DT_FP8, ("frac", 1.0), (1, 8), (0, 2)),                # all dense (baseline form)
+    (24, 64, DT_BF16, ("frac", 0.5), (1, 7), (0, 1)),                # one macro-step each
+    (17, 512, DT_F32, ("frac", 0.25), (1, 4), (0,)),                 # fp32 path
+    (33, 100, DT_F32, ("rand", 20), (3,), (0,)),
+]
+
+
+@pytest.mark.parametrize("case", EDGE, ids=lambda c: f"N{c[0]}K{c[1]}dt{c[2]}{c[3][0]}{c[3][1]}")
+def test_edge_shapes(case):
+    N, K, wdtype, dense, Ms, splits_list = case
+    log(f"[edge] {case}")
+    W, s = _small(N, K, wdtype, 100 + N)
+    xdt = DT_F32 if wdtype == DT_F32 else DT_BF16
+    X = synth.make_x(max(Ms), K, xdt, np.random.default_rng(200 + K))
+    if dense[0] == "frac":
+        pi, K_s, K_d = oracle.resolve_dense_set(K, dense_fraction=dense[1])
+        D = np.sort(pi[K_s:])
+        h = pack_dev(to_dev(W, wdtype), wdtype, to_dev(s, DT_F32) if s is not None else None, dense_fraction=dense[1])
+    else:
+        D = synth.random_dense_set(K, dense[1], 300 + K)
+        h = pack_dev(to_dev(W, wdtype), wdtype, to_dev(s, DT_F32) if s is not None else None, dense_cols=D)
+    try:
+        ref = oracle_pack_rows(W, wdtype, D)
+        assert_pack_equal(export(h, wdtype), ref)
+        Xd = to_dev(X, xdt)
+        for M in Ms:
+            Yref, B = oracle.linear_ref(X[:M], xdt, ref, s)
+            for sp in splits_list:
+                Y = linear_dev(h, Xd[:M], N, splits=sp).cpu().numpy()
+                r = tol_ratio(Y, Yref, B)
+                log(f"  M={M} splits={sp}: ratio {r:.3e}")
+                assert r <= 1.0
+    finally:
+        sdg.spense_free(h)
+
+
+@pytest.mark.parametrize("wdtype", [DT_FP8, DT_BF16])
+def test_bf16_output_is_rne_of_fp32_output(wdtype):
+    N, K, M = 64, 512, 5
+    W, s = _small(N, K, wdtype, 7)
+    X = synth.make_x(M, K, DT_BF16, np.random.default_rng(8))
+    h = pack_dev(to_dev(W, wdtype), wdtype, to_dev(s, DT_F32) if s is not None else None, dense_fraction=0.25)
+    try:
+        Xd = to_dev(X, DT_BF16)
+        for sp in (1, 3):
+            y32 = linear_dev(h, Xd, N, DT_F32, splits=sp)
+            y16 = linear_dev(h, Xd, N, DT_BF16, splits=sp)
+            assert torch.equal(y32.to(torch.bfloat16).view(torch.int16), y16.view(torch.int16))
+    finally:
+        sdg.spense_free(h)
+
+
+@pytest.mark.parametrize("wdtype", [DT_FP8, DT_BF16])
+def test_one_hot_rows_are_exact(wdtype):
+    """X = rows of the identity: each output is one product, so the result is
+    s[n] * Wp[n, k] rounded once to fp32, bit for bit."""
+    N, K = 48, 256
+    W, s = _small(N, K, wdtype, 9)
+    D = synth.random_dense_set(K, 64, 10)
+    X = synth.bf16_encode(np.eye(K))
+    h = pack_dev(to_dev(W, wdtype), wdtype, to_dev(s, DT_F32) if s is not None else None, dense_cols=D)
+    try:
+        ref = oracle_pack_rows(W, wdtype, D)
+        Wp = oracle.decompress(ref)
+        expect = (Wp.T * (s.astype(np.float64)[None, :] if s is not None else 1.0)).astype(np.float32)
+        for sp in (1, 2):
+            Y = linear_dev(h, to_dev(X, DT_BF16), N, splits=sp).cpu().numpy()
+            assert np.array_equal(Y, expect)
+    finally:
+        sdg.spense_free(h)
+
+
+def test_gather_equals_contiguous_bitwise():
+    """(X, W, chosen set) and (X[:, pi], W[:, pi], tail) take the same K order: identical bits."""
+    N, K, M = 96, 1024, 9
+    W, s = _small(N, K, DT_FP8, 11)
+    D = synth.random_dense_set(K, 256, 12)
+    X = synth.make_x(M, K, DT_BF16, np.random.default_rng(13))
+    pi, K_s, K_d = oracle.resolve_dense_set(K, dense_cols=D)
+    sd = to_dev(s, DT_F32)
+    h1 = pack_dev(to_dev(W, DT_FP8), DT_FP8, sd, dense_cols=D)
+    h2 = pack_dev(to_dev(np.ascontiguousarray(W[:, pi]), DT_FP8), DT_FP8, sd, dense_fraction=K_d / K)
+    try:
+        assert sdg.spense_info(h1)["gather"] == 1 and sdg.spense_info(h2)["gather"] == 0
+        for sp in (1, 4):
+            y1 = linear_dev(h1, to_dev(X, DT_BF16), N, splits=sp)
+            y2 = linear_dev(h2, to_dev(np.ascontiguousarray(X[:, pi]), DT_BF16), N, splits=sp)
+            assert torch.equal(y1, y2)
+    finally:
+        sdg.spense_free(h1)
+        sdg.spense_free(h2)
+
+
+def test_power_of_two_scaling_and_determinism():
+    N, K, M = 80, 768, 12
+    W, s = _small(N, K, DT_FP8, 14)
+    X = synth.make_x(M, K, DT_BF16, np.random.default_rng(15))
+    h = pack_dev(to_dev(W, DT_FP8), DT_FP8, to_dev(s, DT_F32), dense_fraction=0.25)
+    try:
+        Xd = to_dev(X, DT_BF16)
+        for sp in (1, 5):
+            y = linear_dev(h, Xd, N, splits=sp)
+            y_again = linear_dev(h, Xd, N, splits=sp)
+            assert torch.equal(y, y_again)
+            y4 = linear_dev(h, (Xd.float() * 4.0).to(torch.bfloat16), N, splits=sp)
+            assert torch.equal(y4, y * 4.0)
+    finally:
+        sdg.spense_free(h)
+
+
+def test_non_default_stream_and_strided_operands():
+    N, K, M = 64, 512, 6
+    W, s = _small(N, K, DT_FP8, 16)
+    X = synth.make_x(M, K, DT_BF16, np.random.default_rng(17))
+    D = synth.random_dense_set(K, 128, 18)
+    Wbig = torch.zeros((N, K + 64), dtype=torch.uint8, device="cuda")
+    Wbig[:, :K] = to_dev(W, DT_FP8)
+    st = torch.cuda.Stream()
+    with torch.cuda.stream(st):
+        h = sdg.spense_pack(Wbig, DT_FP8, scales=to_dev(s, DT_F32), dense_cols=D, K=K, ldw=K + 64, stream=st)
+        Xbig = torch.zeros((M, K + 24), dtype=torch.bfloat16, device="cuda")
+        Xbig[:, :K] = to_dev(X, DT_BF16)
+        Ybig = torch.full((M, N + 8), -7.0, dtype=torch.float32, device="cuda")
+        sdg.spense_linear(h, Xbig, Ybig, M=M, ldx=K + 24, ldy=N + 8, stream=st)
+    st.synchronize()
+    try:
+        ref = oracle_pack_rows(W, DT_FP8, D)
+        Yref, B = oracle.linear_ref(X, DT_BF16, ref, s)
+        Yb = Ybig.cpu().numpy()
+        assert tol_ratio(Yb[:, :N], Yref, B) <= 1.0
+        assert np.all(Yb[:, N:] == -7.0)  # padding columns untouched
+    finally:
+        sdg.spense_free(h)
