@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--splits", type=int, default=0, help="force the split-K factor (0 = automatic)")
     ap.add_argument("--ms", type=str, default="", help="override batch sizes, e.g. 1,4,16")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed region, run a plain 512 MiB device copy (reference for HBM byte counters)")
     return ap.parse_args()
 
 
@@ -86,7 +88,7 @@ def main():
     Xd = torch.from_numpy(X.view(np.int16)).to(dev).view(torch.bfloat16)
     stream = torch.cuda.current_stream()
 
-    # ---- pack (a1..a3): once per weight; timed on its own ----
+    # ---- pack: once per weight; timed on its own ----
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     h0 = sdg.spense_pack(Wd, sdg.DT_FP8, scales=sd, dense_cols=D)
@@ -95,7 +97,7 @@ def main():
     wbytes = info["weight_bytes"]
     copies = max(4, -(-2 * MALL_BYTES // info["device_bytes"]) + 1)
     handles = [h0] + [sdg.spense_pack(Wd, sdg.DT_FP8, scales=sd, dense_cols=D) for _ in range(copies - 1)]
-    # all-dense baseline (a8): same kernel template with K_s = 0
+    # all-dense baseline: same kernel template with K_s = 0
     hd0 = sdg.spense_pack(Wd, sdg.DT_FP8, scales=sd, dense_fraction=1.0)
     dinfo = sdg.spense_info(hd0)
     dcopies = max(4, -(-2 * MALL_BYTES // dinfo["device_bytes"]) + 1)
@@ -158,6 +160,14 @@ def main():
 
     for hh in handles + dhandles:
         sdg.spense_free(hh)
+    if args.copy_calibration:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(2):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -8,6 +8,8 @@
 // columns ascending, which moves the chosen set into one contiguous block.
 #include <algorithm>
 #include <cmath>
+#include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <new>
 #include <vector>
@@ -159,7 +161,8 @@ int spense_pack(const void* W, int32_t wdtype, int64_t N, int64_t K, int64_t ldw
     d.n_dm = (K_d + kMacro - 1) / kMacro;
     d.K_sp = d.n_sm * kMacro;
     d.K_p = d.K_sp + d.n_dm * kMacro;
-    d.tile_bytes = d.n_sm * sparse_block_bytes(wdtype) + d.n_dm * dense_block_bytes(wdtype);
+    d.idx_off = (d.n_sm + 2 * d.n_dm) * unit_bytes(wdtype);
+    d.tile_bytes = d.idx_off + d.n_sm * kIdxBlock;
     bool identity = (K_s % kMacro == 0) && (K_d % kMacro == 0);
     for (int64_t c = 0; identity && c < K; ++c) identity = h->pi_host[(size_t)c] == c;
     d.gather = identity ? 0 : 1;
@@ -203,16 +206,61 @@ int spense_pack(const void* W, int32_t wdtype, int64_t N, int64_t K, int64_t ldw
   return SPENSE_OK;
 }
 
+// Optional tuning override "waves,depth" (e.g. "8,8") for the decode kernel.
+static bool decode_override(int& waves, int& depth) {
+  const char* e = std::getenv("SPENSE_DECODE");
+  if (!e || !*e) return false;
+  int w = 0, dp = 0;
+  if (std::sscanf(e, "%d,%d", &w, &dp) != 2) return false;
+  if ((w != 4 && w != 8) || (dp != 4 && dp != 8)) return false;
+  waves = w;
+  depth = dp;
+  return true;
+}
+
+static int64_t decode_lds_bytes(const LayerDesc& d, int64_t M, int64_t S) {
+  const int64_t steps = (d.n_sm + S - 1) / S + (d.n_dm + S - 1) / S;
+  return M * (steps * kMacro + 8) * 2;
+}
+
 static int plan_linear(const spense_layer* h, int64_t M, int32_t splits, LinearPlan& p) {
   const LayerDesc& d = h->d;
+  const int64_t steps = std::max<int64_t>(d.n_sm, d.n_dm);
+  const int64_t max_splits = std::max<int64_t>(1, std::min<int64_t>(steps, 64));
+  if (splits < 0 || splits > max_splits) return SPENSE_EINVAL;
+  p = LinearPlan{};
+  if (M <= 16) {
+    // decode: one 16-row m-tile, weights streamed through a register ring
+    p.decode = 1;
+    p.mt = 1;
+    p.mgroups = 1;
+    // 8 waves per workgroup, 4 units in flight per wave; one split when the
+    // row tiles alone give enough waves (each split adds a partial-sum
+    // handshake at the end of the kernel), else about 1280 waves
+    p.waves = 8;
+    p.depth = 4;
+    int w, dp;
+    if (decode_override(w, dp)) {
+      p.waves = w;
+      p.depth = dp;
+    }
+    p.rgroups = (int)((d.NT + p.waves - 1) / p.waves);
+    int64_t S = splits;
+    if (S == 0) {
+      S = d.NT >= 1024 ? 1 : std::max<int64_t>(1, (1280 + d.NT - 1) / d.NT);
+      S = std::min<int64_t>(S, max_splits);
+      while (S < max_splits && decode_lds_bytes(d, M, S) > 64 * 1024) ++S;
+    }
+    p.splits = (int)S;
+    p.lds_bytes = (int)decode_lds_bytes(d, M, S);
+    if (p.lds_bytes <= 64 * 1024) return SPENSE_OK;
+    // the forced split leaves too much to stage: use the chunked kernel
+  }
+  p.decode = 0;
   p.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
   p.mgroups = (int)((M + 16 * p.mt - 1) / (16 * p.mt));
   p.rgroups = (int)((d.NT + kWavesPerWG - 1) / kWavesPerWG);
-  const int64_t steps = std::max<int64_t>(d.n_sm, d.n_dm);
-  const int64_t max_splits = std::max<int64_t>(1, std::min<int64_t>(steps, 64));
-  if (splits < 0) return SPENSE_EINVAL;
   if (splits > 0) {
-    if (splits > max_splits) return SPENSE_EINVAL;
     p.splits = splits;
     return SPENSE_OK;
   }
@@ -243,15 +291,17 @@ int spense_linear_splits(spense_handle h, const void* X, int32_t xdtype, int64_t
   if (d.wdtype == SPENSE_F32) {
     if (splits > 1) return SPENSE_EINVAL;
     a.splits = 1;
-    LinearPlan p{1, 1, 1, 1};
+    LinearPlan p{};
+    p.mt = p.mgroups = p.rgroups = p.splits = 1;
     hipError_t e = launch_linear(d, a, p, s);
     return e == hipSuccess ? SPENSE_OK : hip_fail(e);
   }
   LinearPlan p{};
+  const bool x_aligned = aligned16(X) && (ldx % 8) == 0;
   int rc = plan_linear(h, M, splits, p);
   if (rc != SPENSE_OK) return rc;
   a.splits = p.splits;
-  a.gather = d.gather || !aligned16(X) || (ldx % 8) != 0;
+  a.gather = d.gather || !x_aligned;
   if (p.splits > 1) {
     const size_t need = (size_t)p.splits * (size_t)M * (size_t)(d.NT * kRowTile) * 4;
     const size_t need_cnt = (size_t)p.rgroups * (size_t)p.mgroups;

@@ -1,30 +1,32 @@
 // Internal declarations shared by the host API (spense_api.cpp) and the HIP
 // kernels (spense_kernels.hip).  Not part of the public interface.
 //
-// Device-resident packed form ("fragment layout") for bf16 / e4m3 weights.
+// Device-resident packed form ("unit layout") for bf16 / e4m3 weights.
 //
-// Output rows are grouped in row tiles of 16 (one MFMA tile).  The permuted
-// activation X'p is the padded column order: sparse columns pi[0..K_s) padded
-// with zero columns to K_sp = 128*n_sm, then dense columns pi[K_s..K) padded to
-// 128*n_dm.  Work proceeds in macro-steps of 128 X'p columns = two 64-column
-// MFMA steps q = 0, 1.  For a 64-column step at X'p column k0, lane l of a wave
-// (r = l % 16, g = l / 16) uses:
-//   B operand (activations): X'p[m = l%16][k0 + 16g + t], t = 0..15.
-//   sparse A (v_smfmac_f32_16x16x64_bf16): row r, eight kept values covering
-//     four 2:4 groups; slot pair j (0..3) is group k0/4 + gl(g, j) with
-//     gl(g, j) = ((g&1)*2 + (j>>1))*4 + (g>>1)*2 + (j&1); the pair's 2-bit
-//     indices sit at bits 4j..4j+3 of the step's 16-bit index half (abid = q).
-//   dense A (two v_mfma_f32_16x16x32_bf16): row r, dense columns
-//     k0 + 16g + t; t = 0..7 pairs with B t = 0..7, t = 8..15 with B t = 8..15.
-//
-// Per row tile, blocks are stored sparse macro-steps first, then dense ones:
-//   e4m3 sparse block (1280 B): [64 lanes][16 B values: step0 slots 0..7, step1 slots 0..7]
-//                               [64 lanes][4 B index dword: step0 bits 0..15, step1 bits 16..31]
-//   bf16 sparse block (2304 B): [step q][64 lanes][16 B = 8 values] x2, then [64 lanes][4 B]
-//   e4m3 dense block (2048 B):  [step q][64 lanes][16 B = 16 values]
-//   bf16 dense block (4096 B):  [step q][half h][64 lanes][16 B = 8 values, t = 8h..8h+7]
-// Padding rows, padding groups and padding columns hold zero values (sparse
-// padding groups use indices (0, 1)).
+// Output rows are grouped in row tiles of 16 (one matrix-instruction tile).
+// The permuted activation X'p is the padded column order: sparse columns
+// pi[0..K_s) padded with zero columns to K_sp = 128*n_sm, then dense columns
+// pi[K_s..K) padded to 128*n_dm.  Both regions run on
+// v_smfmac_f32_16x16x64_bf16.  For a 64-column step at X'p column k0, lane l
+// of a wave (r = l % 16, g = l / 16) supplies:
+//   B (activations): X'p[m = l%16][k0 + 16g + t], t = 0..15;
+//   A (weights of row r): eight values, slot pair j (0..3) covering the 2:4
+//     group gl(g, j) = ((g&1)*2 + (j>>1))*4 + (g>>1)*2 + (j&1) of the step,
+//     with the pair's two 2-bit positions in bits 4j..4j+3 of the 16-bit index
+//     half selected by abid.
+// A "unit" holds the A operands of two SMFMACs for every lane (16 values per
+// lane: A0 = values 0..7, A1 = values 8..15):
+//   sparse unit i (X'p columns 128i..128i+127): A0 = step q=0, A1 = step q=1,
+//     plus one index dword per lane (step 0 in bits 0..15, step 1 in 16..31);
+//   dense unit t (dense columns 64t..64t+63, one step): A0 = the values at
+//     group positions 0 and 1, A1 = positions 2 and 3, with the fixed index
+//     word 0xEEEE4444 (abid 0 -> 0x4444, abid 1 -> 0xEEEE), i.e. a dense
+//     16x64 block is exactly two structured-sparse products.
+// Unit bytes: e4m3 1024 ([64 lanes][16 B]); bf16 2048 ([A0: 64 lanes x 16 B]
+// [A1: 64 lanes x 16 B]).  Per row tile: [n_sm sparse units][2*n_dm dense
+// units][n_sm index blocks of 64 lanes x 4 B], so every wave streams whole
+// 1 KB (e4m3) or 2 KB (bf16) units.  Padding rows, groups and columns hold
+// zero values (sparse padding groups use positions (0, 1)).
 //
 // fp32 weights keep the canonical packed form on the device (vals [N][K_s/2],
 // meta [N][ceil(K_s/32)], dense [N][K_d]) and run on a VALU kernel, since the
@@ -41,8 +43,8 @@ enum : int32_t { DT_F32 = 0, DT_BF16 = 1, DT_FP8 = 2 };
 constexpr int kRowTile = 16;   // output rows per MFMA tile
 constexpr int kMacro = 128;    // X'p columns per macro-step
 
-inline constexpr int64_t sparse_block_bytes(int32_t wdt) { return wdt == DT_FP8 ? 1280 : 2304; }
-inline constexpr int64_t dense_block_bytes(int32_t wdt) { return wdt == DT_FP8 ? 2048 : 4096; }
+inline constexpr int64_t unit_bytes(int32_t wdt) { return wdt == DT_FP8 ? 1024 : 2048; }
+constexpr int64_t kIdxBlock = 256;  // index dwords of one sparse unit (64 lanes x 4 B)
 
 struct LayerDesc {
   int64_t N, K, K_s, K_d;
@@ -52,8 +54,9 @@ struct LayerDesc {
   int64_t n_sm, n_dm;    // sparse / dense macro-steps
   int64_t K_sp;          // 128 * n_sm, first dense column of X'p
   int64_t K_p;           // K_sp + 128 * n_dm
-  int64_t tile_bytes;    // n_sm * sparse_block_bytes + n_dm * dense_block_bytes
-  uint8_t* wpack;        // fragment layout, NT * tile_bytes bytes
+  int64_t tile_bytes;    // (n_sm + 2 n_dm) * unit_bytes + n_sm * kIdxBlock
+  int64_t idx_off;       // offset of the index blocks within a row tile
+  uint8_t* wpack;        // unit layout, NT * tile_bytes bytes
   const float* scales;   // [NT * 16] (e4m3) or nullptr
   const int32_t* pi;     // [K]
   const int32_t* pip;    // [K_p] padded column map
@@ -80,8 +83,13 @@ struct LinearArgs {
 struct LinearPlan {
   int mt;        // m-tiles (16 rows of X each) per workgroup pass: 1, 2 or 4
   int mgroups;   // ceil(M / (16 * mt))
-  int rgroups;   // ceil(NT / waves_per_wg)
+  int rgroups;   // ceil(NT / waves per workgroup)
   int splits;
+  // decode path (M <= 16)
+  int decode;    // 1: linear_decode_kernel
+  int waves;     // waves per workgroup: 4 or 8
+  int depth;     // macro-steps in flight per wave: 4 or 8
+  int lds_bytes; // dynamic LDS of the decode kernel
 };
 
 constexpr int kWavesPerWG = 4;

@@ -3,7 +3,7 @@
 // Method: SpenseGPT gist.science explainer, Technical Summary 2.A (a 2:4
 // region and a dense region along K, input-split with accumulation into one
 // output) and 2.B (dense set = last p% or a chosen set permuted into the dense
-// block).  The fragment layout these kernels read and write is described in
+// block).  The unit layout these kernels read and write is described in
 // spense_internal.h.
 #include "spense_internal.h"
 
@@ -16,14 +16,24 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// Index word of a dense unit: abid 0 reads 0x4444 (slots at group positions 0
+// and 1), abid 1 reads 0xEEEE (positions 2 and 3).
+constexpr uint32_t kDenseIdx = 0xEEEE4444u;
+
 // ---------------------------------------------------------------------------
-// shared helpers
+// helpers
 // ---------------------------------------------------------------------------
 
-// Group of a 64-column step that slot pair j of lane group g covers (see the
-// layout notes in spense_internal.h).
+// Group of a 64-column step that slot pair j of lane group g covers.
 __device__ __forceinline__ int group_local(int g, int j) {
   return ((((g & 1) << 1) + (j >> 1)) << 2) + ((g >> 1) << 1) + (j & 1);
+}
+
+// Inverse of group_local: group gl (0..15) -> (lane group g, pair j).
+__device__ __forceinline__ void group_owner(int gl, int& g, int& j) {
+  const int hi2 = gl >> 2, mid = (gl >> 1) & 1, lo1 = gl & 1;
+  g = (mid << 1) | (hi2 >> 1);
+  j = ((hi2 & 1) << 1) | lo1;
 }
 
 __device__ __forceinline__ uint32_t mag_key(uint8_t w) { return w & 0x7Fu; }
@@ -79,6 +89,87 @@ __device__ __forceinline__ bf16x16 as_bf16x16(u32x4 lo, u32x4 hi) {
   return __builtin_bit_cast(bf16x16, w);
 }
 
+// Structured-sparse matrix instruction.  Its destination is tied to the
+// accumulator input, which is live across the instruction, so the destination
+// can never share registers with the A or B operands (a matrix instruction
+// whose destination overlaps srcA/srcB gives wrong results; tests/test_isa.py
+// checks the built code for that).
+template <int ABID>
+__device__ __forceinline__ f32x4 smfmac_bf16(const bf16x8& a, const bf16x16& b, const f32x4& c, int idx) {
+  return __builtin_amdgcn_smfmac_f32_16x16x64_bf16(a, b, c, idx, 0, ABID);
+}
+
+// Split-K handshake without cache maintenance.  Partials are written and read
+// with device-scope accesses (coherent at the device level, so no L2
+// write-back or invalidate is needed); each thread waits until its partial
+// stores have completed before the workgroup's arrival is counted, and the
+// workgroup that arrives last reads every partial.
+__device__ __forceinline__ void store_partial(float* p, const f32x4& v) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) __hip_atomic_store(p + r, v[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ f32x4 load_partial(const float* p) {
+  f32x4 v;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) v[r] = __hip_atomic_load(p + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return v;
+}
+
+// Returns true in every thread of the last-arriving workgroup; that workgroup
+// also rearms the counter for the next launch.
+__device__ __forceinline__ bool arrive_last(int32_t* cnt, int S, int* flag) {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const int old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *flag = (old == S - 1);
+    if (old == S - 1) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  return *flag != 0;
+}
+
+__device__ __forceinline__ void store_y(const LayerDesc& d, const LinearArgs& a, int64_t m, int64_t n, float acc) {
+  const float y = acc * (d.scales ? d.scales[n] : 1.0f);
+  if (a.ydtype == DT_F32) ((float*)a.Y)[m * a.ldy + n] = y;
+  else ((uint16_t*)a.Y)[m * a.ldy + n] = (uint16_t)bf16_rne(y);
+}
+
+// Writes Y (S == 1) or this split's partial; with S > 1 the last workgroup of
+// the tile adds the partials in split order.  acc: lane l, register r =
+// Y^T[n = 16rt + 4(l/16) + r][m = m0 + 16mt + l%16].
+__device__ __forceinline__ void finish_tile(const LayerDesc& d, const LinearArgs& a, const f32x4* acc, int mtiles,
+                                            int64_t rt, bool active, int64_t m0, int s, int S, int64_t cnt_index,
+                                            int* last_flag) {
+  const int lane = threadIdx.x & 63;
+  const int nb = 4 * (lane >> 4);
+  const int64_t NP = d.NT * 16;
+  if (S > 1) {
+    if (active)
+      for (int mt = 0; mt < mtiles; ++mt) {
+        const int64_t m = m0 + 16 * mt + (lane & 15);
+        if (m < a.M) store_partial(a.ws + ((int64_t)s * a.M + m) * NP + rt * 16 + nb, acc[mt]);
+      }
+    if (!arrive_last(a.counters + cnt_index, S, last_flag)) return;
+  }
+  if (!active) return;
+  for (int mt = 0; mt < mtiles; ++mt) {
+    const int64_t m = m0 + 16 * mt + (lane & 15);
+    if (m >= a.M) continue;
+    f32x4 sum = acc[mt];
+    if (S > 1) {
+      sum = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int s2 = 0; s2 < S; ++s2) sum += load_partial(a.ws + ((int64_t)s2 * a.M + m) * NP + rt * 16 + nb);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int64_t n = rt * 16 + nb + r;
+      if (n < d.N) store_y(d, a, m, n, sum[r]);
+    }
+  }
+}
+
 template <typename WT>
 __device__ __forceinline__ u32x4 pack16(const WT* v, int first);
 
@@ -103,17 +194,32 @@ __device__ __forceinline__ u32x4 pack16<uint16_t>(const uint16_t* v, int first) 
 }
 
 template <typename WT>
-constexpr int64_t kSparseBlock = sizeof(WT) == 1 ? 1280 : 2304;
+constexpr int64_t kUnit = sizeof(WT) == 1 ? 1024 : 2048;
+
+// One unit = one lane's A operands of two SMFMACs: 16 values v[0..15], A0 =
+// v[0..7], A1 = v[8..15].  e4m3: 16 B at +16 lane; bf16: A0 at +16 lane, A1 at
+// +1024 + 16 lane.
 template <typename WT>
-constexpr int64_t kDenseBlock = sizeof(WT) == 1 ? 2048 : 4096;
+__device__ __forceinline__ void store_unit(uint8_t* unit, int lane, const WT* v) {
+  if constexpr (sizeof(WT) == 1) {
+    *(u32x4*)(unit + 16 * lane) = pack16<WT>(v, 0);
+  } else {
+    *(u32x4*)(unit + 16 * lane) = pack16<WT>(v, 0);
+    *(u32x4*)(unit + 1024 + 16 * lane) = pack16<WT>(v, 8);
+  }
+}
+
 template <typename WT>
-constexpr int64_t kIdxOffset = sizeof(WT) == 1 ? 1024 : 2048;
+__device__ __forceinline__ WT unit_value(const uint8_t* unit, int lane, int slot) {
+  if constexpr (sizeof(WT) == 1) return unit[16 * lane + slot];
+  else return ((const uint16_t*)(unit + (slot >> 3) * 1024 + 16 * lane))[slot & 7];
+}
 
 // ---------------------------------------------------------------------------
-// pack: 2:4 selection + compression into the fragment layout (bf16 / e4m3)
+// pack: 2:4 selection + compression into the unit layout (bf16 / e4m3)
 // ---------------------------------------------------------------------------
 
-// One thread per (row tile, sparse macro-step, lane): eight groups of one row.
+// One thread per (row tile, sparse unit, lane): eight groups of one row.
 template <typename WT>
 __global__ void pack_sparse_kernel(LayerDesc d, const WT* __restrict__ W, int64_t ldw) {
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -151,42 +257,33 @@ __global__ void pack_sparse_kernel(LayerDesc d, const WT* __restrict__ W, int64_
       v[8 * q + 2 * j + 1] = b;
     }
   }
-  uint8_t* blk = d.wpack + rt * d.tile_bytes + i * kSparseBlock<WT>;
-  if constexpr (sizeof(WT) == 1) {
-    *(u32x4*)(blk + 16 * lane) = pack16<WT>(v, 0);
-  } else {
-    *(u32x4*)(blk + 16 * lane) = pack16<WT>(v, 0);
-    *(u32x4*)(blk + 1024 + 16 * lane) = pack16<WT>(v, 8);
-  }
-  *(uint32_t*)(blk + kIdxOffset<WT> + 4 * lane) = idx;
+  uint8_t* tile = d.wpack + rt * d.tile_bytes;
+  store_unit<WT>(tile + i * kUnit<WT>, lane, v);
+  *(uint32_t*)(tile + d.idx_off + i * 256 + 4 * lane) = idx;
 }
 
-// One thread per (row tile, dense macro-step, lane): 2 x 16 dense values of one row.
+// One thread per (row tile, dense unit = 64 dense columns, lane).
 template <typename WT>
 __global__ void pack_dense_kernel(LayerDesc d, const WT* __restrict__ W, int64_t ldw) {
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= d.NT * d.n_dm * 64) return;
+  const int64_t units = 2 * d.n_dm;
+  if (gid >= d.NT * units * 64) return;
   const int lane = (int)(gid & 63);
   const int64_t rest = gid >> 6;
-  const int64_t i = rest % d.n_dm, rt = rest / d.n_dm;
+  const int64_t t = rest % units, rt = rest / units;
   const int r = lane & 15, g = lane >> 4;
   const int64_t n = rt * 16 + r;
-  uint8_t* blk = d.wpack + rt * d.tile_bytes + d.n_sm * kSparseBlock<WT> + i * kDenseBlock<WT>;
+  WT v[16];
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    WT v[16];
+  for (int half = 0; half < 2; ++half)
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
-      const int64_t c = 128 * i + 64 * q + 16 * g + t;
-      v[t] = (n < d.N && c < d.K_d) ? W[n * ldw + d.pi[d.K_s + c]] : (WT)0;
-    }
-    if constexpr (sizeof(WT) == 1) {
-      *(u32x4*)(blk + q * 1024 + 16 * lane) = pack16<WT>(v, 0);
-    } else {
-      *(u32x4*)(blk + q * 2048 + 16 * lane) = pack16<WT>(v, 0);
-      *(u32x4*)(blk + q * 2048 + 1024 + 16 * lane) = pack16<WT>(v, 8);
-    }
-  }
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int w = 0; w < 2; ++w) {
+        const int64_t c = 64 * t + 4 * group_local(g, j) + 2 * half + w;
+        v[8 * half + 2 * j + w] = (n < d.N && c < d.K_d) ? W[n * ldw + d.pi[d.K_s + c]] : (WT)0;
+      }
+  store_unit<WT>(d.wpack + rt * d.tile_bytes + (d.n_sm + t) * kUnit<WT>, lane, v);
 }
 
 // fp32: canonical form.  One thread per (row, meta word) for the sparse part.
@@ -221,7 +318,7 @@ __global__ void pack_f32_dense_kernel(LayerDesc d, const uint32_t* __restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-// export: fragment layout -> canonical form
+// export: unit layout -> canonical form
 // ---------------------------------------------------------------------------
 template <typename WT>
 __global__ void export_sparse_kernel(LayerDesc d, WT* __restrict__ vals, uint32_t* __restrict__ meta,
@@ -231,29 +328,21 @@ __global__ void export_sparse_kernel(LayerDesc d, WT* __restrict__ vals, uint32_
   const int64_t n = gid / d.meta_words, w = gid % d.meta_words;
   const int64_t rt = n / 16;
   const int r = (int)(n % 16);
+  const uint8_t* tile = d.wpack + rt * d.tile_bytes;
   uint32_t word = 0;
   for (int jj = 0; jj < 8; ++jj) {
     const int64_t G = 8 * w + jj;
     if (4 * G >= d.K_s) break;
     const int64_t i = G / 32;
     const int q = (int)((G % 32) / 16);
-    const int gl = (int)(G % 16);
-    const int hi2 = gl >> 2, mid = (gl >> 1) & 1, lo1 = gl & 1;
-    const int g = (mid << 1) | (hi2 >> 1);
-    const int j = ((hi2 & 1) << 1) | lo1;
+    int g, j;
+    group_owner((int)(G % 16), g, j);
     const int lane = 16 * g + r;
-    const uint8_t* blk = d.wpack + rt * d.tile_bytes + i * kSparseBlock<WT>;
-    const uint32_t idx = *(const uint32_t*)(blk + kIdxOffset<WT> + 4 * lane);
+    const uint32_t idx = *(const uint32_t*)(tile + d.idx_off + i * 256 + 4 * lane);
     const uint32_t nib = (idx >> (16 * q + 4 * j)) & 15u;
-    WT v0, v1;
-    if constexpr (sizeof(WT) == 1) {
-      v0 = blk[16 * lane + 8 * q + 2 * j];
-      v1 = blk[16 * lane + 8 * q + 2 * j + 1];
-    } else {
-      const uint16_t* h = (const uint16_t*)(blk + q * 1024 + 16 * lane);
-      v0 = h[2 * j];
-      v1 = h[2 * j + 1];
-    }
+    const uint8_t* unit = tile + i * kUnit<WT>;
+    const WT v0 = unit_value<WT>(unit, lane, 8 * q + 2 * j);
+    const WT v1 = unit_value<WT>(unit, lane, 8 * q + 2 * j + 1);
     if (vals) {
       vals[n * (d.K_s / 2) + 2 * G] = v0;
       vals[n * (d.K_s / 2) + 2 * G + 1] = v1;
@@ -274,17 +363,14 @@ __global__ void export_dense_kernel(LayerDesc d, WT* __restrict__ dense) {
   const int64_t n = gid / d.K_d, c = gid % d.K_d;
   const int64_t rt = n / 16;
   const int r = (int)(n % 16);
-  const int64_t i = c / 128;
-  const int q = (int)((c % 128) / 64), g = (int)((c % 64) / 16), t = (int)(c % 16);
+  const int64_t t = c / 64;
+  const int cc = (int)(c % 64);
+  int g, j;
+  group_owner(cc >> 2, g, j);
+  const int pos = cc & 3;
   const int lane = 16 * g + r;
-  const uint8_t* blk = d.wpack + rt * d.tile_bytes + d.n_sm * kSparseBlock<WT> + i * kDenseBlock<WT>;
-  WT v;
-  if constexpr (sizeof(WT) == 1) {
-    v = blk[q * 1024 + 16 * lane + t];
-  } else {
-    v = ((const uint16_t*)(blk + q * 2048 + (t >> 3) * 1024 + 16 * lane))[t & 7];
-  }
-  dense[n * d.K_d + c] = v;
+  const uint8_t* unit = d.wpack + rt * d.tile_bytes + (d.n_sm + t) * kUnit<WT>;
+  dense[n * d.K_d + c] = unit_value<WT>(unit, lane, 8 * (pos >> 1) + 2 * j + (pos & 1));
 }
 
 // fp32 canonical form: vals / meta / dense are stored as exported; only the mask is derived.
@@ -298,11 +384,86 @@ __global__ void export_f32_mask_kernel(LayerDesc d, uint8_t* __restrict__ mask) 
 }
 
 // ---------------------------------------------------------------------------
-// linear: SMFMAC (sparse region) + MFMA (dense region) into one accumulator
+// linear, shared pieces
+// ---------------------------------------------------------------------------
+
+// One lane's unit in registers: A operands of two SMFMACs and the index word.
+template <typename WT>
+struct UnitFrag;
+template <>
+struct UnitFrag<uint8_t> {
+  u32x4 a;
+  uint32_t idx;
+};
+template <>
+struct UnitFrag<uint16_t> {
+  u32x4 a0, a1;
+  uint32_t idx;
+};
+
+// Loads one unit.  The index load is issued for dense units too (from the
+// unit itself, a cached address) and its value replaced by the dense index
+// word at use, so sparse and dense units issue the same loads.
+template <typename WT>
+__device__ __forceinline__ void load_unit(UnitFrag<WT>& f, const uint8_t* unit, const uint8_t* idx_addr, int lane) {
+  if constexpr (sizeof(WT) == 1) {
+    f.a = *(const u32x4*)(unit + 16 * lane);
+  } else {
+    f.a0 = *(const u32x4*)(unit + 16 * lane);
+    f.a1 = *(const u32x4*)(unit + 1024 + 16 * lane);
+  }
+  f.idx = *(const uint32_t*)idx_addr;
+}
+
+// Two SMFMACs: A0 with B0 (index half 0), A1 with B1 (index half 1).
+template <typename WT>
+__device__ __forceinline__ void mac_unit(f32x4& acc0, f32x4& acc1, const UnitFrag<WT>& f, int idx, const bf16x16& B0,
+                                         const bf16x16& B1) {
+  bf16x8 A0, A1;
+  if constexpr (sizeof(WT) == 1) {
+    A0 = fp8x8_to_bf16(f.a.x, f.a.y);
+    A1 = fp8x8_to_bf16(f.a.z, f.a.w);
+  } else {
+    A0 = as_bf16x8(f.a0);
+    A1 = as_bf16x8(f.a1);
+  }
+  acc0 = smfmac_bf16<0>(A0, B0, acc0, idx);
+  acc1 = smfmac_bf16<1>(A1, B1, acc1, idx);
+}
+
+// B operand (16 activations of one lane) from a staged row: 32 contiguous bytes.
+__device__ __forceinline__ bf16x16 lds_b(const uint16_t* p) {
+  return as_bf16x16(*(const u32x4*)p, *(const u32x4*)(p + 8));
+}
+
+// Eight activations of row xr at the column indices i0, i1 (negative: zero).
+__device__ __forceinline__ u32x4 gather8_from(const uint16_t* xr, const u32x4& i0, const u32x4& i1) {
+  const int src[8] = {(int)i0.x, (int)i0.y, (int)i0.z, (int)i0.w, (int)i1.x, (int)i1.y, (int)i1.z, (int)i1.w};
+  uint32_t h[8];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) h[t] = xr[src[t] >= 0 ? src[t] : 0];
+#pragma unroll
+  for (int t = 0; t < 8; ++t) h[t] = src[t] >= 0 ? h[t] : 0u;
+  u32x4 val;
+  val.x = h[0] | (h[1] << 16);
+  val.y = h[2] | (h[3] << 16);
+  val.z = h[4] | (h[5] << 16);
+  val.w = h[6] | (h[7] << 16);
+  return val;
+}
+
+// Gathers 8 activations X'p[row][col..col+8) (col a multiple of 8).
+__device__ __forceinline__ u32x4 gather8(const LinearArgs& a, const LayerDesc& d, const uint16_t* xr, int64_t col) {
+  if (!a.gather) return *(const u32x4*)(xr + col);
+  return gather8_from(xr, *(const u32x4*)(d.pip + col), *(const u32x4*)(d.pip + col + 4));
+}
+
+// ---------------------------------------------------------------------------
+// linear, general M: chunks of CH macro-steps staged in LDS per workgroup,
+// MT m-tiles of 16 activation rows per pass
 // ---------------------------------------------------------------------------
 constexpr int kPitch = 136;  // staged X'p row: 128 bf16 + 8 pad (272 B, conflict-free 16 B reads)
 
-// Stage X'p[m0 .. m0+mloc)[col_base + 128u + (0..127)] for u < nc into LDS.
 template <int MT, int CH>
 __device__ __forceinline__ void stage_chunk(uint16_t (*xs)[MT * 16][kPitch], const LayerDesc& d, const LinearArgs& a,
                                             int64_t col_base, int nc, int64_t m0, int mloc) {
@@ -313,39 +474,18 @@ __device__ __forceinline__ void stage_chunk(uint16_t (*xs)[MT * 16][kPitch], con
     const int u = e / per_macro;
     const int rem = e - u * per_macro;
     const int m = rem >> 4, c8 = rem & 15;
-    const int64_t col = col_base + 128 * u + 8 * c8;
-    const uint16_t* xrow = X + (m0 + m) * a.ldx;
-    u32x4 val;
-    if (!a.gather) {
-      val = *(const u32x4*)(xrow + col);
-    } else {
-      uint32_t h[8];
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const int32_t src = d.pip[col + t];
-        h[t] = src >= 0 ? (uint32_t)xrow[src] : 0u;
-      }
-      val.x = h[0] | (h[1] << 16);
-      val.y = h[2] | (h[3] << 16);
-      val.z = h[4] | (h[5] << 16);
-      val.w = h[6] | (h[7] << 16);
-    }
-    *(u32x4*)&xs[u][m][8 * c8] = val;
+    *(u32x4*)&xs[u][m][8 * c8] = gather8(a, d, X + (m0 + m) * a.ldx, col_base + 128 * u + 8 * c8);
   }
 }
 
 template <int MT>
-__device__ __forceinline__ void load_b(bf16x16 (&B)[MT], const uint16_t (*xsu)[kPitch], int q, int lane, int mloc) {
-  const int bcol = 64 * q + 16 * (lane >> 4);
+__device__ __forceinline__ void load_bt(bf16x16 (&B)[MT], const uint16_t (*xsu)[kPitch], int col, int lane, int mloc) {
+  const int bcol = col + 16 * (lane >> 4);
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) {
     const int m = 16 * mt + (lane & 15);
-    if (m < mloc) {
-      const uint16_t* p = &xsu[m][bcol];
-      B[mt] = as_bf16x16(*(const u32x4*)p, *(const u32x4*)(p + 8));
-    } else {
-      B[mt] = as_bf16x16(u32x4{0, 0, 0, 0}, u32x4{0, 0, 0, 0});
-    }
+    if (m < mloc) B[mt] = lds_b(&xsu[m][bcol]);
+    else B[mt] = as_bf16x16(u32x4{0, 0, 0, 0}, u32x4{0, 0, 0, 0});
   }
 }
 
@@ -368,11 +508,11 @@ __global__ __launch_bounds__(kWavesPerWG * 64) void linear_kernel(LayerDesc d, L
   const int64_t md0 = d.n_dm * s / S, md1 = d.n_dm * (s + 1) / S;
   const uint8_t* tile = d.wpack + (active ? rt : 0) * d.tile_bytes;
 
-  f32x4 acc[MT];
+  f32x4 acc[MT], acc1[MT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = acc1[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // sparse region: v_smfmac_f32_16x16x64_bf16, two steps per macro-step
+  // sparse region: one unit per macro-step, two SMFMACs (steps q = 0, 1)
   for (int64_t c0 = ms0; c0 < ms1; c0 += CH) {
     const int nc = (int)(ms1 - c0 < CH ? ms1 - c0 : CH);
     __syncthreads();
@@ -382,32 +522,19 @@ __global__ __launch_bounds__(kWavesPerWG * 64) void linear_kernel(LayerDesc d, L
 #pragma unroll
       for (int u = 0; u < CH; ++u) {
         if (u < nc) {
-          const uint8_t* blk = tile + (c0 + u) * kSparseBlock<WT>;
-          bf16x8 A0, A1;
-          if constexpr (sizeof(WT) == 1) {
-            const u32x4 v = *(const u32x4*)(blk + 16 * lane);
-            A0 = fp8x8_to_bf16(v.x, v.y);
-            A1 = fp8x8_to_bf16(v.z, v.w);
-          } else {
-            A0 = as_bf16x8(*(const u32x4*)(blk + 16 * lane));
-            A1 = as_bf16x8(*(const u32x4*)(blk + 1024 + 16 * lane));
-          }
-          const int idx = (int)*(const uint32_t*)(blk + kIdxOffset<WT> + 4 * lane);
-          bf16x16 B[MT];
-          load_b<MT>(B, xs[u], 0, lane, mloc);
+          UnitFrag<WT> f;
+          load_unit<WT>(f, tile + (c0 + u) * kUnit<WT>, tile + d.idx_off + (c0 + u) * 256 + 4 * lane, lane);
+          bf16x16 B0[MT], B1[MT];
+          load_bt<MT>(B0, xs[u], 0, lane, mloc);
+          load_bt<MT>(B1, xs[u], 64, lane, mloc);
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
-            acc[mt] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(A0, B[mt], acc[mt], idx, 0, 0);
-          load_b<MT>(B, xs[u], 1, lane, mloc);
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
-            acc[mt] = __builtin_amdgcn_smfmac_f32_16x16x64_bf16(A1, B[mt], acc[mt], idx, 0, 1);
+          for (int mt = 0; mt < MT; ++mt) mac_unit<WT>(acc[mt], acc1[mt], f, (int)f.idx, B0[mt], B1[mt]);
         }
       }
     }
   }
 
-  // dense region: v_mfma_f32_16x16x32_bf16, four per macro-step
+  // dense region: two units per macro-step, each two SMFMACs on one 64-column step
   for (int64_t c0 = md0; c0 < md1; c0 += CH) {
     const int nc = (int)(md1 - c0 < CH ? md1 - c0 : CH);
     __syncthreads();
@@ -417,89 +544,150 @@ __global__ __launch_bounds__(kWavesPerWG * 64) void linear_kernel(LayerDesc d, L
 #pragma unroll
       for (int u = 0; u < CH; ++u) {
         if (u < nc) {
-          const uint8_t* blk = tile + d.n_sm * kSparseBlock<WT> + (c0 + u) * kDenseBlock<WT>;
 #pragma unroll
-          for (int q = 0; q < 2; ++q) {
-            bf16x8 Alo, Ahi;
-            if constexpr (sizeof(WT) == 1) {
-              const u32x4 v = *(const u32x4*)(blk + q * 1024 + 16 * lane);
-              Alo = fp8x8_to_bf16(v.x, v.y);
-              Ahi = fp8x8_to_bf16(v.z, v.w);
-            } else {
-              Alo = as_bf16x8(*(const u32x4*)(blk + q * 2048 + 16 * lane));
-              Ahi = as_bf16x8(*(const u32x4*)(blk + q * 2048 + 1024 + 16 * lane));
-            }
+          for (int h = 0; h < 2; ++h) {
+            const uint8_t* unit = tile + (d.n_sm + 2 * (c0 + u) + h) * kUnit<WT>;
+            UnitFrag<WT> f;
+            load_unit<WT>(f, unit, unit + 16 * lane, lane);
             bf16x16 B[MT];
-            load_b<MT>(B, xs[u], q, lane, mloc);
+            load_bt<MT>(B, xs[u], 64 * h, lane, mloc);
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-              const bf16x8 blo = __builtin_shufflevector(B[mt], B[mt], 0, 1, 2, 3, 4, 5, 6, 7);
-              const bf16x8 bhi = __builtin_shufflevector(B[mt], B[mt], 8, 9, 10, 11, 12, 13, 14, 15);
-              acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Alo, blo, acc[mt], 0, 0, 0);
-              acc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(Ahi, bhi, acc[mt], 0, 0, 0);
-            }
+            for (int mt = 0; mt < MT; ++mt) mac_unit<WT>(acc[mt], acc1[mt], f, (int)kDenseIdx, B[mt], B[mt]);
           }
         }
       }
     }
   }
+#pragma unroll
+  for (int mt = 0; mt < MT; ++mt) acc[mt] += acc1[mt];
+  finish_tile(d, a, acc, MT, rt, active, m0, s, S, (int64_t)mg * p.rgroups + rg, &last_flag);
+}
 
-  // epilogue: accumulator lane l, register r holds Y^T[n = 16rt + 4(l/16) + r][m = m0 + 16mt + l%16]
-  const int nb = 4 * (lane >> 4);
-  if (S == 1) {
-    if (!active) return;
+// ---------------------------------------------------------------------------
+// linear, decode (M <= 16): each wave streams its row tile's units straight
+// into registers through a ring of P in-flight units; the activations of the
+// workgroup's split are staged (and gathered) into LDS once, so the K loop
+// has no barrier.  Sparse and dense units issue the same loads and the same
+// two SMFMACs (only addresses and the index word differ), so the loop body is
+// straight-line code and the in-order load counter stays P-1 units ahead.
+// ---------------------------------------------------------------------------
+template <typename WT, int NW, int P, bool GATHER>
+__global__ __launch_bounds__(NW * 64) void linear_decode_kernel(LayerDesc d, LinearArgs a, LinearPlan p) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t xs_dyn[];
+  __shared__ int last_flag;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar address math
+  const int rg = blockIdx.x % p.rgroups;
+  const int S = p.splits;
+  const int s = (blockIdx.x / p.rgroups) % S;
+  const int64_t rt = (int64_t)rg * NW + wave;
+  const bool active = rt < d.NT;
+  const int64_t ms0 = d.n_sm * s / S, ms1 = d.n_sm * (s + 1) / S;
+  const int64_t md0 = d.n_dm * s / S, md1 = d.n_dm * (s + 1) / S;
+  const int ns = (int)(ms1 - ms0), nd = (int)(md1 - md0);
+  const int total = ns + 2 * nd;  // units
+  const int M = (int)a.M;
+  const int m = lane & 15, g = lane >> 4;
+  const uint8_t* tile = d.wpack + (active ? rt : 0) * d.tile_bytes;
+  // unit k of this split: sparse units ms0.. then dense units 2*md0..; both
+  // contiguous, so the unit index within the tile is k plus a per-range offset
+  const int64_t sbase = ms0, dbase = d.n_sm + 2 * md0 - ns;
+  const uint8_t* sidx = tile + d.idx_off + ms0 * 256;
+  const int pitch = (ns + nd) * 128 + 8;
+
+  // weights of unit k (lane offset 16 lane) and its index word (lane offset
+  // 4 lane; a dense unit reads a word of itself, replaced at use)
+  auto unit_ptr = [&](int k) { return tile + (k + (k < ns ? sbase : dbase)) * kUnit<WT>; };
+  auto idx_ptr = [&](int k) { return k < ns ? sidx + k * 256 : unit_ptr(k); };
+
+  UnitFrag<WT> wr[P];
+  const bool stream = active && total > 0;
+  if (stream) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int64_t m = m0 + 16 * mt + (lane & 15);
-      if (m >= a.M) continue;
+    for (int i = 0; i < P; ++i) {
+      const int k = i < total ? i : total - 1;
+      load_unit<WT>(wr[i], unit_ptr(k), idx_ptr(k) + 4 * lane, lane);
+    }
+  }
+
+  // stage X'p[0..M)[split columns] once: sparse macro-steps, then dense ones.
+  // Batches of kStageBatch 16-byte pieces per thread: all index loads, then all
+  // activation loads, then the LDS writes, so a batch costs one (contiguous) or
+  // two (gathered) memory round trips instead of one or two per piece.
+  {
+    const uint16_t* X = (const uint16_t*)a.X;
+    const int per_row = (ns + nd) * 16;
+    const int pieces = M * per_row;
+    constexpr int kStageBatch = GATHER ? 2 : 4;
+    for (int e0 = threadIdx.x; e0 < pieces; e0 += kStageBatch * NW * 64) {
+      int64_t col[kStageBatch];
+      int lds_off[kStageBatch], row[kStageBatch];
+      bool ok[kStageBatch];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t n = rt * 16 + nb + r;
-        if (n >= d.N) continue;
-        const float y = acc[mt][r] * (d.scales ? d.scales[n] : 1.0f);
-        if (a.ydtype == DT_F32) ((float*)a.Y)[m * a.ldy + n] = y;
-        else ((uint16_t*)a.Y)[m * a.ldy + n] = (uint16_t)bf16_rne(y);
+      for (int j = 0; j < kStageBatch; ++j) {
+        const int e = e0 + j * NW * 64;
+        ok[j] = e < pieces;
+        const int ee = ok[j] ? e : 0;
+        const int mrow = ee / per_row;
+        const int rem = ee - mrow * per_row;
+        const int u = rem >> 4, c8 = rem & 15;
+        row[j] = mrow;
+        col[j] = (u < ns ? 128 * (ms0 + u) : d.K_sp + 128 * (md0 + u - ns)) + 8 * c8;
+        lds_off[j] = mrow * pitch + 128 * u + 8 * c8;
+      }
+      u32x4 val[kStageBatch];
+      if constexpr (!GATHER) {
+#pragma unroll
+        for (int j = 0; j < kStageBatch; ++j)
+          if (ok[j]) val[j] = *(const u32x4*)(X + (int64_t)row[j] * a.ldx + col[j]);
+      } else {
+        u32x4 i0[kStageBatch], i1[kStageBatch];
+#pragma unroll
+        for (int j = 0; j < kStageBatch; ++j)
+          if (ok[j]) {
+            i0[j] = *(const u32x4*)(d.pip + col[j]);
+            i1[j] = *(const u32x4*)(d.pip + col[j] + 4);
+          }
+#pragma unroll
+        for (int j = 0; j < kStageBatch; ++j)
+          if (ok[j]) val[j] = gather8_from(X + (int64_t)row[j] * a.ldx, i0[j], i1[j]);
+      }
+#pragma unroll
+      for (int j = 0; j < kStageBatch; ++j)
+        if (ok[j]) *(u32x4*)(xs_dyn + lds_off[j]) = val[j];
+    }
+  }
+  __syncthreads();
+
+  f32x4 acc0 = f32x4{0.f, 0.f, 0.f, 0.f}, acc1 = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (stream) {
+    // Lanes of activation rows m >= M read row 0: output column m depends only
+    // on B column m, and columns m >= M are never stored.
+    const uint16_t* xb = xs_dyn + (m < M ? m : 0) * pitch + 16 * g;
+    auto consume = [&](int i, int k) {
+      const bool sp = k < ns;
+      const int col0 = sp ? 128 * k : 128 * ns + 64 * (k - ns);
+      const int col1 = sp ? col0 + 64 : col0;
+      mac_unit<WT>(acc0, acc1, wr[i], sp ? (int)wr[i].idx : (int)kDenseIdx, lds_b(xb + col0), lds_b(xb + col1));
+    };
+    // whole rings: every slot is consumed and refilled unconditionally, so
+    // each slot waits for exactly its own loads
+    int k0 = 0;
+    for (; k0 + P <= total; k0 += P) {
+#pragma unroll
+      for (int i = 0; i < P; ++i) {
+        consume(i, k0 + i);
+        const int kn = k0 + i + P < total ? k0 + i + P : total - 1;
+        load_unit<WT>(wr[i], unit_ptr(kn), idx_ptr(kn) + 4 * lane, lane);
       }
     }
-    return;
-  }
-
-  // split-K: write the partial, the last workgroup of the tile adds all partials in split order
-  const int64_t NP = d.NT * 16;
-  if (active) {
+    // drain: the last total % P units are already in the ring
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const int64_t m = m0 + 16 * mt + (lane & 15);
-      if (m < a.M) *(f32x4*)(a.ws + ((int64_t)s * a.M + m) * NP + rt * 16 + nb) = acc[mt];
-    }
+    for (int i = 0; i < P; ++i)
+      if (k0 + i < total) consume(i, k0 + i);
   }
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    int32_t* cnt = a.counters + (int64_t)mg * p.rgroups + rg;
-    const int old = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    last_flag = (old == S - 1);
-    if (old == S - 1) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  __syncthreads();
-  if (!last_flag) return;
-  __threadfence();
-  if (!active) return;
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int64_t m = m0 + 16 * mt + (lane & 15);
-    if (m >= a.M) continue;
-    f32x4 sum = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int s2 = 0; s2 < S; ++s2) sum += *(const f32x4*)(a.ws + ((int64_t)s2 * a.M + m) * NP + rt * 16 + nb);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t n = rt * 16 + nb + r;
-      if (n >= d.N) continue;
-      const float y = sum[r] * (d.scales ? d.scales[n] : 1.0f);
-      if (a.ydtype == DT_F32) ((float*)a.Y)[m * a.ldy + n] = y;
-      else ((uint16_t*)a.Y)[m * a.ldy + n] = (uint16_t)bf16_rne(y);
-    }
-  }
+  const f32x4 acc = acc0 + acc1;
+  finish_tile(d, a, &acc, 1, rt, active, 0, s, S, rg, &last_flag);
 }
 
 // fp32 weights: VALU, one wave per output row, lanes stride over groups and dense columns.
@@ -538,16 +726,17 @@ __global__ void zero_i32_kernel(int32_t* p, int64_t n) {
 inline unsigned blocks_for(int64_t n, int threads) { return (unsigned)((n + threads - 1) / threads); }
 
 template <typename WT>
-hipError_t launch_pack_frag(const LayerDesc& d, const void* W, int64_t ldw, hipStream_t s) {
+hipError_t launch_pack_units(const LayerDesc& d, const void* W, int64_t ldw, hipStream_t s) {
   if (d.n_sm > 0)
     pack_sparse_kernel<WT><<<blocks_for(d.NT * d.n_sm * 64, 256), 256, 0, s>>>(d, (const WT*)W, ldw);
   if (d.n_dm > 0)
-    pack_dense_kernel<WT><<<blocks_for(d.NT * d.n_dm * 64, 256), 256, 0, s>>>(d, (const WT*)W, ldw);
+    pack_dense_kernel<WT><<<blocks_for(d.NT * 2 * d.n_dm * 64, 256), 256, 0, s>>>(d, (const WT*)W, ldw);
   return hipGetLastError();
 }
 
 template <typename WT>
-hipError_t launch_export_frag(const LayerDesc& d, void* vals, uint32_t* meta, uint8_t* mask, void* dense, hipStream_t s) {
+hipError_t launch_export_units(const LayerDesc& d, void* vals, uint32_t* meta, uint8_t* mask, void* dense,
+                               hipStream_t s) {
   if (d.K_s > 0 && (vals || meta || mask))
     export_sparse_kernel<WT><<<blocks_for(d.N * d.meta_words, 256), 256, 0, s>>>(d, (WT*)vals, meta, mask);
   if (d.K_d > 0 && dense) export_dense_kernel<WT><<<blocks_for(d.N * d.K_d, 256), 256, 0, s>>>(d, (WT*)dense);
@@ -561,8 +750,25 @@ hipError_t launch_linear_t(const LayerDesc& d, const LinearArgs& a, const Linear
   return hipGetLastError();
 }
 
+template <typename WT, int NW, int P>
+hipError_t launch_decode_t(const LayerDesc& d, const LinearArgs& a, const LinearPlan& p, hipStream_t s) {
+  const unsigned grid = (unsigned)((int64_t)p.rgroups * p.splits);
+  if (a.gather) linear_decode_kernel<WT, NW, P, true><<<grid, NW * 64, p.lds_bytes, s>>>(d, a, p);
+  else linear_decode_kernel<WT, NW, P, false><<<grid, NW * 64, p.lds_bytes, s>>>(d, a, p);
+  return hipGetLastError();
+}
+
 template <typename WT>
-hipError_t launch_linear_frag(const LayerDesc& d, const LinearArgs& a, const LinearPlan& p, hipStream_t s) {
+hipError_t launch_linear_units(const LayerDesc& d, const LinearArgs& a, const LinearPlan& p, hipStream_t s) {
+  if (p.decode) {
+    switch (p.waves * 100 + p.depth) {
+      case 404: return launch_decode_t<WT, 4, 4>(d, a, p, s);
+      case 408: return launch_decode_t<WT, 4, 8>(d, a, p, s);
+      case 804: return launch_decode_t<WT, 8, 4>(d, a, p, s);
+      case 808: return launch_decode_t<WT, 8, 8>(d, a, p, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (p.mt) {
     case 1: return launch_linear_t<WT, 1, 4>(d, a, p, s);
     case 2: return launch_linear_t<WT, 2, 4>(d, a, p, s);
@@ -575,8 +781,8 @@ hipError_t launch_linear_frag(const LayerDesc& d, const LinearArgs& a, const Lin
 
 hipError_t launch_pack(const LayerDesc& d, const void* W, int64_t ldw, hipStream_t s) {
   switch (d.wdtype) {
-    case DT_FP8: return launch_pack_frag<uint8_t>(d, W, ldw, s);
-    case DT_BF16: return launch_pack_frag<uint16_t>(d, W, ldw, s);
+    case DT_FP8: return launch_pack_units<uint8_t>(d, W, ldw, s);
+    case DT_BF16: return launch_pack_units<uint16_t>(d, W, ldw, s);
     case DT_F32:
       if (d.K_s > 0)
         pack_f32_sparse_kernel<<<blocks_for(d.N * d.meta_words, 256), 256, 0, s>>>(d, (const uint32_t*)W, ldw);
@@ -589,11 +795,12 @@ hipError_t launch_pack(const LayerDesc& d, const void* W, int64_t ldw, hipStream
 
 hipError_t launch_export(const LayerDesc& d, void* vals, uint32_t* meta, uint8_t* mask, void* dense, hipStream_t s) {
   switch (d.wdtype) {
-    case DT_FP8: return launch_export_frag<uint8_t>(d, vals, meta, mask, dense, s);
-    case DT_BF16: return launch_export_frag<uint16_t>(d, vals, meta, mask, dense, s);
+    case DT_FP8: return launch_export_units<uint8_t>(d, vals, meta, mask, dense, s);
+    case DT_BF16: return launch_export_units<uint16_t>(d, vals, meta, mask, dense, s);
     case DT_F32: {
       hipError_t e = hipSuccess;
-      if (vals && d.K_s > 0) e = hipMemcpyAsync(vals, d.vals32, (size_t)(d.N * (d.K_s / 2)) * 4, hipMemcpyDeviceToDevice, s);
+      if (vals && d.K_s > 0)
+        e = hipMemcpyAsync(vals, d.vals32, (size_t)(d.N * (d.K_s / 2)) * 4, hipMemcpyDeviceToDevice, s);
       if (e == hipSuccess && meta && d.K_s > 0)
         e = hipMemcpyAsync(meta, d.meta32, (size_t)(d.N * d.meta_words) * 4, hipMemcpyDeviceToDevice, s);
       if (e == hipSuccess && dense && d.K_d > 0)
@@ -608,8 +815,8 @@ hipError_t launch_export(const LayerDesc& d, void* vals, uint32_t* meta, uint8_t
 
 hipError_t launch_linear(const LayerDesc& d, const LinearArgs& a, const LinearPlan& p, hipStream_t s) {
   switch (d.wdtype) {
-    case DT_FP8: return launch_linear_frag<uint8_t>(d, a, p, s);
-    case DT_BF16: return launch_linear_frag<uint16_t>(d, a, p, s);
+    case DT_FP8: return launch_linear_units<uint8_t>(d, a, p, s);
+    case DT_BF16: return launch_linear_units<uint16_t>(d, a, p, s);
     case DT_F32:
       linear_f32_kernel<<<blocks_for(d.N, 4), 256, 0, s>>>(d, a);
       return hipGetLastError();

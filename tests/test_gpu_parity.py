@@ -238,3 +238,38 @@ def test_non_default_stream_and_strided_operands():
         assert np.all(Yb[:, N:] == -7.0)  # padding columns untouched
     finally:
         sdg.spense_free(h)
+
+
+DECODE_VARIANTS = ["4,4", "4,8", "8,4", "8,8"]
+
+
+@pytest.mark.parametrize("wdtype", [DT_FP8, DT_BF16])
+@pytest.mark.parametrize("dense", [("frac", 0.25), ("rand", 192)])
+def test_decode_variants(wdtype, dense, monkeypatch):
+    """Every decode-kernel variant (waves per workgroup, ring depth) and several
+    split counts agree with the oracle."""
+    N, K = 200, 1536
+    W, s = _small(N, K, wdtype, 21)
+    X = synth.make_x(16, K, DT_BF16, np.random.default_rng(22))
+    sd = to_dev(s, DT_F32) if s is not None else None
+    if dense[0] == "frac":
+        h = pack_dev(to_dev(W, wdtype), wdtype, sd, dense_fraction=dense[1])
+        pi, K_s, _ = oracle.resolve_dense_set(K, dense_fraction=dense[1])
+        D = np.sort(pi[K_s:])
+    else:
+        D = synth.random_dense_set(K, dense[1], 23)
+        h = pack_dev(to_dev(W, wdtype), wdtype, sd, dense_cols=D)
+    try:
+        ref = oracle_pack_rows(W, wdtype, D)
+        Xd = to_dev(X, DT_BF16)
+        for v in DECODE_VARIANTS:
+            monkeypatch.setenv("SPENSE_DECODE", v)
+            for M in (1, 5, 16):
+                Yref, B = oracle.linear_ref(X[:M], DT_BF16, ref, s)
+                for sp in (0, 1, 3, 9):
+                    Y = linear_dev(h, Xd[:M], N, splits=sp).cpu().numpy()
+                    r = tol_ratio(Y, Yref, B)
+                    assert r <= 1.0, (v, M, sp, r)
+        log(f"[decode variants] wdtype={wdtype} dense={dense}: all variants within tolerance")
+    finally:
+        sdg.spense_free(h)

@@ -1,0 +1,66 @@
+"""Checks on the gfx950 code the compiler emits for the HIP kernels (host-only).
+
+A matrix instruction whose destination registers overlap its A or B source
+registers gave wrong results on MI355X (seen with v_mfma_f32_16x16x32_bf16 and
+VGPR accumulators, where the destination is a separate operand).  The kernels
+now use only v_smfmac_f32_16x16x64_bf16, whose destination is tied to the
+accumulator; this test scans the emitted code for any overlap.
+"""
+
+import os
+import re
+import subprocess
+import tempfile
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "sparse_dense_gemm_amd", "csrc", "spense_kernels.hip")
+HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
+
+
+def _regs(tok):
+    m = re.match(r"([va])\[(\d+):(\d+)\]", tok)
+    if m:
+        return {(m.group(1), i) for i in range(int(m.group(2)), int(m.group(3)) + 1)}
+    m = re.match(r"([va])(\d+)$", tok)
+    return {(m.group(1), int(m.group(2)))} if m else set()
+
+
+@pytest.fixture(scope="module")
+def gfx950_asm():
+    if not os.path.exists(HIPCC):
+        pytest.skip("hipcc not available")
+    with tempfile.TemporaryDirectory() as d:
+        cmd = [HIPCC, "-O3", "-std=c++17", "--offload-arch=gfx950", "--cuda-device-only", "-S",
+               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+               "-I", os.path.join(ROOT, "include"), SRC, "-o", os.path.join(d, "k.s")]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr[-2000:]
+        with open(os.path.join(d, "k.s")) as f:
+            return f.read()
+
+
+def test_matrix_instructions_do_not_overwrite_their_sources(gfx950_asm):
+    total, bad = 0, []
+    for line in gfx950_asm.splitlines():
+        m = re.match(r"\s+(v_s?mfmac?_\S+)\s+(.*)", line)
+        if not m:
+            continue
+        ops = [o.strip() for o in m.group(2).split(";")[0].split(",")]
+        total += 1
+        if _regs(ops[0]) & (_regs(ops[1]) | _regs(ops[2])):
+            bad.append(line.strip())
+    assert total > 100
+    assert not bad, bad[:5]
+
+
+def test_no_packed_fp32_arithmetic(gfx950_asm):
+    assert not re.search(r"\bv_pk_(add|mul|fma)_f32\b", gfx950_asm)
+
+
+def test_both_regions_run_on_structured_sparse_instructions(gfx950_asm):
+    # the 2:4 region and the dense region (as pairs of fixed-index products,
+    # index word 0xEEEE4444) both use v_smfmac_f32_16x16x64_bf16
+    assert "v_smfmac_f32_16x16x64_bf16" in gfx950_asm
+    assert re.search(r"0xeeee4444", gfx950_asm, re.I)
