@@ -206,57 +206,82 @@ int spense_pack(const void* W, int32_t wdtype, int64_t N, int64_t K, int64_t ldw
   return SPENSE_OK;
 }
 
-// Optional tuning override "waves,depth" (e.g. "8,8") for the decode kernel.
-static bool decode_override(int& waves, int& depth) {
+// Optional tuning override "waves,depth[,chunked]" (e.g. "8,4,1") for the decode kernels.
+static bool decode_override(int& waves, int& depth, int& chunked) {
   const char* e = std::getenv("SPENSE_DECODE");
   if (!e || !*e) return false;
-  int w = 0, dp = 0;
-  if (std::sscanf(e, "%d,%d", &w, &dp) != 2) return false;
+  int w = 0, dp = 0, ch = -1;
+  const int n = std::sscanf(e, "%d,%d,%d", &w, &dp, &ch);
+  if (n < 2) return false;
   if ((w != 4 && w != 8) || (dp != 4 && dp != 8)) return false;
   waves = w;
   depth = dp;
+  if (n == 3 && (ch == 0 || ch == 1)) chunked = ch;
   return true;
 }
 
+// dynamic LDS of the single-shot decode kernel: the whole split's activations
 static int64_t decode_lds_bytes(const LayerDesc& d, int64_t M, int64_t S) {
   const int64_t steps = (d.n_sm + S - 1) / S + (d.n_dm + S - 1) / S;
   return M * (steps * kMacro + 8) * 2;
 }
 
-static int plan_linear(const spense_layer* h, int64_t M, int32_t splits, LinearPlan& p) {
+// dynamic LDS of the chunked decode kernel: two chunk buffers (+ the split's
+// column map when activations are gathered)
+static int64_t stream_lds_bytes(const LayerDesc& d, int64_t M, int64_t S, bool gather) {
+  const int64_t steps = (d.n_sm + S - 1) / S + (d.n_dm + S - 1) / S;
+  return 2 * M * (kStreamChunk * kMacro + 8) * 2 + (gather ? steps * kMacro * 4 : 0);
+}
+
+static int plan_linear(const spense_layer* h, int64_t M, int32_t splits, bool gather, LinearPlan& p) {
   const LayerDesc& d = h->d;
   const int64_t steps = std::max<int64_t>(d.n_sm, d.n_dm);
   const int64_t max_splits = std::max<int64_t>(1, std::min<int64_t>(steps, 64));
   if (splits < 0 || splits > max_splits) return SPENSE_EINVAL;
   p = LinearPlan{};
   if (M <= 16) {
-    // decode: one 16-row m-tile, weights streamed through a register ring
+    // decode: one 16-row m-tile, weights streamed through a register ring,
+    // 8 waves per workgroup, 4 units in flight per wave.  One split when the
+    // row tiles alone give enough waves (each split adds a partial-sum
+    // handshake at the end of the kernel), else about 1280 waves.  The split's
+    // activations are staged in LDS at once when they fit in 64 KB, else in
+    // double-buffered chunks.
     p.decode = 1;
+    p.chunked = 1;
     p.mt = 1;
     p.mgroups = 1;
-    // 8 waves per workgroup, 4 units in flight per wave; one split when the
-    // row tiles alone give enough waves (each split adds a partial-sum
-    // handshake at the end of the kernel), else about 1280 waves
     p.waves = 8;
     p.depth = 4;
-    int w, dp;
-    if (decode_override(w, dp)) {
+    int w, dp, ch = -1;
+    const bool overridden = decode_override(w, dp, ch);
+    if (overridden) {
       p.waves = w;
       p.depth = dp;
     }
-    p.rgroups = (int)((d.NT + p.waves - 1) / p.waves);
+    const bool forced_chunking = ch == 1;
+    if (ch == 0) p.chunked = 0;
     int64_t S = splits;
     if (S == 0) {
       S = d.NT >= 1024 ? 1 : std::max<int64_t>(1, (1280 + d.NT - 1) / d.NT);
       S = std::min<int64_t>(S, max_splits);
-      while (S < max_splits && decode_lds_bytes(d, M, S) > 64 * 1024) ++S;
+      if (ch == 0)  // single-shot staging requested: split until it fits
+        while (S < max_splits && decode_lds_bytes(d, M, S) > 64 * 1024) ++S;
     }
+    // stage the whole split at once when it fits (no per-chunk barriers)
+    if (!forced_chunking && decode_lds_bytes(d, M, S) <= 64 * 1024) p.chunked = 0;
+    // chunked staging of contiguous activations: two chunk buffers per
+    // workgroup bound the residency, so smaller workgroups keep more waves
+    // per CU streaming
+    if (p.chunked && !gather && !overridden) p.waves = 4;
+    p.rgroups = (int)((d.NT + p.waves - 1) / p.waves);
     p.splits = (int)S;
-    p.lds_bytes = (int)decode_lds_bytes(d, M, S);
-    if (p.lds_bytes <= 64 * 1024) return SPENSE_OK;
-    // the forced split leaves too much to stage: use the chunked kernel
+    const int64_t lds = p.chunked ? stream_lds_bytes(d, M, S, gather) : decode_lds_bytes(d, M, S);
+    p.lds_bytes = (int)lds;
+    if (lds <= (p.chunked ? 96 * 1024 : 64 * 1024)) return SPENSE_OK;
+    // too much to stage for this split count: use the general kernel
   }
   p.decode = 0;
+  p.chunked = 0;
   p.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
   p.mgroups = (int)((M + 16 * p.mt - 1) / (16 * p.mt));
   p.rgroups = (int)((d.NT + kWavesPerWG - 1) / kWavesPerWG);
@@ -298,10 +323,10 @@ int spense_linear_splits(spense_handle h, const void* X, int32_t xdtype, int64_t
   }
   LinearPlan p{};
   const bool x_aligned = aligned16(X) && (ldx % 8) == 0;
-  int rc = plan_linear(h, M, splits, p);
+  a.gather = d.gather || !x_aligned;
+  int rc = plan_linear(h, M, splits, a.gather != 0, p);
   if (rc != SPENSE_OK) return rc;
   a.splits = p.splits;
-  a.gather = d.gather || !x_aligned;
   if (p.splits > 1) {
     const size_t need = (size_t)p.splits * (size_t)M * (size_t)(d.NT * kRowTile) * 4;
     const size_t need_cnt = (size_t)p.rgroups * (size_t)p.mgroups;

@@ -90,9 +90,11 @@ struct LinearPlan {
   int waves;     // waves per workgroup: 4 or 8
   int depth;     // macro-steps in flight per wave: 4 or 8
   int lds_bytes; // dynamic LDS of the decode kernel
+  int chunked;   // 1: activations staged in double-buffered chunks (linear_stream_kernel)
 };
 
 constexpr int kWavesPerWG = 4;
+constexpr int kStreamChunk = 8;  // units per activation chunk of linear_stream_kernel
 
 hipError_t launch_pack(const LayerDesc& d, const void* W, int64_t ldw, hipStream_t s);
 hipError_t launch_export(const LayerDesc& d, void* vals, uint32_t* meta, uint8_t* mask, void* dense, hipStream_t s);

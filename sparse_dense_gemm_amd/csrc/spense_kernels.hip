@@ -690,6 +690,166 @@ __global__ __launch_bounds__(NW * 64) void linear_decode_kernel(LayerDesc d, Lin
   finish_tile(d, a, &acc, 1, rt, active, 0, s, S, rg, &last_flag);
 }
 
+// ---------------------------------------------------------------------------
+// linear, decode (M <= 16) with chunked activation staging: the split's
+// activations pass through a double-buffered LDS ring of CH-unit chunks, so
+// the LDS footprint does not grow with the split width and one split covers
+// the whole K range at any M <= 16.  One barrier per chunk; it waits on LDS
+// only, so the weight ring stays in flight across it.  For a chosen dense set
+// the split's column map is staged in LDS once, so the per-chunk gathers
+// depend on LDS reads only.
+// ---------------------------------------------------------------------------
+template <typename WT, int NW, int P, int CH, bool GATHER>
+__global__ __launch_bounds__(NW * 64) void linear_stream_kernel(LayerDesc d, LinearArgs a, LinearPlan p) {
+  static_assert(CH % P == 0, "a chunk must hold whole rings");
+  extern __shared__ __attribute__((aligned(16))) uint16_t xs_dyn[];
+  __shared__ int last_flag;
+  constexpr int kPitch2 = CH * 128 + 8;                 // staged row: CH unit slots of 128 columns + pad
+  constexpr int kPieces = (16 * CH * 16) / (NW * 64);  // 16-byte pieces per thread per chunk at M = 16
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rg = blockIdx.x % p.rgroups;
+  const int S = p.splits;
+  const int s = (blockIdx.x / p.rgroups) % S;
+  const int64_t rt = (int64_t)rg * NW + wave;
+  const bool active = rt < d.NT;
+  const int64_t ms0 = d.n_sm * s / S, ms1 = d.n_sm * (s + 1) / S;
+  const int64_t md0 = d.n_dm * s / S, md1 = d.n_dm * (s + 1) / S;
+  const int ns = (int)(ms1 - ms0), nd = (int)(md1 - md0);
+  const int total = ns + 2 * nd;  // units
+  const int nchunks = (total + CH - 1) / CH;
+  const int M = (int)a.M;
+  const int m = lane & 15, g = lane >> 4;
+  const uint8_t* tile = d.wpack + (active ? rt : 0) * d.tile_bytes;
+  const int64_t sbase = ms0, dbase = d.n_sm + 2 * md0 - ns;
+  const uint8_t* sidx = tile + d.idx_off + ms0 * 256;
+  uint16_t* xbuf0 = xs_dyn;
+  uint16_t* xbuf1 = xs_dyn + M * kPitch2;
+  int32_t* pip_l = (int32_t*)(xs_dyn + 2 * M * kPitch2);  // split column map (GATHER)
+  const uint16_t* X = (const uint16_t*)a.X;
+
+  auto unit_ptr = [&](int k) { return tile + (k + (k < ns ? sbase : dbase)) * kUnit<WT>; };
+  auto idx_ptr = [&](int k) { return k < ns ? sidx + k * 256 : unit_ptr(k); };
+  // first column of unit k in the split's column list: sparse units 128 wide, dense units 64
+  auto unit_lcol = [&](int k) { return k < ns ? 128 * k : 128 * ns + 64 * (k - ns); };
+
+  UnitFrag<WT> wr[P];
+  const bool stream = active && total > 0;
+  if (stream) {
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      const int k = i < total ? i : total - 1;
+      load_unit<WT>(wr[i], unit_ptr(k), idx_ptr(k) + 4 * lane, lane);
+    }
+  }
+
+  if constexpr (GATHER) {
+    // the split's column map: sparse columns of X'p, then dense ones
+    const int ncols = 128 * (ns + nd);
+    for (int e = threadIdx.x; 4 * e < ncols; e += NW * 64) {
+      const int c = 4 * e;
+      const int64_t col = c < 128 * ns ? 128 * ms0 + c : d.K_sp + 128 * md0 + (c - 128 * ns);
+      *(u32x4*)(pip_l + c) = *(const u32x4*)(d.pip + col);
+    }
+    __syncthreads();
+  }
+
+  // piece e of a chunk: row = e / (16 CH), unit slot j = (e / 16) % CH, 8-column group c8 = e % 16.
+  // Loads are issued here and only consumed by write_chunk (after the chunk's
+  // compute), so waiting for them never stalls the weight ring.
+  u32x4 xv[GATHER ? 1 : kPieces];
+  uint32_t xh[GATHER ? kPieces : 1][8];
+  auto issue_chunk = [&](int c) {
+#pragma unroll
+    for (int i = 0; i < kPieces; ++i) {
+      const int e = threadIdx.x + i * NW * 64;
+      const int row = e / (16 * CH);
+      const int j = (e / 16) % CH, c8 = e % 16;
+      const int k = c * CH + j;
+      const bool ok = row < M && k < total && (k < ns || c8 < 8);
+      if (ok) {
+        const int lc = unit_lcol(k) + 8 * c8;
+        const uint32_t rowoff = (uint32_t)(row * a.ldx);
+        if constexpr (!GATHER) {
+          const int64_t col = k < ns ? 128 * ms0 + lc : d.K_s + 128 * md0 + (lc - 128 * ns);
+          xv[i] = *(const u32x4*)(X + rowoff + (uint32_t)col);
+        } else {
+          const u32x4 i0 = *(const u32x4*)(pip_l + lc), i1 = *(const u32x4*)(pip_l + lc + 4);
+          const int src[8] = {(int)i0.x, (int)i0.y, (int)i0.z, (int)i0.w, (int)i1.x, (int)i1.y, (int)i1.z, (int)i1.w};
+#pragma unroll
+          for (int t = 0; t < 8; ++t) xh[i][t] = src[t] >= 0 ? (uint32_t)X[rowoff + (uint32_t)src[t]] : 0u;
+        }
+      }
+    }
+  };
+  auto write_chunk = [&](uint16_t* buf) {
+#pragma unroll
+    for (int i = 0; i < kPieces; ++i) {
+      const int e = threadIdx.x + i * NW * 64;
+      const int row = e / (16 * CH);
+      if (row < M) {
+        u32x4 v;
+        if constexpr (!GATHER) {
+          v = xv[i];
+        } else {
+          v.x = xh[i][0] | (xh[i][1] << 16);
+          v.y = xh[i][2] | (xh[i][3] << 16);
+          v.z = xh[i][4] | (xh[i][5] << 16);
+          v.w = xh[i][6] | (xh[i][7] << 16);
+        }
+        *(u32x4*)(buf + row * kPitch2 + 128 * ((e / 16) % CH) + 8 * (e % 16)) = v;
+      }
+    }
+  };
+
+  issue_chunk(0);
+  write_chunk(xbuf0);
+  __syncthreads();
+
+  f32x4 acc0 = f32x4{0.f, 0.f, 0.f, 0.f}, acc1 = f32x4{0.f, 0.f, 0.f, 0.f};
+  // Lanes of activation rows m >= M read row 0: output column m depends only
+  // on B column m, and columns m >= M are never stored.
+  const int xoff = (m < M ? m : 0) * kPitch2 + 16 * g;
+  for (int c = 0; c < nchunks; ++c) {
+    const bool more = c + 1 < nchunks;
+    if (more) issue_chunk(c + 1);
+    const uint16_t* xb = ((c & 1) ? xbuf1 : xbuf0) + xoff;
+    if (stream) {
+      if ((c + 1) * CH <= total) {
+        // whole chunk: every ring slot consumed and refilled unconditionally
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+          const int k = c * CH + j;
+          const bool sp = k < ns;
+          const int col1 = sp ? 128 * j + 64 : 128 * j;
+          UnitFrag<WT>& f = wr[j % P];
+          mac_unit<WT>(acc0, acc1, f, sp ? (int)f.idx : (int)kDenseIdx, lds_b(xb + 128 * j), lds_b(xb + col1));
+          const int kn = k + P < total ? k + P : total - 1;
+          load_unit<WT>(f, unit_ptr(kn), idx_ptr(kn) + 4 * lane, lane);
+        }
+      } else {
+        // last, partial chunk: the remaining units are already in the ring
+#pragma unroll
+        for (int j = 0; j < CH; ++j) {
+          const int k = c * CH + j;
+          if (k < total) {
+            const bool sp = k < ns;
+            const int col1 = sp ? 128 * j + 64 : 128 * j;
+            UnitFrag<WT>& f = wr[j % P];
+            mac_unit<WT>(acc0, acc1, f, sp ? (int)f.idx : (int)kDenseIdx, lds_b(xb + 128 * j), lds_b(xb + col1));
+            const int kn = k + P < total ? k + P : total - 1;
+            if (k + P < total) load_unit<WT>(f, unit_ptr(kn), idx_ptr(kn) + 4 * lane, lane);
+          }
+        }
+      }
+    }
+    if (more) write_chunk((c & 1) ? xbuf0 : xbuf1);
+    __syncthreads();
+  }
+  const f32x4 acc = acc0 + acc1;
+  finish_tile(d, a, &acc, 1, rt, active, 0, s, S, rg, &last_flag);
+}
+
 // fp32 weights: VALU, one wave per output row, lanes stride over groups and dense columns.
 __global__ __launch_bounds__(256) void linear_f32_kernel(LayerDesc d, LinearArgs a) {
   const int lane = threadIdx.x & 63;
@@ -758,8 +918,40 @@ hipError_t launch_decode_t(const LayerDesc& d, const LinearArgs& a, const Linear
   return hipGetLastError();
 }
 
+// Kernels that may need more than the default 64 KB of dynamic LDS opt in once.
+template <typename K>
+hipError_t allow_lds(K kernel, int bytes) {
+  if (bytes <= 64 * 1024) return hipSuccess;
+  return hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+}
+
+template <typename WT, int NW, int P>
+hipError_t launch_stream_t(const LayerDesc& d, const LinearArgs& a, const LinearPlan& p, hipStream_t s) {
+  const unsigned grid = (unsigned)((int64_t)p.rgroups * p.splits);
+  hipError_t e;
+  if (a.gather) {
+    auto k = linear_stream_kernel<WT, NW, P, kStreamChunk, true>;
+    if ((e = allow_lds(k, p.lds_bytes)) != hipSuccess) return e;
+    k<<<grid, NW * 64, p.lds_bytes, s>>>(d, a, p);
+  } else {
+    auto k = linear_stream_kernel<WT, NW, P, kStreamChunk, false>;
+    if ((e = allow_lds(k, p.lds_bytes)) != hipSuccess) return e;
+    k<<<grid, NW * 64, p.lds_bytes, s>>>(d, a, p);
+  }
+  return hipGetLastError();
+}
+
 template <typename WT>
 hipError_t launch_linear_units(const LayerDesc& d, const LinearArgs& a, const LinearPlan& p, hipStream_t s) {
+  if (p.decode && p.chunked) {
+    switch (p.waves * 100 + p.depth) {
+      case 404: return launch_stream_t<WT, 4, 4>(d, a, p, s);
+      case 408: return launch_stream_t<WT, 4, 8>(d, a, p, s);
+      case 804: return launch_stream_t<WT, 8, 4>(d, a, p, s);
+      case 808: return launch_stream_t<WT, 8, 8>(d, a, p, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
   if (p.decode) {
     switch (p.waves * 100 + p.depth) {
       case 404: return launch_decode_t<WT, 4, 4>(d, a, p, s);

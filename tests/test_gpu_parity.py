@@ -240,14 +240,15 @@ def test_non_default_stream_and_strided_operands():
         sdg.spense_free(h)
 
 
-DECODE_VARIANTS = ["4,4", "4,8", "8,4", "8,8"]
+DECODE_VARIANTS = ["4,4,0", "4,8,0", "8,4,0", "8,8,0", "4,4,1", "4,8,1", "8,4,1", "8,8,1"]
 
 
 @pytest.mark.parametrize("wdtype", [DT_FP8, DT_BF16])
 @pytest.mark.parametrize("dense", [("frac", 0.25), ("rand", 192)])
 def test_decode_variants(wdtype, dense, monkeypatch):
-    """Every decode-kernel variant (waves per workgroup, ring depth) and several
-    split counts agree with the oracle."""
+    """Every decode-kernel variant (waves per workgroup, ring depth, single-shot
+    or chunked activation staging) and several split counts agree with the
+    oracle."""
     N, K = 200, 1536
     W, s = _small(N, K, wdtype, 21)
     X = synth.make_x(16, K, DT_BF16, np.random.default_rng(22))
