@@ -30,7 +30,8 @@
  *     then returns the hipError_t value.  Faults inside a kernel surface at the
  *     caller's next synchronisation, as for any HIP launch.
  *   - The library is not thread-safe per handle: at most one spense_linear may
- *     be in flight on a handle at a time (its split-K workspace is shared).
+ *     be in flight on a handle at a time (its split-K and gather workspaces
+ *     are shared).
  */
 #ifndef SPENSE_H
 #define SPENSE_H
@@ -107,11 +108,14 @@ int spense_pack(const void* W, int32_t wdtype, int64_t N, int64_t K, int64_t ldw
  * spense_linear - Y = X . W_pruned^T (times the per-channel scales), the layer forward.
  *
  * Input-split execution (Technical Summary 2.A): the sparse region runs on the
- * structured-sparse SMFMAC matrix instructions, the dense region on dense MFMA,
- * both accumulating into the same fp32 accumulators; when the dense set is not
- * a 128-aligned tail the activation columns are gathered through pi in the
- * same kernel.  Accumulation is fp32; products of bf16 activations with bf16
- * or e4m3 weights are exact.
+ * structured-sparse SMFMAC matrix instructions, the dense region on the same
+ * instruction with index words that select every position (a dense 16x64
+ * block is two such products), both accumulating into the same fp32
+ * accumulators; when the dense set is not a 128-aligned tail the activation
+ * columns are gathered through pi, inside the layer kernel for small batches
+ * or into a handle-owned workspace by a preceding kernel on the same stream.
+ * Accumulation is fp32; products of bf16 activations with bf16 or e4m3
+ * weights are exact.
  *
  *   h          handle from spense_pack.
  *   X          device pointer, [M, ldx] elements of `xdtype`, ldx >= K.
@@ -122,7 +126,8 @@ int spense_pack(const void* W, int32_t wdtype, int64_t N, int64_t K, int64_t ldw
  *
  * Asynchronous on `stream`.  Deterministic: repeated calls give bitwise equal
  * Y (split-K partial sums are added in a fixed order).  The first call at a
- * larger M than before may allocate a larger split-K workspace (hipMalloc).
+ * larger M than before may synchronise `stream` and allocate a larger split-K
+ * or gather workspace (hipMalloc); SPENSE_ENOMEM if that fails.
  */
 int spense_linear(spense_handle h, const void* X, int32_t xdtype, int64_t M, int64_t ldx, void* Y, int32_t ydtype,
                   int64_t ldy, void* stream);

@@ -32,6 +32,8 @@ struct spense_layer {
   float* dense32 = nullptr;
   float* ws = nullptr;
   size_t ws_bytes = 0;
+  void* xws = nullptr;  // gathered activations [M][K_p] bf16 (chunked staging of a chosen dense set)
+  size_t xws_bytes = 0;
   int32_t* counters = nullptr;
   size_t n_counters = 0;
   int64_t weight_bytes = 0;
@@ -53,7 +55,7 @@ int64_t elem_bytes(int32_t t) { return t == SPENSE_F32 ? 4 : t == SPENSE_BF16 ? 
 
 void release(spense_layer* h) {
   if (!h) return;
-  void* ptrs[] = {h->wpack, h->scales, h->pi, h->pip, h->vals32, h->meta32, h->dense32, h->ws, h->counters};
+  void* ptrs[] = {h->wpack, h->scales, h->pi, h->pip, h->vals32, h->meta32, h->dense32, h->ws, h->counters, h->xws};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
   delete h;
@@ -177,12 +179,19 @@ int spense_pack(const void* W, int32_t wdtype, int64_t N, int64_t K, int64_t ldw
       e = hipMemcpyAsync(h->pip, pip.data(), (size_t)d.K_p * 4, hipMemcpyHostToDevice, s);
     d.wpack = h->wpack;
     d.pip = h->pip;
+    // per-row output scales, padded to whole row tiles; 1.0 for bf16 weights,
+    // so the kernels load and apply them unconditionally
+    const size_t sbytes = (size_t)(d.NT * kRowTile) * 4;
+    if (e == hipSuccess) e = dev_alloc(&h->scales, sbytes);
     if (wdtype == SPENSE_FP8_E4M3) {
-      if (e == hipSuccess) e = dev_alloc(&h->scales, (size_t)(d.NT * kRowTile) * 4);
-      if (e == hipSuccess) e = hipMemsetAsync(h->scales, 0, (size_t)(d.NT * kRowTile) * 4, s);
+      if (e == hipSuccess) e = hipMemsetAsync(h->scales, 0, sbytes, s);
       if (e == hipSuccess) e = hipMemcpyAsync(h->scales, scales, (size_t)N * 4, hipMemcpyDeviceToDevice, s);
-      d.scales = h->scales;
+    } else {
+      const std::vector<float> ones((size_t)(d.NT * kRowTile), 1.0f);
+      if (e == hipSuccess) e = hipMemcpyAsync(h->scales, ones.data(), sbytes, hipMemcpyHostToDevice, s);
+      if (e == hipSuccess) e = hipStreamSynchronize(s);  // the host buffer is released on return
     }
+    d.scales = h->scales;
   } else {
     d.gather = 1;
     const size_t vbytes = (size_t)(N * (K_s / 2)) * 4, mbytes = (size_t)(N * d.meta_words) * 4,
@@ -226,40 +235,38 @@ static int64_t decode_lds_bytes(const LayerDesc& d, int64_t M, int64_t S) {
   return M * (steps * kMacro + 8) * 2;
 }
 
-// dynamic LDS of the chunked decode kernel: two chunk buffers (+ the split's
-// column map when activations are gathered)
-static int64_t stream_lds_bytes(const LayerDesc& d, int64_t M, int64_t S, bool gather) {
-  const int64_t steps = (d.n_sm + S - 1) / S + (d.n_dm + S - 1) / S;
-  return 2 * M * (kStreamChunk * kMacro + 8) * 2 + (gather ? steps * kMacro * 4 : 0);
-}
+// dynamic LDS of the chunked decode kernel: two chunk buffers
+static int64_t stream_lds_bytes(int64_t M) { return 2 * M * (kStreamChunk * kMacro + 8) * 2; }
 
-static int plan_linear(const spense_layer* h, int64_t M, int32_t splits, bool gather, LinearPlan& p) {
+constexpr int64_t kCUs = 256;             // compute units of the target GPU
+constexpr int64_t kLdsPerCU = 160 * 1024;  // LDS bytes per CU
+
+static int plan_linear(const spense_layer* h, int64_t M, int32_t splits, LinearPlan& p) {
   const LayerDesc& d = h->d;
   const int64_t steps = std::max<int64_t>(d.n_sm, d.n_dm);
   const int64_t max_splits = std::max<int64_t>(1, std::min<int64_t>(steps, 64));
   if (splits < 0 || splits > max_splits) return SPENSE_EINVAL;
   p = LinearPlan{};
+  p.preset = -1;
+  p.nr = 1;
+  p.mt = 1;
+  p.mgroups = 1;
   if (M <= 16) {
     // decode: one 16-row m-tile, weights streamed through a register ring,
     // 8 waves per workgroup, 4 units in flight per wave.  One split when the
     // row tiles alone give enough waves (each split adds a partial-sum
     // handshake at the end of the kernel), else about 1280 waves.  The split's
-    // activations are staged in LDS at once when they fit in 64 KB, else in
-    // double-buffered chunks.
-    p.decode = 1;
-    p.chunked = 1;
-    p.mt = 1;
-    p.mgroups = 1;
+    // activations are staged in LDS at once when they fit in 64 KB (no
+    // barrier in the K loop), else in double-buffered chunks.
     p.waves = 8;
     p.depth = 4;
+    p.chunk = kStreamChunk;
     int w, dp, ch = -1;
     const bool overridden = decode_override(w, dp, ch);
     if (overridden) {
       p.waves = w;
       p.depth = dp;
     }
-    const bool forced_chunking = ch == 1;
-    if (ch == 0) p.chunked = 0;
     int64_t S = splits;
     if (S == 0) {
       S = d.NT >= 1024 ? 1 : std::max<int64_t>(1, (1280 + d.NT - 1) / d.NT);
@@ -267,31 +274,58 @@ static int plan_linear(const spense_layer* h, int64_t M, int32_t splits, bool ga
       if (ch == 0)  // single-shot staging requested: split until it fits
         while (S < max_splits && decode_lds_bytes(d, M, S) > 64 * 1024) ++S;
     }
-    // stage the whole split at once when it fits (no per-chunk barriers)
-    if (!forced_chunking && decode_lds_bytes(d, M, S) <= 64 * 1024) p.chunked = 0;
-    // chunked staging of contiguous activations: two chunk buffers per
-    // workgroup bound the residency, so smaller workgroups keep more waves
-    // per CU streaming
-    if (p.chunked && !gather && !overridden) p.waves = 4;
+    p.chunked = (ch == 1 || decode_lds_bytes(d, M, S) > 64 * 1024) ? 1 : 0;
+    // chunked staging: two chunk buffers per workgroup bound the residency,
+    // so smaller workgroups keep more waves per CU streaming
+    if (p.chunked && !overridden) p.waves = 4;
     p.rgroups = (int)((d.NT + p.waves - 1) / p.waves);
     p.splits = (int)S;
-    const int64_t lds = p.chunked ? stream_lds_bytes(d, M, S, gather) : decode_lds_bytes(d, M, S);
-    p.lds_bytes = (int)lds;
-    if (lds <= (p.chunked ? 96 * 1024 : 64 * 1024)) return SPENSE_OK;
-    // too much to stage for this split count: use the general kernel
-  }
-  p.decode = 0;
-  p.chunked = 0;
-  p.mt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
-  p.mgroups = (int)((M + 16 * p.mt - 1) / (16 * p.mt));
-  p.rgroups = (int)((d.NT + kWavesPerWG - 1) / kWavesPerWG);
-  if (splits > 0) {
-    p.splits = splits;
+    p.lds_bytes = (int)(p.chunked ? stream_lds_bytes(M) : decode_lds_bytes(d, M, S));
     return SPENSE_OK;
   }
-  const int64_t wgs = (int64_t)p.rgroups * p.mgroups;
-  int64_t s = (1024 + wgs - 1) / wgs;
-  p.splits = (int)std::max<int64_t>(1, std::min<int64_t>(s, max_splits));
+  // More than 16 rows: the chunked streaming kernel with register-blocked
+  // tiles (row tiles x m-tiles per wave; every weight unit feeds each m-tile,
+  // every staged activation fragment each row tile), activations contiguous
+  // (a chosen dense set is gathered into a workspace first).  Enough splits
+  // to fill the CUs with resident workgroups when the row tiles alone do not.
+  struct Preset { int nw, nr, p, ch, mt; };
+  static const Preset kPresets[] = {
+#define SPENSE_PRESET(i, nw, nr, pp, ch, mt) {nw, nr, pp, ch, mt},
+      SPENSE_TILE_PRESETS(SPENSE_PRESET)
+#undef SPENSE_PRESET
+  };
+  constexpr int kNumPresets = (int)(sizeof(kPresets) / sizeof(kPresets[0]));
+  // Two m-tiles per wave up to 128 rows (four need more LDS per workgroup
+  // than they save there), four beyond.  Two row tiles per wave halve the LDS
+  // reads per product but give fewer workgroups: used when the row tiles
+  // alone still give at least one workgroup per two CUs; otherwise one row
+  // tile per wave plus splits.
+  const int64_t wg_nr2 = (d.NT + 15) / 16 * ((M + 31) / 32);
+  int pre = M <= 32 || wg_nr2 < kCUs / 2 ? 0 : M <= 64 ? 1 : M <= 128 ? 2 : 6;
+  if (const char* t = std::getenv("SPENSE_TILE")) {
+    const int v = std::atoi(t);
+    if (v >= 0 && v < kNumPresets) pre = v;
+  }
+  const Preset& q = kPresets[pre];
+  p.chunked = 1;
+  p.preset = pre;
+  p.waves = q.nw;
+  p.nr = q.nr;
+  p.depth = q.p;
+  p.chunk = q.ch;
+  p.mt = q.mt;
+  p.mgroups = (int)((M + 16 * p.mt - 1) / (16 * p.mt));
+  const int64_t rows = std::min<int64_t>(M, 16 * p.mt);
+  const int64_t lds = 2 * rows * (p.chunk * kMacro + 8) * 2;
+  p.lds_bytes = (int)lds;
+  p.rgroups = (int)((d.NT + p.waves * p.nr - 1) / (p.waves * p.nr));
+  int64_t S = splits;
+  if (S == 0) {
+    const int64_t units = (int64_t)p.rgroups * p.mgroups;
+    const int64_t resident = kCUs * std::max<int64_t>(1, kLdsPerCU / lds);
+    S = units >= kCUs / 2 ? 1 : std::max<int64_t>(1, std::min<int64_t>(resident / units, max_splits));
+  }
+  p.splits = (int)S;
   return SPENSE_OK;
 }
 
@@ -324,9 +358,28 @@ int spense_linear_splits(spense_handle h, const void* X, int32_t xdtype, int64_t
   LinearPlan p{};
   const bool x_aligned = aligned16(X) && (ldx % 8) == 0;
   a.gather = d.gather || !x_aligned;
-  int rc = plan_linear(h, M, splits, a.gather != 0, p);
+  int rc = plan_linear(h, M, splits, p);
   if (rc != SPENSE_OK) return rc;
   a.splits = p.splits;
+  if (p.chunked && a.gather) {
+    // the chunked kernels stage a contiguous X'p: gather it once into the handle's workspace
+    const size_t need = (size_t)M * (size_t)d.K_p * 2;
+    if (need > h->xws_bytes) {
+      hipError_t e = hipStreamSynchronize(s);  // earlier launches may still read the old workspace
+      if (e != hipSuccess) return hip_fail(e);
+      if (h->xws) (void)hipFree(h->xws);
+      h->xws = nullptr;
+      h->xws_bytes = 0;
+      e = hipMalloc(&h->xws, need);
+      if (e != hipSuccess) return e == hipErrorOutOfMemory ? SPENSE_ENOMEM : hip_fail(e);
+      h->xws_bytes = need;
+    }
+    hipError_t e = launch_gather_x(d, X, M, ldx, h->xws, s);
+    if (e != hipSuccess) return hip_fail(e);
+    a.X = h->xws;
+    a.ldx = d.K_p;
+    a.gather = 0;
+  }
   if (p.splits > 1) {
     const size_t need = (size_t)p.splits * (size_t)M * (size_t)(d.NT * kRowTile) * 4;
     const size_t need_cnt = (size_t)p.rgroups * (size_t)p.mgroups;

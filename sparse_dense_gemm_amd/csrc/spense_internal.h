@@ -81,24 +81,38 @@ struct LinearArgs {
 
 // Launch configuration chosen on the host.
 struct LinearPlan {
-  int mt;        // m-tiles (16 rows of X each) per workgroup pass: 1, 2 or 4
+  int mt;        // m-tiles (16 rows of X each) per wave: 1, 2 or 4
   int mgroups;   // ceil(M / (16 * mt))
-  int rgroups;   // ceil(NT / waves per workgroup)
+  int rgroups;   // ceil(NT / (waves * nr))
   int splits;
-  // decode path (M <= 16)
-  int decode;    // 1: linear_decode_kernel
   int waves;     // waves per workgroup: 4 or 8
-  int depth;     // macro-steps in flight per wave: 4 or 8
-  int lds_bytes; // dynamic LDS of the decode kernel
-  int chunked;   // 1: activations staged in double-buffered chunks (linear_stream_kernel)
+  int depth;     // units in flight per row tile of a wave (ring depth)
+  int lds_bytes; // dynamic LDS
+  int chunked;   // 0: linear_decode_kernel (whole split staged); 1: linear_stream_kernel
+  int chunk;     // units per staged chunk of linear_stream_kernel
+  int nr;        // row tiles per wave (linear_stream_kernel)
+  int preset;    // index into SPENSE_TILE_PRESETS, or -1 (one row tile and m-tile per wave)
 };
 
-constexpr int kWavesPerWG = 4;
+// Blocked configurations of linear_stream_kernel for batches above 16 rows:
+// X(index, waves per workgroup, row tiles per wave, ring depth, chunk units, m-tiles).
+#define SPENSE_TILE_PRESETS(X) \
+  X(0, 8, 1, 4, 8, 2)          \
+  X(1, 4, 2, 4, 4, 2)          \
+  X(2, 8, 2, 4, 4, 2)          \
+  X(3, 8, 1, 4, 4, 4)          \
+  X(4, 4, 2, 4, 4, 4)          \
+  X(5, 4, 2, 2, 2, 4)          \
+  X(6, 8, 2, 2, 2, 4)          \
+  X(7, 4, 1, 4, 8, 2)
+
 constexpr int kStreamChunk = 8;  // units per activation chunk of linear_stream_kernel
 
 hipError_t launch_pack(const LayerDesc& d, const void* W, int64_t ldw, hipStream_t s);
 hipError_t launch_export(const LayerDesc& d, void* vals, uint32_t* meta, uint8_t* mask, void* dense, hipStream_t s);
 hipError_t launch_linear(const LayerDesc& d, const LinearArgs& a, const LinearPlan& p, hipStream_t s);
 hipError_t launch_zero_i32(int32_t* p, int64_t n, hipStream_t s);
+// X'p = X[:, pip] as a contiguous [M][K_p] bf16 buffer
+hipError_t launch_gather_x(const LayerDesc& d, const void* X, int64_t M, int64_t ldx, void* Xp, hipStream_t s);
 
 }  // namespace spense

@@ -130,8 +130,13 @@ __device__ __forceinline__ bool arrive_last(int32_t* cnt, int S, int* flag) {
   return *flag != 0;
 }
 
-__device__ __forceinline__ void store_y(const LayerDesc& d, const LinearArgs& a, int64_t m, int64_t n, float acc) {
-  const float y = acc * (d.scales ? d.scales[n] : 1.0f);
+// Scales of this lane's four output rows of row tile rt (rows rt*16 + 4(lane/16) + 0..3),
+// loaded when a kernel starts so that its epilogue does not wait on memory.
+__device__ __forceinline__ f32x4 row_scales(const LayerDesc& d, int64_t rt, int lane) {
+  return *(const f32x4*)(d.scales + rt * 16 + 4 * (lane >> 4));
+}
+
+__device__ __forceinline__ void store_y(const LinearArgs& a, int64_t m, int64_t n, float y) {
   if (a.ydtype == DT_F32) ((float*)a.Y)[m * a.ldy + n] = y;
   else ((uint16_t*)a.Y)[m * a.ldy + n] = (uint16_t)bf16_rne(y);
 }
@@ -139,33 +144,41 @@ __device__ __forceinline__ void store_y(const LayerDesc& d, const LinearArgs& a,
 // Writes Y (S == 1) or this split's partial; with S > 1 the last workgroup of
 // the tile adds the partials in split order.  acc: lane l, register r =
 // Y^T[n = 16rt + 4(l/16) + r][m = m0 + 16mt + l%16].
-__device__ __forceinline__ void finish_tile(const LayerDesc& d, const LinearArgs& a, const f32x4* acc, int mtiles,
-                                            int64_t rt, bool active, int64_t m0, int s, int S, int64_t cnt_index,
-                                            int* last_flag) {
+// Epilogue of a wave's nr row tiles (rt0 ..) x mtiles m-tiles; acc[r * mtiles + t],
+// sc[r] = row_scales of row tile rt0 + r.
+__device__ __forceinline__ void finish_tile(const LayerDesc& d, const LinearArgs& a, const f32x4* acc,
+                                            const f32x4* sc, int nr, int mtiles, int64_t rt0, int64_t m0, int s,
+                                            int S, int64_t cnt_index, int* last_flag) {
   const int lane = threadIdx.x & 63;
   const int nb = 4 * (lane >> 4);
   const int64_t NP = d.NT * 16;
   if (S > 1) {
-    if (active)
+    for (int r = 0; r < nr; ++r) {
+      const int64_t rt = rt0 + r;
+      if (rt >= d.NT) break;
       for (int mt = 0; mt < mtiles; ++mt) {
         const int64_t m = m0 + 16 * mt + (lane & 15);
-        if (m < a.M) store_partial(a.ws + ((int64_t)s * a.M + m) * NP + rt * 16 + nb, acc[mt]);
+        if (m < a.M) store_partial(a.ws + ((int64_t)s * a.M + m) * NP + rt * 16 + nb, acc[r * mtiles + mt]);
       }
+    }
     if (!arrive_last(a.counters + cnt_index, S, last_flag)) return;
   }
-  if (!active) return;
-  for (int mt = 0; mt < mtiles; ++mt) {
-    const int64_t m = m0 + 16 * mt + (lane & 15);
-    if (m >= a.M) continue;
-    f32x4 sum = acc[mt];
-    if (S > 1) {
-      sum = f32x4{0.f, 0.f, 0.f, 0.f};
-      for (int s2 = 0; s2 < S; ++s2) sum += load_partial(a.ws + ((int64_t)s2 * a.M + m) * NP + rt * 16 + nb);
-    }
+  for (int r = 0; r < nr; ++r) {
+    const int64_t rt = rt0 + r;
+    if (rt >= d.NT) break;
+    for (int mt = 0; mt < mtiles; ++mt) {
+      const int64_t m = m0 + 16 * mt + (lane & 15);
+      if (m >= a.M) continue;
+      f32x4 sum = acc[r * mtiles + mt];
+      if (S > 1) {
+        sum = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int s2 = 0; s2 < S; ++s2) sum += load_partial(a.ws + ((int64_t)s2 * a.M + m) * NP + rt * 16 + nb);
+      }
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int64_t n = rt * 16 + nb + r;
-      if (n < d.N) store_y(d, a, m, n, sum[r]);
+      for (int q = 0; q < 4; ++q) {
+        const int64_t n = rt * 16 + nb + q;
+        if (n < d.N) store_y(a, m, n, sum[q] * sc[r][q]);
+      }
     }
   }
 }
@@ -416,10 +429,9 @@ __device__ __forceinline__ void load_unit(UnitFrag<WT>& f, const uint8_t* unit, 
 }
 
 // Two SMFMACs: A0 with B0 (index half 0), A1 with B1 (index half 1).
+// The unit's two A operands as bf16 (e4m3 widened exactly).
 template <typename WT>
-__device__ __forceinline__ void mac_unit(f32x4& acc0, f32x4& acc1, const UnitFrag<WT>& f, int idx, const bf16x16& B0,
-                                         const bf16x16& B1) {
-  bf16x8 A0, A1;
+__device__ __forceinline__ void unit_a(const UnitFrag<WT>& f, bf16x8& A0, bf16x8& A1) {
   if constexpr (sizeof(WT) == 1) {
     A0 = fp8x8_to_bf16(f.a.x, f.a.y);
     A1 = fp8x8_to_bf16(f.a.z, f.a.w);
@@ -427,6 +439,13 @@ __device__ __forceinline__ void mac_unit(f32x4& acc0, f32x4& acc1, const UnitFra
     A0 = as_bf16x8(f.a0);
     A1 = as_bf16x8(f.a1);
   }
+}
+
+template <typename WT>
+__device__ __forceinline__ void mac_unit(f32x4& acc0, f32x4& acc1, const UnitFrag<WT>& f, int idx, const bf16x16& B0,
+                                         const bf16x16& B1) {
+  bf16x8 A0, A1;
+  unit_a<WT>(f, A0, A1);
   acc0 = smfmac_bf16<0>(A0, B0, acc0, idx);
   acc1 = smfmac_bf16<1>(A1, B1, acc1, idx);
 }
@@ -456,111 +475,6 @@ __device__ __forceinline__ u32x4 gather8_from(const uint16_t* xr, const u32x4& i
 __device__ __forceinline__ u32x4 gather8(const LinearArgs& a, const LayerDesc& d, const uint16_t* xr, int64_t col) {
   if (!a.gather) return *(const u32x4*)(xr + col);
   return gather8_from(xr, *(const u32x4*)(d.pip + col), *(const u32x4*)(d.pip + col + 4));
-}
-
-// ---------------------------------------------------------------------------
-// linear, general M: chunks of CH macro-steps staged in LDS per workgroup,
-// MT m-tiles of 16 activation rows per pass
-// ---------------------------------------------------------------------------
-constexpr int kPitch = 136;  // staged X'p row: 128 bf16 + 8 pad (272 B, conflict-free 16 B reads)
-
-template <int MT, int CH>
-__device__ __forceinline__ void stage_chunk(uint16_t (*xs)[MT * 16][kPitch], const LayerDesc& d, const LinearArgs& a,
-                                            int64_t col_base, int nc, int64_t m0, int mloc) {
-  const uint16_t* X = (const uint16_t*)a.X;
-  const int per_macro = mloc * 16;
-  const int units = nc * per_macro;
-  for (int e = threadIdx.x; e < units; e += kWavesPerWG * 64) {
-    const int u = e / per_macro;
-    const int rem = e - u * per_macro;
-    const int m = rem >> 4, c8 = rem & 15;
-    *(u32x4*)&xs[u][m][8 * c8] = gather8(a, d, X + (m0 + m) * a.ldx, col_base + 128 * u + 8 * c8);
-  }
-}
-
-template <int MT>
-__device__ __forceinline__ void load_bt(bf16x16 (&B)[MT], const uint16_t (*xsu)[kPitch], int col, int lane, int mloc) {
-  const int bcol = col + 16 * (lane >> 4);
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) {
-    const int m = 16 * mt + (lane & 15);
-    if (m < mloc) B[mt] = lds_b(&xsu[m][bcol]);
-    else B[mt] = as_bf16x16(u32x4{0, 0, 0, 0}, u32x4{0, 0, 0, 0});
-  }
-}
-
-template <typename WT, int MT, int CH>
-__global__ __launch_bounds__(kWavesPerWG * 64) void linear_kernel(LayerDesc d, LinearArgs a, LinearPlan p) {
-  __shared__ __attribute__((aligned(16))) uint16_t xs[CH][MT * 16][kPitch];
-  __shared__ int last_flag;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int bid = blockIdx.x;
-  const int rg = bid % p.rgroups;
-  const int rest = bid / p.rgroups;
-  const int S = p.splits;
-  const int s = rest % S;
-  const int mg = rest / S;
-  const int64_t rt = (int64_t)rg * kWavesPerWG + wave;
-  const bool active = rt < d.NT;
-  const int64_t m0 = (int64_t)mg * MT * 16;
-  const int mloc = (int)(a.M - m0 < MT * 16 ? a.M - m0 : MT * 16);
-  const int64_t ms0 = d.n_sm * s / S, ms1 = d.n_sm * (s + 1) / S;
-  const int64_t md0 = d.n_dm * s / S, md1 = d.n_dm * (s + 1) / S;
-  const uint8_t* tile = d.wpack + (active ? rt : 0) * d.tile_bytes;
-
-  f32x4 acc[MT], acc1[MT];
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt] = acc1[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // sparse region: one unit per macro-step, two SMFMACs (steps q = 0, 1)
-  for (int64_t c0 = ms0; c0 < ms1; c0 += CH) {
-    const int nc = (int)(ms1 - c0 < CH ? ms1 - c0 : CH);
-    __syncthreads();
-    stage_chunk<MT, CH>(xs, d, a, 128 * c0, nc, m0, mloc);
-    __syncthreads();
-    if (active) {
-#pragma unroll
-      for (int u = 0; u < CH; ++u) {
-        if (u < nc) {
-          UnitFrag<WT> f;
-          load_unit<WT>(f, tile + (c0 + u) * kUnit<WT>, tile + d.idx_off + (c0 + u) * 256 + 4 * lane, lane);
-          bf16x16 B0[MT], B1[MT];
-          load_bt<MT>(B0, xs[u], 0, lane, mloc);
-          load_bt<MT>(B1, xs[u], 64, lane, mloc);
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) mac_unit<WT>(acc[mt], acc1[mt], f, (int)f.idx, B0[mt], B1[mt]);
-        }
-      }
-    }
-  }
-
-  // dense region: two units per macro-step, each two SMFMACs on one 64-column step
-  for (int64_t c0 = md0; c0 < md1; c0 += CH) {
-    const int nc = (int)(md1 - c0 < CH ? md1 - c0 : CH);
-    __syncthreads();
-    stage_chunk<MT, CH>(xs, d, a, d.K_sp + 128 * c0, nc, m0, mloc);
-    __syncthreads();
-    if (active) {
-#pragma unroll
-      for (int u = 0; u < CH; ++u) {
-        if (u < nc) {
-#pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            const uint8_t* unit = tile + (d.n_sm + 2 * (c0 + u) + h) * kUnit<WT>;
-            UnitFrag<WT> f;
-            load_unit<WT>(f, unit, unit + 16 * lane, lane);
-            bf16x16 B[MT];
-            load_bt<MT>(B, xs[u], 64 * h, lane, mloc);
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) mac_unit<WT>(acc[mt], acc1[mt], f, (int)kDenseIdx, B[mt], B[mt]);
-          }
-        }
-      }
-    }
-  }
-#pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt] += acc1[mt];
-  finish_tile(d, a, acc, MT, rt, active, m0, s, S, (int64_t)mg * p.rgroups + rg, &last_flag);
 }
 
 // ---------------------------------------------------------------------------
@@ -600,61 +514,84 @@ __global__ __launch_bounds__(NW * 64) void linear_decode_kernel(LayerDesc d, Lin
   auto unit_ptr = [&](int k) { return tile + (k + (k < ns ? sbase : dbase)) * kUnit<WT>; };
   auto idx_ptr = [&](int k) { return k < ns ? sidx + k * 256 : unit_ptr(k); };
 
-  UnitFrag<WT> wr[P];
-  const bool stream = active && total > 0;
-  if (stream) {
+  const f32x4 sc = row_scales(d, active ? rt : 0, lane);
+
+  // Stage X'p[0..M)[split columns] in LDS once: sparse macro-steps, then
+  // dense ones, in batches of kStageBatch 16-byte pieces per thread (all index
+  // loads, then all activation loads, then the LDS writes, so a batch costs one
+  // (contiguous) or two (gathered) memory round trips).  Every thread issues
+  // every load of a batch: pieces past the end read piece 0 (a valid address)
+  // and are not stored, so the load count is fixed.  The first batch's
+  // activation loads go out before the weight ring, so writing them to LDS
+  // does not wait for the ring.
+  const uint16_t* X = (const uint16_t*)a.X;
+  const int per_row = (ns + nd) * 16;
+  const int pieces = M * per_row;
+  constexpr int kStageBatch = GATHER ? 2 : 8;
+  int64_t rowoff[kStageBatch], col[kStageBatch];
+  int lds_off[kStageBatch];
+  bool ok[kStageBatch];
+  u32x4 val[kStageBatch], i0[kStageBatch], i1[kStageBatch];
+  auto locate = [&](int e0) {
 #pragma unroll
-    for (int i = 0; i < P; ++i) {
-      const int k = i < total ? i : total - 1;
-      load_unit<WT>(wr[i], unit_ptr(k), idx_ptr(k) + 4 * lane, lane);
+    for (int j = 0; j < kStageBatch; ++j) {
+      const int e = e0 + j * NW * 64;
+      ok[j] = e < pieces;
+      const int ee = ok[j] ? e : 0;
+      const int mrow = ee / per_row;
+      const int rem = ee - mrow * per_row;
+      const int u = rem >> 4, c8 = rem & 15;
+      rowoff[j] = (int64_t)mrow * a.ldx;
+      col[j] = (u < ns ? 128 * (ms0 + u) : d.K_sp + 128 * (md0 + u - ns)) + 8 * c8;
+      lds_off[j] = mrow * pitch + 128 * u + 8 * c8;
     }
+  };
+  auto load_first = [&]() {  // contiguous: the activations; gathered: the column indices
+#pragma unroll
+    for (int j = 0; j < kStageBatch; ++j) {
+      if constexpr (!GATHER) {
+        val[j] = *(const u32x4*)(X + rowoff[j] + col[j]);
+      } else {
+        i0[j] = *(const u32x4*)(d.pip + col[j]);
+        i1[j] = *(const u32x4*)(d.pip + col[j] + 4);
+      }
+    }
+  };
+  auto load_second = [&]() {  // gathered: the activations at those columns
+    if constexpr (GATHER) {
+#pragma unroll
+      for (int j = 0; j < kStageBatch; ++j) val[j] = gather8_from(X + rowoff[j], i0[j], i1[j]);
+    }
+  };
+  auto store = [&]() {
+#pragma unroll
+    for (int j = 0; j < kStageBatch; ++j)
+      if (ok[j]) *(u32x4*)(xs_dyn + lds_off[j]) = val[j];
+  };
+  const bool staging = pieces > 0;
+  if (staging) {
+    locate(threadIdx.x);
+    load_first();
   }
 
-  // stage X'p[0..M)[split columns] once: sparse macro-steps, then dense ones.
-  // Batches of kStageBatch 16-byte pieces per thread: all index loads, then all
-  // activation loads, then the LDS writes, so a batch costs one (contiguous) or
-  // two (gathered) memory round trips instead of one or two per piece.
-  {
-    const uint16_t* X = (const uint16_t*)a.X;
-    const int per_row = (ns + nd) * 16;
-    const int pieces = M * per_row;
-    constexpr int kStageBatch = GATHER ? 2 : 4;
-    for (int e0 = threadIdx.x; e0 < pieces; e0 += kStageBatch * NW * 64) {
-      int64_t col[kStageBatch];
-      int lds_off[kStageBatch], row[kStageBatch];
-      bool ok[kStageBatch];
+  // weight ring; waves without units (past the last row tile, or an empty
+  // split) load unit 0 of tile 0 so that every wave issues the same loads
+  const bool stream = active && total > 0;
+  UnitFrag<WT> wr[P];
 #pragma unroll
-      for (int j = 0; j < kStageBatch; ++j) {
-        const int e = e0 + j * NW * 64;
-        ok[j] = e < pieces;
-        const int ee = ok[j] ? e : 0;
-        const int mrow = ee / per_row;
-        const int rem = ee - mrow * per_row;
-        const int u = rem >> 4, c8 = rem & 15;
-        row[j] = mrow;
-        col[j] = (u < ns ? 128 * (ms0 + u) : d.K_sp + 128 * (md0 + u - ns)) + 8 * c8;
-        lds_off[j] = mrow * pitch + 128 * u + 8 * c8;
-      }
-      u32x4 val[kStageBatch];
-      if constexpr (!GATHER) {
-#pragma unroll
-        for (int j = 0; j < kStageBatch; ++j)
-          if (ok[j]) val[j] = *(const u32x4*)(X + (int64_t)row[j] * a.ldx + col[j]);
-      } else {
-        u32x4 i0[kStageBatch], i1[kStageBatch];
-#pragma unroll
-        for (int j = 0; j < kStageBatch; ++j)
-          if (ok[j]) {
-            i0[j] = *(const u32x4*)(d.pip + col[j]);
-            i1[j] = *(const u32x4*)(d.pip + col[j] + 4);
-          }
-#pragma unroll
-        for (int j = 0; j < kStageBatch; ++j)
-          if (ok[j]) val[j] = gather8_from(X + (int64_t)row[j] * a.ldx, i0[j], i1[j]);
-      }
-#pragma unroll
-      for (int j = 0; j < kStageBatch; ++j)
-        if (ok[j]) *(u32x4*)(xs_dyn + lds_off[j]) = val[j];
+  for (int i = 0; i < P; ++i) {
+    const int k = i < total ? i : total - 1;
+    load_unit<WT>(wr[i], stream ? unit_ptr(k) : d.wpack, (stream ? idx_ptr(k) : d.wpack) + 4 * lane, lane);
+  }
+
+  if (staging) {
+    load_second();
+    store();
+    for (int e0 = threadIdx.x + kStageBatch * NW * 64; e0 < pieces; e0 += kStageBatch * NW * 64) {
+      locate(e0);
+      load_first();
+      load_second();
+      store();
     }
   }
   __syncthreads();
@@ -687,78 +624,84 @@ __global__ __launch_bounds__(NW * 64) void linear_decode_kernel(LayerDesc d, Lin
       if (k0 + i < total) consume(i, k0 + i);
   }
   const f32x4 acc = acc0 + acc1;
-  finish_tile(d, a, &acc, 1, rt, active, 0, s, S, rg, &last_flag);
+  finish_tile(d, a, &acc, &sc, 1, 1, rt, 0, s, S, rg, &last_flag);
 }
 
 // ---------------------------------------------------------------------------
-// linear, decode (M <= 16) with chunked activation staging: the split's
-// activations pass through a double-buffered LDS ring of CH-unit chunks, so
-// the LDS footprint does not grow with the split width and one split covers
-// the whole K range at any M <= 16.  One barrier per chunk; it waits on LDS
-// only, so the weight ring stays in flight across it.  For a chosen dense set
-// the split's column map is staged in LDS once, so the per-chunk gathers
-// depend on LDS reads only.
+// linear, streamed activations: the split's activations pass through a
+// double-buffered LDS ring of CH-unit chunks, so the LDS footprint does not
+// grow with the split width.  One barrier per chunk; it waits on LDS only, so
+// the weight ring stays in flight across it.  Each wave owns NR consecutive
+// 16-row tiles and MT m-tiles of 16 activation rows: every weight unit loaded
+// from HBM feeds MT pairs of products, and every activation fragment read
+// from LDS feeds NR of them.  Activations are read as a contiguous X'p (for
+// a chosen dense set the host gathers it into a workspace first).
 // ---------------------------------------------------------------------------
-template <typename WT, int NW, int P, int CH, bool GATHER>
+template <typename WT, int NW, int NR, int P, int CH, int MT>
 __global__ __launch_bounds__(NW * 64) void linear_stream_kernel(LayerDesc d, LinearArgs a, LinearPlan p) {
   static_assert(CH % P == 0, "a chunk must hold whole rings");
   extern __shared__ __attribute__((aligned(16))) uint16_t xs_dyn[];
   __shared__ int last_flag;
-  constexpr int kPitch2 = CH * 128 + 8;                 // staged row: CH unit slots of 128 columns + pad
-  constexpr int kPieces = (16 * CH * 16) / (NW * 64);  // 16-byte pieces per thread per chunk at M = 16
+  constexpr int kPitch2 = CH * 128 + 8;                      // staged row: CH unit slots of 128 columns + pad
+  constexpr int kPieces = (16 * MT * CH * 16) / (NW * 64);  // 16-byte pieces per thread per chunk (full m-group)
+  static_assert(kPieces * NW * 64 == 16 * MT * CH * 16, "pieces must divide evenly");
+  constexpr bool kSplitAcc = NR == 1 && MT == 1;  // two accumulators when there is nothing to interleave
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rg = blockIdx.x % p.rgroups;
   const int S = p.splits;
   const int s = (blockIdx.x / p.rgroups) % S;
-  const int64_t rt = (int64_t)rg * NW + wave;
-  const bool active = rt < d.NT;
+  const int mg = blockIdx.x / (p.rgroups * S);
+  const int64_t rt0 = ((int64_t)rg * NW + wave) * NR;
   const int64_t ms0 = d.n_sm * s / S, ms1 = d.n_sm * (s + 1) / S;
   const int64_t md0 = d.n_dm * s / S, md1 = d.n_dm * (s + 1) / S;
   const int ns = (int)(ms1 - ms0), nd = (int)(md1 - md0);
   const int total = ns + 2 * nd;  // units
   const int nchunks = (total + CH - 1) / CH;
-  const int M = (int)a.M;
+  const int64_t m0 = (int64_t)mg * 16 * MT;
+  const int mloc = (int)(a.M - m0 < 16 * MT ? a.M - m0 : 16 * MT);  // activation rows of this m-group
+  const int rows = (int)(a.M < 16 * MT ? a.M : 16 * MT);            // rows of one staged buffer
   const int m = lane & 15, g = lane >> 4;
-  const uint8_t* tile = d.wpack + (active ? rt : 0) * d.tile_bytes;
   const int64_t sbase = ms0, dbase = d.n_sm + 2 * md0 - ns;
-  const uint8_t* sidx = tile + d.idx_off + ms0 * 256;
+  // row tiles past the end read tile 0 (valid memory); their results are never stored
+  const uint8_t* tile[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) tile[r] = d.wpack + (rt0 + r < d.NT ? rt0 + r : 0) * d.tile_bytes;
   uint16_t* xbuf0 = xs_dyn;
-  uint16_t* xbuf1 = xs_dyn + M * kPitch2;
-  int32_t* pip_l = (int32_t*)(xs_dyn + 2 * M * kPitch2);  // split column map (GATHER)
-  const uint16_t* X = (const uint16_t*)a.X;
+  uint16_t* xbuf1 = xs_dyn + rows * kPitch2;
+  const uint16_t* X = (const uint16_t*)a.X + m0 * a.ldx;
 
-  auto unit_ptr = [&](int k) { return tile + (k + (k < ns ? sbase : dbase)) * kUnit<WT>; };
-  auto idx_ptr = [&](int k) { return k < ns ? sidx + k * 256 : unit_ptr(k); };
+  auto unit_ptr = [&](int r, int k) { return tile[r] + (k + (k < ns ? sbase : dbase)) * kUnit<WT>; };
+  auto idx_ptr = [&](int r, int k) { return k < ns ? tile[r] + d.idx_off + (ms0 + k) * 256 : unit_ptr(r, k); };
   // first column of unit k in the split's column list: sparse units 128 wide, dense units 64
   auto unit_lcol = [&](int k) { return k < ns ? 128 * k : 128 * ns + 64 * (k - ns); };
+  auto load_step = [&](UnitFrag<WT>(&f)[NR], int k) {
+#pragma unroll
+    for (int r = 0; r < NR; ++r) load_unit<WT>(f[r], unit_ptr(r, k), idx_ptr(r, k) + 4 * lane, lane);
+  };
 
-  UnitFrag<WT> wr[P];
-  const bool stream = active && total > 0;
+  f32x4 sc[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) sc[r] = row_scales(d, rt0 + r < d.NT ? rt0 + r : 0, lane);
+
+  UnitFrag<WT> wr[P][NR];
+  // every wave streams (waves whose row tiles are all past the end stream tile
+  // 0), so all waves of the workgroup meet the same barriers
+  const bool stream = total > 0;
   if (stream) {
 #pragma unroll
-    for (int i = 0; i < P; ++i) {
-      const int k = i < total ? i : total - 1;
-      load_unit<WT>(wr[i], unit_ptr(k), idx_ptr(k) + 4 * lane, lane);
-    }
-  }
-
-  if constexpr (GATHER) {
-    // the split's column map: sparse columns of X'p, then dense ones
-    const int ncols = 128 * (ns + nd);
-    for (int e = threadIdx.x; 4 * e < ncols; e += NW * 64) {
-      const int c = 4 * e;
-      const int64_t col = c < 128 * ns ? 128 * ms0 + c : d.K_sp + 128 * md0 + (c - 128 * ns);
-      *(u32x4*)(pip_l + c) = *(const u32x4*)(d.pip + col);
-    }
-    __syncthreads();
+    for (int i = 0; i < P; ++i) load_step(wr[i], i < total ? i : total - 1);
   }
 
   // piece e of a chunk: row = e / (16 CH), unit slot j = (e / 16) % CH, 8-column group c8 = e % 16.
   // Loads are issued here and only consumed by write_chunk (after the chunk's
-  // compute), so waiting for them never stalls the weight ring.
-  u32x4 xv[GATHER ? 1 : kPieces];
-  uint32_t xh[GATHER ? kPieces : 1][8];
+  // compute).  Every thread issues the same loads whatever its piece: pieces
+  // outside the batch or the split read row 0, column 0 (X'p holds at least
+  // 128 columns) and their values are never used.  With a fixed load count
+  // the wait before write_chunk covers just these loads, so the weight ring
+  // stays in flight.  The sparse region of X'p starts at column 0, the dense
+  // one at K_sp (equal to K_s when X itself is X'p).
+  u32x4 xv[kPieces];
   auto issue_chunk = [&](int c) {
 #pragma unroll
     for (int i = 0; i < kPieces; ++i) {
@@ -766,20 +709,11 @@ __global__ __launch_bounds__(NW * 64) void linear_stream_kernel(LayerDesc d, Lin
       const int row = e / (16 * CH);
       const int j = (e / 16) % CH, c8 = e % 16;
       const int k = c * CH + j;
-      const bool ok = row < M && k < total && (k < ns || c8 < 8);
-      if (ok) {
-        const int lc = unit_lcol(k) + 8 * c8;
-        const uint32_t rowoff = (uint32_t)(row * a.ldx);
-        if constexpr (!GATHER) {
-          const int64_t col = k < ns ? 128 * ms0 + lc : d.K_s + 128 * md0 + (lc - 128 * ns);
-          xv[i] = *(const u32x4*)(X + rowoff + (uint32_t)col);
-        } else {
-          const u32x4 i0 = *(const u32x4*)(pip_l + lc), i1 = *(const u32x4*)(pip_l + lc + 4);
-          const int src[8] = {(int)i0.x, (int)i0.y, (int)i0.z, (int)i0.w, (int)i1.x, (int)i1.y, (int)i1.z, (int)i1.w};
-#pragma unroll
-          for (int t = 0; t < 8; ++t) xh[i][t] = src[t] >= 0 ? (uint32_t)X[rowoff + (uint32_t)src[t]] : 0u;
-        }
-      }
+      const bool ok = row < mloc && k < total && (k < ns || c8 < 8);
+      const int lc = ok ? unit_lcol(k) + 8 * c8 : 0;
+      const uint32_t rowoff = ok ? (uint32_t)(row * a.ldx) : 0u;
+      const int64_t col = !ok ? 0 : k < ns ? 128 * ms0 + lc : d.K_sp + 128 * md0 + (lc - 128 * ns);
+      xv[i] = *(const u32x4*)(X + rowoff + (uint32_t)col);
     }
   };
   auto write_chunk = [&](uint16_t* buf) {
@@ -787,18 +721,7 @@ __global__ __launch_bounds__(NW * 64) void linear_stream_kernel(LayerDesc d, Lin
     for (int i = 0; i < kPieces; ++i) {
       const int e = threadIdx.x + i * NW * 64;
       const int row = e / (16 * CH);
-      if (row < M) {
-        u32x4 v;
-        if constexpr (!GATHER) {
-          v = xv[i];
-        } else {
-          v.x = xh[i][0] | (xh[i][1] << 16);
-          v.y = xh[i][2] | (xh[i][3] << 16);
-          v.z = xh[i][4] | (xh[i][5] << 16);
-          v.w = xh[i][6] | (xh[i][7] << 16);
-        }
-        *(u32x4*)(buf + row * kPitch2 + 128 * ((e / 16) % CH) + 8 * (e % 16)) = v;
-      }
+      if (row < mloc) *(u32x4*)(buf + row * kPitch2 + 128 * ((e / 16) % CH) + 8 * (e % 16)) = xv[i];
     }
   };
 
@@ -806,48 +729,86 @@ __global__ __launch_bounds__(NW * 64) void linear_stream_kernel(LayerDesc d, Lin
   write_chunk(xbuf0);
   __syncthreads();
 
-  f32x4 acc0 = f32x4{0.f, 0.f, 0.f, 0.f}, acc1 = f32x4{0.f, 0.f, 0.f, 0.f};
-  // Lanes of activation rows m >= M read row 0: output column m depends only
-  // on B column m, and columns m >= M are never stored.
-  const int xoff = (m < M ? m : 0) * kPitch2 + 16 * g;
-  for (int c = 0; c < nchunks; ++c) {
+  f32x4 acc[NR * MT], acc1 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int t = 0; t < NR * MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // Lanes of activation rows beyond the batch read row 0: output column m
+  // depends only on B column m, and those columns are never stored.
+  int xoff[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) xoff[t] = (16 * t + m < mloc ? 16 * t + m : 0) * kPitch2 + 16 * g;
+  auto consume = [&](const UnitFrag<WT>(&f)[NR], int k, int j, const uint16_t* xb) {
+    const bool sp = k < ns;
+    const int col1 = sp ? 128 * j + 64 : 128 * j;
+    if constexpr (kSplitAcc) {
+      mac_unit<WT>(acc[0], acc1, f[0], sp ? (int)f[0].idx : (int)kDenseIdx, lds_b(xb + xoff[0] + 128 * j),
+                   lds_b(xb + xoff[0] + col1));
+    } else {
+      bf16x8 A0[NR], A1[NR];
+      int idx[NR];
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        unit_a<WT>(f[r], A0[r], A1[r]);
+        idx[r] = sp ? (int)f[r].idx : (int)kDenseIdx;
+      }
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        const bf16x16 B0 = lds_b(xb + xoff[t] + 128 * j);
+#pragma unroll
+        for (int r = 0; r < NR; ++r) acc[r * MT + t] = smfmac_bf16<0>(A0[r], B0, acc[r * MT + t], idx[r]);
+      }
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        const bf16x16 B1 = lds_b(xb + xoff[t] + col1);
+#pragma unroll
+        for (int r = 0; r < NR; ++r) acc[r * MT + t] = smfmac_bf16<1>(A1[r], B1, acc[r * MT + t], idx[r]);
+      }
+    }
+  };
+  // Full chunks: every ring slot is consumed and refilled unconditionally and
+  // the loop body has no branch around ring registers (a merge of two paths
+  // would copy them, and a copy must wait for their loads to land).
+  const int nfull = total / CH;
+  for (int c = 0; c < nfull; ++c) {
     const bool more = c + 1 < nchunks;
     if (more) issue_chunk(c + 1);
-    const uint16_t* xb = ((c & 1) ? xbuf1 : xbuf0) + xoff;
-    if (stream) {
-      if ((c + 1) * CH <= total) {
-        // whole chunk: every ring slot consumed and refilled unconditionally
+    const uint16_t* xb = (c & 1) ? xbuf1 : xbuf0;
 #pragma unroll
-        for (int j = 0; j < CH; ++j) {
-          const int k = c * CH + j;
-          const bool sp = k < ns;
-          const int col1 = sp ? 128 * j + 64 : 128 * j;
-          UnitFrag<WT>& f = wr[j % P];
-          mac_unit<WT>(acc0, acc1, f, sp ? (int)f.idx : (int)kDenseIdx, lds_b(xb + 128 * j), lds_b(xb + col1));
-          const int kn = k + P < total ? k + P : total - 1;
-          load_unit<WT>(f, unit_ptr(kn), idx_ptr(kn) + 4 * lane, lane);
-        }
-      } else {
-        // last, partial chunk: the remaining units are already in the ring
-#pragma unroll
-        for (int j = 0; j < CH; ++j) {
-          const int k = c * CH + j;
-          if (k < total) {
-            const bool sp = k < ns;
-            const int col1 = sp ? 128 * j + 64 : 128 * j;
-            UnitFrag<WT>& f = wr[j % P];
-            mac_unit<WT>(acc0, acc1, f, sp ? (int)f.idx : (int)kDenseIdx, lds_b(xb + 128 * j), lds_b(xb + col1));
-            const int kn = k + P < total ? k + P : total - 1;
-            if (k + P < total) load_unit<WT>(f, unit_ptr(kn), idx_ptr(kn) + 4 * lane, lane);
-          }
-        }
-      }
+    for (int j = 0; j < CH; ++j) {
+      const int k = c * CH + j;
+      consume(wr[j % P], k, j, xb);
+      load_step(wr[j % P], k + P < total ? k + P : total - 1);
     }
     if (more) write_chunk((c & 1) ? xbuf0 : xbuf1);
     __syncthreads();
   }
-  const f32x4 acc = acc0 + acc1;
-  finish_tile(d, a, &acc, 1, rt, active, 0, s, S, rg, &last_flag);
+  // last, partial chunk (never followed by another): its first units are in the ring
+  if (nfull < nchunks) {
+    const int c = nfull;
+    const uint16_t* xb = (c & 1) ? xbuf1 : xbuf0;
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const int k = c * CH + j;
+      if (k < total) {
+        consume(wr[j % P], k, j, xb);
+        if (k + P < total) load_step(wr[j % P], k + P);
+      }
+    }
+  }
+  if constexpr (kSplitAcc) acc[0] += acc1;
+  finish_tile(d, a, acc, sc, NR, MT, rt0, m0, s, S, (int64_t)mg * p.rgroups + rg, &last_flag);
+}
+
+// X'p[m][j] = X[m][pip[j]] (0 where pip[j] < 0), as a contiguous [M][K_p]
+// workspace for batches staged by several m-tiles.  One thread per 8 columns.
+__global__ void gather_x_kernel(LayerDesc d, const uint16_t* __restrict__ X, int64_t M, int64_t ldx,
+                                uint16_t* __restrict__ Xp) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t per_row = d.K_p / 8;
+  if (gid >= M * per_row) return;
+  const int64_t mrow = gid / per_row, col = 8 * (gid % per_row);
+  *(u32x4*)(Xp + mrow * d.K_p + col) =
+      gather8_from(X + mrow * ldx, *(const u32x4*)(d.pip + col), *(const u32x4*)(d.pip + col + 4));
 }
 
 // fp32 weights: VALU, one wave per output row, lanes stride over groups and dense columns.
@@ -903,13 +864,6 @@ hipError_t launch_export_units(const LayerDesc& d, void* vals, uint32_t* meta, u
   return hipGetLastError();
 }
 
-template <typename WT, int MT, int CH>
-hipError_t launch_linear_t(const LayerDesc& d, const LinearArgs& a, const LinearPlan& p, hipStream_t s) {
-  const unsigned grid = (unsigned)((int64_t)p.rgroups * p.splits * p.mgroups);
-  linear_kernel<WT, MT, CH><<<grid, kWavesPerWG * 64, 0, s>>>(d, a, p);
-  return hipGetLastError();
-}
-
 template <typename WT, int NW, int P>
 hipError_t launch_decode_t(const LayerDesc& d, const LinearArgs& a, const LinearPlan& p, hipStream_t s) {
   const unsigned grid = (unsigned)((int64_t)p.rgroups * p.splits);
@@ -925,25 +879,41 @@ hipError_t allow_lds(K kernel, int bytes) {
   return hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
 }
 
+template <typename WT, int NW, int NR, int P, int CH, int MT>
+hipError_t launch_stream_k(const LayerDesc& d, const LinearArgs& a, const LinearPlan& p, hipStream_t s) {
+  if (p.waves != NW || p.nr != NR || p.depth != P || p.chunk != CH || p.mt != MT) return hipErrorInvalidValue;
+  const unsigned grid = (unsigned)((int64_t)p.rgroups * p.splits * p.mgroups);
+  auto k = linear_stream_kernel<WT, NW, NR, P, CH, MT>;
+  hipError_t e = allow_lds(k, p.lds_bytes);
+  if (e != hipSuccess) return e;
+  k<<<grid, NW * 64, p.lds_bytes, s>>>(d, a, p);
+  return hipGetLastError();
+}
+
+// single row tile and m-tile per wave: X'p contiguous (gathered beforehand when needed)
 template <typename WT, int NW, int P>
 hipError_t launch_stream_t(const LayerDesc& d, const LinearArgs& a, const LinearPlan& p, hipStream_t s) {
-  const unsigned grid = (unsigned)((int64_t)p.rgroups * p.splits);
-  hipError_t e;
-  if (a.gather) {
-    auto k = linear_stream_kernel<WT, NW, P, kStreamChunk, true>;
-    if ((e = allow_lds(k, p.lds_bytes)) != hipSuccess) return e;
-    k<<<grid, NW * 64, p.lds_bytes, s>>>(d, a, p);
-  } else {
-    auto k = linear_stream_kernel<WT, NW, P, kStreamChunk, false>;
-    if ((e = allow_lds(k, p.lds_bytes)) != hipSuccess) return e;
-    k<<<grid, NW * 64, p.lds_bytes, s>>>(d, a, p);
+  if (a.gather) return hipErrorInvalidValue;
+  return launch_stream_k<WT, NW, 1, P, kStreamChunk, 1>(d, a, p, s);
+}
+
+// blocked tiles (table kTilePresets): X'p contiguous, gathered beforehand when needed
+template <typename WT>
+hipError_t launch_stream_preset(const LayerDesc& d, const LinearArgs& a, const LinearPlan& p, hipStream_t s) {
+  if (a.gather) return hipErrorInvalidValue;
+  switch (p.preset) {
+#define SPENSE_PRESET(i, nw, nr, pp, ch, mt) \
+  case i: return launch_stream_k<WT, nw, nr, pp, ch, mt>(d, a, p, s);
+    SPENSE_TILE_PRESETS(SPENSE_PRESET)
+#undef SPENSE_PRESET
+    default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }
 
 template <typename WT>
 hipError_t launch_linear_units(const LayerDesc& d, const LinearArgs& a, const LinearPlan& p, hipStream_t s) {
-  if (p.decode && p.chunked) {
+  if (p.chunked && p.preset >= 0) return launch_stream_preset<WT>(d, a, p, s);
+  if (p.chunked) {
     switch (p.waves * 100 + p.depth) {
       case 404: return launch_stream_t<WT, 4, 4>(d, a, p, s);
       case 408: return launch_stream_t<WT, 4, 8>(d, a, p, s);
@@ -952,19 +922,11 @@ hipError_t launch_linear_units(const LayerDesc& d, const LinearArgs& a, const Li
       default: return hipErrorInvalidValue;
     }
   }
-  if (p.decode) {
-    switch (p.waves * 100 + p.depth) {
-      case 404: return launch_decode_t<WT, 4, 4>(d, a, p, s);
-      case 408: return launch_decode_t<WT, 4, 8>(d, a, p, s);
-      case 804: return launch_decode_t<WT, 8, 4>(d, a, p, s);
-      case 808: return launch_decode_t<WT, 8, 8>(d, a, p, s);
-      default: return hipErrorInvalidValue;
-    }
-  }
-  switch (p.mt) {
-    case 1: return launch_linear_t<WT, 1, 4>(d, a, p, s);
-    case 2: return launch_linear_t<WT, 2, 4>(d, a, p, s);
-    case 4: return launch_linear_t<WT, 4, 2>(d, a, p, s);
+  switch (p.waves * 100 + p.depth) {
+    case 404: return launch_decode_t<WT, 4, 4>(d, a, p, s);
+    case 408: return launch_decode_t<WT, 4, 8>(d, a, p, s);
+    case 804: return launch_decode_t<WT, 8, 4>(d, a, p, s);
+    case 808: return launch_decode_t<WT, 8, 8>(d, a, p, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -983,6 +945,11 @@ hipError_t launch_pack(const LayerDesc& d, const void* W, int64_t ldw, hipStream
       return hipGetLastError();
     default: return hipErrorInvalidValue;
   }
+}
+
+hipError_t launch_gather_x(const LayerDesc& d, const void* X, int64_t M, int64_t ldx, void* Xp, hipStream_t s) {
+  gather_x_kernel<<<blocks_for(M * (d.K_p / 8), 256), 256, 0, s>>>(d, (const uint16_t*)X, M, ldx, (uint16_t*)Xp);
+  return hipGetLastError();
 }
 
 hipError_t launch_export(const LayerDesc& d, void* vals, uint32_t* meta, uint8_t* mask, void* dense, hipStream_t s) {

@@ -274,3 +274,40 @@ def test_decode_variants(wdtype, dense, monkeypatch):
         log(f"[decode variants] wdtype={wdtype} dense={dense}: all variants within tolerance")
     finally:
         sdg.spense_free(h)
+
+
+TILE_PRESETS = list(range(8))
+
+
+@pytest.mark.parametrize("wdtype", [DT_FP8, DT_BF16])
+@pytest.mark.parametrize("dense", [("frac", 0.25), ("rand", 192)])
+def test_tile_presets(wdtype, dense, monkeypatch):
+    """Every register-blocked configuration of the streaming kernel (row tiles
+    and m-tiles per wave, ring depth, chunk size), on ragged row counts, batch
+    sizes that end mid m-tile, several split counts, and a chosen dense set
+    (gathered into the workspace first), agrees with the oracle."""
+    N, K = 232, 1536  # 14.5 row tiles: the last row group is partial for every blocking
+    W, s = _small(N, K, wdtype, 31)
+    X = synth.make_x(130, K, DT_BF16, np.random.default_rng(32))
+    sd = to_dev(s, DT_F32) if s is not None else None
+    if dense[0] == "frac":
+        h = pack_dev(to_dev(W, wdtype), wdtype, sd, dense_fraction=dense[1])
+        pi, K_s, _ = oracle.resolve_dense_set(K, dense_fraction=dense[1])
+        D = np.sort(pi[K_s:])
+    else:
+        D = synth.random_dense_set(K, dense[1], 33)
+        h = pack_dev(to_dev(W, wdtype), wdtype, sd, dense_cols=D)
+    try:
+        ref = oracle_pack_rows(W, wdtype, D)
+        Xd = to_dev(X, DT_BF16)
+        for v in TILE_PRESETS:
+            monkeypatch.setenv("SPENSE_TILE", str(v))
+            for M in (17, 40, 64, 130):
+                Yref, B = oracle.linear_ref(X[:M], DT_BF16, ref, s)
+                for sp in (0, 1, 3):
+                    Y = linear_dev(h, Xd[:M], N, splits=sp).cpu().numpy()
+                    r = tol_ratio(Y, Yref, B)
+                    assert r <= 1.0, (v, M, sp, r)
+        log(f"[tile presets] wdtype={wdtype} dense={dense}: all presets within tolerance")
+    finally:
+        sdg.spense_free(h)
