@@ -1,15 +1,26 @@
 """Benchmark of the Spense linear layer on one MI355X.
 
-Workload: 32B-class FFN gate/up projection W[25600, 5120] e4m3 with
-per-channel fp32 scales, dense tail = last 25% of K, X[M, 5120] bf16 for
-M in {1, 4, 16} (decode).  One step = one spense_linear launch per batch size
-(bf16 output), weights already resident in HBM.  Packed weight copies are
-rotated so the working set exceeds the 256 MB Infinity Cache and every launch
-streams its weights from HBM.  The all-dense MFMA baseline (same kernel
-template, dense fraction 1.0) is timed the same way for the speedup.
+Default workload (the headline line): 32B-class FFN gate/up projection
+W[25600, 5120] e4m3 with per-channel fp32 scales, dense tail = last 25% of K,
+X[M, 5120] bf16 for M in {1, 4, 16} (decode).  One step = one spense_linear
+launch per batch size (bf16 output), weights already resident in HBM.  Packed
+weight copies are rotated so the working set exceeds the 256 MB Infinity Cache
+and every launch streams its weights from HBM.  The all-dense baseline (same
+kernels, dense fraction 1.0) is timed the same way for the speedup.
 
-Prints one JSON line.  Extra keys: per-M timings, dense baseline, pack time,
-roofline of the linear kernel, and the CPU oracle baseline.
+Other workloads (``--workload``):
+  down_fp8       FFN down W[5120, 25600] e4m3, 6400 chosen dense columns, M in {1, 8, 32, 64}
+  layer32b_fp8   32B-class decoder linear set (QKV, O, gate+up, down), e4m3, dense
+                 tail fraction in {0, 12.5, 25, 50}%, M = 32; one step = the four
+                 layers of every fraction
+  layer36b_fp8   36B-class decoder linear set, e4m3, 25% chosen dense columns per
+                 layer, M in {128, 2048}
+  layer36b_bf16  the same with bf16 weights
+A layer set streams more than the Infinity Cache per pass, so its packed
+weights are not rotated.
+
+Prints one JSON line.  Extra keys: per-M (and per-layer) timings, dense
+baseline, roofline of the linear kernel, and the CPU oracle baseline.
 """
 
 from __future__ import annotations
@@ -27,12 +38,25 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+# Dense bf16 matrix peak.  The structured-sparse instruction performs half the
+# multiply-adds of a dense one in the same time, so 2.5 PFLOP/s is also its
+# peak on the nonzero multiply-adds that the algorithmic flops count.
+MFMA_PEAK_TFLOPS = 2500.0
 MALL_BYTES = 256 << 20
-WORKLOAD = "gateup_fp8"
 CSRC = os.path.join(ROOT, "sparse_dense_gemm_amd", "csrc")
 # the kernels and the launch planner that picks them decide the HBM traffic
 KERNEL_SRCS = [os.path.join(CSRC, f) for f in ("spense_kernels.hip", "spense_internal.h", "spense_api.cpp")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "spense_linear_gateup_fp8_traffic.json")
+METRIC = "Spense linear us + achieved HBM GB/s at decode M=1..64; speedup vs dense GEMM"
+
+SETS = {
+    "gateup_fp8": ["gateup_fp8"],
+    "down_fp8": ["down_fp8"],
+    "layer32b_fp8": ["layer32b_fp8_d0", "layer32b_fp8_d12p5", "layer32b_fp8_d25", "layer32b_fp8_d50"],
+    "layer36b_fp8": ["layer36b_fp8"],
+    "layer36b_bf16": ["layer36b_bf16"],
+}
+HEADLINE_VARIANT = {"layer32b_fp8": "layer32b_fp8_d25"}
 
 
 def parse():
@@ -40,6 +64,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="gateup_fp8", choices=sorted(SETS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--splits", type=int, default=0, help="force the split-K factor (0 = automatic)")
     ap.add_argument("--ms", type=str, default="", help="override batch sizes, e.g. 1,4,16")
@@ -56,8 +81,8 @@ def kernel_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def load_traffic(per_launch_alg_bytes):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they match this kernel source."""
+def load_traffic():
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they match these sources."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -66,6 +91,55 @@ def load_traffic(per_launch_alg_bytes):
     if t.get("kernel_sha256_16") != kernel_hash():
         return None
     return t.get("hbm_bytes_per_launch")
+
+
+class Layer:
+    """One layer's inputs on the device and its packed handles (Spense and all-dense)."""
+
+    def __init__(self, sdg, torch, dev, spec, Mmax, rotate):
+        import synth
+
+        self.spec = spec
+        W, s, X, D = synth.layer_inputs(spec, Mmax)
+        self.host = (W, s, X, D)
+        bits = W.view(np.int16) if W.dtype == np.uint16 else W
+        Wd = torch.from_numpy(bits).to(dev)
+        self.sd = torch.from_numpy(s).to(dev) if s is not None else None
+        self.Xd = torch.from_numpy(X.view(np.int16)).to(dev).view(torch.bfloat16)
+        self.Y = torch.empty((Mmax, spec.N), dtype=torch.bfloat16, device=dev)
+        wdt = spec.wdtype
+
+        def copies(info):  # enough rotated copies to stream more than twice the Infinity Cache
+            return max(4, -(-2 * MALL_BYTES // info["device_bytes"]) + 1) if rotate else 1
+
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        h0 = sdg.spense_pack(Wd, wdt, scales=self.sd, dense_cols=D)
+        self.pack_ms = (time.perf_counter() - t0) * 1e3
+        info = sdg.spense_info(h0)
+        self.wbytes = info["weight_bytes"]
+        self.handles = [h0] + [sdg.spense_pack(Wd, wdt, scales=self.sd, dense_cols=D)
+                               for _ in range(copies(info) - 1)]
+        hd0 = sdg.spense_pack(Wd, wdt, scales=self.sd, dense_fraction=1.0)
+        dinfo = sdg.spense_info(hd0)
+        self.dbytes = dinfo["weight_bytes"]
+        self.dhandles = [hd0] + [sdg.spense_pack(Wd, wdt, scales=self.sd, dense_fraction=1.0)
+                                 for _ in range(copies(dinfo) - 1)]
+        del Wd
+
+    def flops(self, M):
+        """2 x nonzero multiply-adds: the algorithmic flops of the layer."""
+        K_s = self.spec.K - self.spec.K_d
+        return 2.0 * M * self.spec.N * (K_s / 2 + self.spec.K_d)
+
+    def alg_bytes(self, M):
+        sp = self.spec
+        scale_b = 4 * sp.N if self.sd is not None else 0
+        return self.wbytes + scale_b + 2 * M * sp.K + 2 * M * sp.N  # weights + scales + X + Y(bf16)
+
+    def free(self, sdg):
+        for h in self.handles + self.dhandles:
+            sdg.spense_free(h)
 
 
 def main():
@@ -78,93 +152,83 @@ def main():
     import sparse_dense_gemm_amd as sdg
     import synth
 
-    wl = synth.WORKLOADS[WORKLOAD]
-    spec = wl.layers[0]
-    Ms = tuple(int(m) for m in args.ms.split(",")) if args.ms else wl.Ms
+    variants = SETS[args.workload]
+    wls = [synth.WORKLOADS[v] for v in variants]
+    Ms = tuple(int(m) for m in args.ms.split(",")) if args.ms else wls[0].Ms
     Mmax = max(Ms)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    single = len(wls) == 1 and len(wls[0].layers) == 1
+    hv = variants.index(HEADLINE_VARIANT.get(args.workload, variants[0]))
 
     t0 = time.time()
-    W, s, X, D = synth.layer_inputs(spec, Mmax)
+    sets = [[Layer(sdg, torch, dev, spec, Mmax, rotate=single) for spec in wl.layers] for wl in wls]
     gen_s = time.time() - t0
-    Wd = torch.from_numpy(W).to(dev)
-    sd = torch.from_numpy(s).to(dev)
-    Xd = torch.from_numpy(X.view(np.int16)).to(dev).view(torch.bfloat16)
-    stream = torch.cuda.current_stream()
 
-    # ---- pack: once per weight; timed on its own ----
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    h0 = sdg.spense_pack(Wd, sdg.DT_FP8, scales=sd, dense_cols=D)
-    pack_ms = (time.perf_counter() - t0) * 1e3
-    info = sdg.spense_info(h0)
-    wbytes = info["weight_bytes"]
-    copies = max(4, -(-2 * MALL_BYTES // info["device_bytes"]) + 1)
-    handles = [h0] + [sdg.spense_pack(Wd, sdg.DT_FP8, scales=sd, dense_cols=D) for _ in range(copies - 1)]
-    # all-dense baseline: same kernel template with K_s = 0
-    hd0 = sdg.spense_pack(Wd, sdg.DT_FP8, scales=sd, dense_fraction=1.0)
-    dinfo = sdg.spense_info(hd0)
-    dcopies = max(4, -(-2 * MALL_BYTES // dinfo["device_bytes"]) + 1)
-    dhandles = [hd0] + [sdg.spense_pack(Wd, sdg.DT_FP8, scales=sd, dense_fraction=1.0) for _ in range(dcopies - 1)]
-    del Wd
-    Ys = {M: torch.empty((M, spec.N), dtype=torch.bfloat16, device=dev) for M in Ms}
+    def run_set(layers, M, i, dense):
+        for L in layers:
+            hs = L.dhandles if dense else L.handles
+            sdg.spense_linear_splits(hs[i % len(hs)], L.Xd[:M], L.Y[:M], args.splits, stream=stream)
 
-    def run(hs, M, i):
-        sdg.spense_linear_splits(hs[i % len(hs)], Xd[:M], Ys[M], args.splits, stream=stream)
-
-    # ---- warmup ----
+    # ---- prime: every packed copy once at every batch size (a handle sizes its
+    # split-K and gather workspaces on first use), then the warmup steps ----
+    for M in Ms:
+        for layers in sets:
+            for L in layers:
+                for h in L.handles + L.dhandles:
+                    sdg.spense_linear_splits(h, L.Xd[:M], L.Y[:M], args.splits, stream=stream)
     for i in range(args.warmup):
         for M in Ms:
-            run(handles, M, i)
-            run(dhandles, M, i)
+            for layers in sets:
+                run_set(layers, M, i, False)
+            run_set(sets[hv], M, i, True)
     torch.cuda.synchronize()
 
-    # ---- timed region: K steps of the Spense layer (one launch per batch size) ----
-    ev = {M: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for M in Ms}
+    # ---- timed region: K steps (one launch per layer, batch size and set variant) ----
+    ev = {}
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
-    for M in Ms:
-        ev[M][0].record(stream)
-        for i in range(args.steps):
-            run(handles, M, i)
-        ev[M][1].record(stream)
+    for vi, layers in enumerate(sets):
+        for M in Ms:
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(args.steps):
+                run_set(layers, M, i, False)
+            e1.record(stream)
+            ev[(vi, M)] = (e0, e1)
     torch.cuda.synchronize()
     wall_s = time.perf_counter() - t_wall
-    spense_us = {M: ev[M][0].elapsed_time(ev[M][1]) * 1e3 / args.steps for M in Ms}
+    spense_us = {k: a.elapsed_time(b) * 1e3 / args.steps for k, (a, b) in ev.items()}
 
-    # ---- dense baseline, same protocol (outside the Spense timed region) ----
-    dev_ = {M: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for M in Ms}
+    # ---- dense baseline (the same layers packed with dense fraction 1.0), same protocol ----
+    dev_ = {}
     torch.cuda.synchronize()
     for M in Ms:
-        dev_[M][0].record(stream)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
         for i in range(args.steps):
-            run(dhandles, M, i)
-        dev_[M][1].record(stream)
+            run_set(sets[hv], M, i, True)
+        e1.record(stream)
+        dev_[M] = (e0, e1)
     torch.cuda.synchronize()
-    dense_us = {M: dev_[M][0].elapsed_time(dev_[M][1]) * 1e3 / args.steps for M in Ms}
+    dense_us = {M: a.elapsed_time(b) * 1e3 / args.steps for M, (a, b) in dev_.items()}
 
-    def alg_bytes(wb, M):
-        return wb + 4 * spec.N + 2 * M * spec.K + 2 * M * spec.N  # weights + scales + X + Y(bf16)
+    # ---- per-layer times inside a pass of a layer set (events between the launches) ----
+    per_layer = {}
+    if not single:
+        layers = sets[hv]
+        for M in Ms:
+            evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(layers) + 1)] for _ in range(args.steps)]
+            for i in range(args.steps):
+                for j, L in enumerate(layers):
+                    evs[i][j].record(stream)
+                    sdg.spense_linear_splits(L.handles[0], L.Xd[:M], L.Y[:M], args.splits, stream=stream)
+                evs[i][-1].record(stream)
+            torch.cuda.synchronize()
+            per_layer[str(M)] = {L.spec.name: round(sum(e[j].elapsed_time(e[j + 1]) for e in evs) * 1e3 / args.steps, 3)
+                                 for j, L in enumerate(layers)}
 
-    per_m = {}
-    for M in Ms:
-        per_m[str(M)] = {
-            "spense_us": round(spense_us[M], 3),
-            "dense_us": round(dense_us[M], 3),
-            "speedup_vs_dense": round(dense_us[M] / spense_us[M], 4),
-            "weight_GBs": round(wbytes / spense_us[M] / 1e3, 1),
-            "weight_frac_of_peak": round(wbytes / spense_us[M] / 1e3 / HBM_PEAK_GBS, 4),
-            "dense_weight_GBs": round(dinfo["weight_bytes"] / dense_us[M] / 1e3, 1),
-        }
-    total_us = sum(spense_us.values())
-    value = len(Ms) * wbytes / total_us / 1e3  # GB/s on compressed + dense weight bytes
-    alg = sum(alg_bytes(wbytes, M) for M in Ms)
-    achieved = alg / total_us / 1e3
-    traffic = load_traffic(alg / len(Ms))
-
-    for hh in handles + dhandles:
-        sdg.spense_free(hh)
     if args.copy_calibration:
         src = torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
@@ -174,12 +238,63 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(spec, W, s, X, D, Ms, wbytes)
+    head = sets[hv]
+    wbytes = sum(L.wbytes for L in head)
+    dbytes = sum(L.dbytes for L in head)
+    per_m = {}
+    for M in Ms:
+        t = spense_us[(hv, M)]
+        per_m[str(M)] = {
+            "spense_us": round(t, 3),
+            "dense_us": round(dense_us[M], 3),
+            "speedup_vs_dense": round(dense_us[M] / t, 4),
+            "weight_GBs": round(wbytes / t / 1e3, 1),
+            "weight_frac_of_peak": round(wbytes / t / 1e3 / HBM_PEAK_GBS, 4),
+            "dense_weight_GBs": round(dbytes / dense_us[M] / 1e3, 1),
+            "alg_TFLOPs": round(sum(L.flops(M) for L in head) / t / 1e6, 1),
+        }
+    total_us = sum(spense_us[(hv, M)] for M in Ms)
+    value = len(Ms) * wbytes / total_us / 1e3  # GB/s on compressed + dense weight bytes
+    big = [M for M in Ms if M >= 1024]
+    if big:
+        # prefill batches dominate the step and are bound by the matrix units
+        t_big = sum(spense_us[(hv, M)] for M in big)
+        ach = sum(sum(L.flops(M) for L in head) for M in big) / t_big / 1e6
+        roofline = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(ach / MFMA_PEAK_TFLOPS, 4), "traffic": None, "batch_sizes": big}
+    else:
+        ach = sum(sum(L.alg_bytes(M) for L in head) for M in Ms) / total_us / 1e3
+        traffic = load_traffic() if args.workload == "gateup_fp8" and not args.ms else None
+        roofline = {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic}
 
+    variants_out = {}
+    if len(sets) > 1:
+        for vi, v in enumerate(variants):
+            variants_out[v] = {"dense_fraction": wls[vi].extra.get("fraction"),
+                               "weight_bytes": sum(L.wbytes for L in sets[vi]),
+                               **{f"M{M}_us": round(spense_us[(vi, M)], 3) for M in Ms},
+                               **{f"M{M}_speedup_vs_dense": round(dense_us[M] / spense_us[(vi, M)], 4) for M in Ms}}
+
+    pack_ms = round(sum(L.pack_ms for L in head), 3)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(head, Ms, single)
+    for layers in sets:
+        for L in layers:
+            L.free(sdg)
+
+    if args.workload == "gateup_fp8":
+        wdesc = ("FFN gate/up W[25600,5120] e4m3 + per-channel scales, dense tail 25% (1280 cols), X bf16, "
+                 "M in {" + ",".join(map(str, Ms)) + "}")
+    else:
+        wdesc = wls[hv].title + (f" (batch sizes {list(Ms)})" if args.ms else "")
+    cfg = {"workload": wdesc, "key": args.workload, "Ms": list(Ms), "splits": args.splits or "auto"}
+    if single:
+        cfg.update({"N": head[0].spec.N, "K": head[0].spec.K, "K_d": head[0].spec.K_d,
+                    "weight_copies": len(head[0].handles)})
+    else:
+        cfg["layers"] = [{"name": L.spec.name, "N": L.spec.N, "K": L.spec.K, "K_d": L.spec.K_d} for L in head]
     out = {
-        "metric": "Spense linear us + achieved HBM GB/s at decode M=1..64; speedup vs dense GEMM",
+        "metric": METRIC,
         "value": round(value, 1),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -189,28 +304,31 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "e4m3 weights x bf16 activations, fp32 accumulate",
+        "dtype": ("e4m3" if head[0].spec.wdtype == synth.DT_FP8 else "bf16")
+        + " weights x bf16 activations, fp32 accumulate",
         "data": "synthetic",
-        "config": {"workload": "FFN gate/up W[25600,5120] e4m3 + per-channel scales, dense tail 25% (1280 cols), "
-                               "X bf16, M in {" + ",".join(map(str, Ms)) + "}",
-                   "N": spec.N, "K": spec.K, "K_d": spec.K_d, "Ms": list(Ms), "weight_copies": copies,
-                   "splits": args.splits or "auto"},
+        "config": cfg,
         "per_m": per_m,
         "speedup_vs_dense": round(sum(dense_us.values()) / total_us, 4),
         "spense_weight_bytes": wbytes,
-        "dense_weight_bytes": dinfo["weight_bytes"],
-        "pack_ms_wall": round(pack_ms, 3),
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
+        "dense_weight_bytes": dbytes,
+        "pack_ms_wall": pack_ms,
+        "roofline": roofline,
         "cpu_baseline": cpu,
         "input_gen_s": round(gen_s, 2),
     }
+    if per_layer:
+        out["per_layer_us"] = per_layer
+    if variants_out:
+        out["variants"] = variants_out
     print(json.dumps(out))
 
 
-def cpu_baseline(spec, W, s, X, D, Ms, wbytes):
-    """The oracle, as it stands, on the same layer: one packed form, then the
-    float64 layer output for each batch size.  Throughput on the same weight bytes."""
+def cpu_baseline(layers, Ms, single):
+    """The oracle, as it stands, on the same layer(s): one packed form, then the
+    float64 layer output.  A single layer: whole passes over the batch sizes
+    until about 10 s of CPU work.  A layer set: the first 256 output rows of
+    each layer at the smallest batch size.  Throughput on the weight bytes covered."""
     import oracle
 
     try:
@@ -219,19 +337,34 @@ def cpu_baseline(spec, W, s, X, D, Ms, wbytes):
         cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
         cores = os.cpu_count() or 1
-    pi, K_s, _ = oracle.resolve_dense_set(spec.K, dense_cols=D)
-    p = oracle.pack(W, oracle.DT_FP8, pi, K_s)
-    # repeat whole passes over the batch sizes until about 10 s of CPU work
-    passes = 0
-    t0 = time.perf_counter()
-    while passes < 20 and (passes == 0 or time.perf_counter() - t0 < 10.0):
-        for M in Ms:
-            oracle.linear_ref(X[:M], oracle.DT_BF16, p, s)
-        passes += 1
-    dt = time.perf_counter() - t0
-    return {"value": round(passes * len(Ms) * wbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(cores),
-            "kind": "oracle",
-            "sample": f"full layer, oracle linear_ref for M in {list(Ms)}, {passes} passes ({dt:.1f} s); pack excluded"}
+    if single:
+        L = layers[0]
+        W, s, X, D = L.host
+        pi, K_s, _ = oracle.resolve_dense_set(L.spec.K, dense_cols=D)
+        p = oracle.pack(W, L.spec.wdtype, pi, K_s)
+        # repeat whole passes over the batch sizes until about 10 s of CPU work
+        passes = 0
+        t0 = time.perf_counter()
+        while passes < 20 and (passes == 0 or time.perf_counter() - t0 < 10.0):
+            for M in Ms:
+                oracle.linear_ref(X[:M], oracle.DT_BF16, p, s)
+            passes += 1
+        dt = time.perf_counter() - t0
+        return {"value": round(passes * len(Ms) * L.wbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(cores),
+                "kind": "oracle",
+                "sample": f"full layer, oracle linear_ref for M in {list(Ms)}, {passes} passes ({dt:.1f} s); pack excluded"}
+    rows, M = 256, min(Ms)
+    nbytes, dt = 0.0, 0.0
+    for L in layers:
+        W, s, X, D = L.host
+        pi, K_s, _ = oracle.resolve_dense_set(L.spec.K, dense_cols=D)
+        p = oracle.pack(W[:rows], L.spec.wdtype, pi, K_s)
+        t0 = time.perf_counter()
+        oracle.linear_ref(X[:M], oracle.DT_BF16, p, None if s is None else s[:rows])
+        dt += time.perf_counter() - t0
+        nbytes += L.wbytes * rows / L.spec.N
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"first {rows} output rows of each layer, M={M} ({dt:.1f} s); pack excluded"}
 
 
 if __name__ == "__main__":

@@ -255,7 +255,8 @@ static int plan_linear(const spense_layer* h, int64_t M, int32_t splits, LinearP
     // decode: one 16-row m-tile, weights streamed through a register ring,
     // 8 waves per workgroup, 4 units in flight per wave.  One split when the
     // row tiles alone give enough waves (each split adds a partial-sum
-    // handshake at the end of the kernel), else about 1280 waves.  The split's
+    // handshake at the end of the kernel), else about 1920 waves (down layer
+    // 5120 x 25600: 6 splits; 4 splits measured 4-15% slower).  The split's
     // activations are staged in LDS at once when they fit in 64 KB (no
     // barrier in the K loop), else in double-buffered chunks.
     p.waves = 8;
@@ -269,7 +270,7 @@ static int plan_linear(const spense_layer* h, int64_t M, int32_t splits, LinearP
     }
     int64_t S = splits;
     if (S == 0) {
-      S = d.NT >= 1024 ? 1 : std::max<int64_t>(1, (1280 + d.NT - 1) / d.NT);
+      S = d.NT >= 1024 ? 1 : std::max<int64_t>(1, (1920 + d.NT - 1) / d.NT);
       S = std::min<int64_t>(S, max_splits);
       if (ch == 0)  // single-shot staging requested: split until it fits
         while (S < max_splits && decode_lds_bytes(d, M, S) > 64 * 1024) ++S;
@@ -296,12 +297,13 @@ static int plan_linear(const spense_layer* h, int64_t M, int32_t splits, LinearP
   };
   constexpr int kNumPresets = (int)(sizeof(kPresets) / sizeof(kPresets[0]));
   // Two m-tiles per wave up to 128 rows (four need more LDS per workgroup
-  // than they save there), four beyond.  Two row tiles per wave halve the LDS
-  // reads per product but give fewer workgroups: used when the row tiles
-  // alone still give at least one workgroup per two CUs; otherwise one row
-  // tile per wave plus splits.
+  // than they save there); beyond, four m-tiles and four row tiles per wave
+  // (each staged activation fragment feeds four products).  Two row tiles
+  // per wave halve the LDS reads per product but give fewer workgroups: used
+  // when the row tiles alone still give at least one workgroup per two CUs;
+  // otherwise one row tile per wave plus splits.
   const int64_t wg_nr2 = (d.NT + 15) / 16 * ((M + 31) / 32);
-  int pre = M <= 32 || wg_nr2 < kCUs / 2 ? 0 : M <= 64 ? 1 : M <= 128 ? 2 : 6;
+  int pre = M <= 32 || wg_nr2 < kCUs / 2 ? 0 : M <= 64 ? 1 : M <= 128 ? 2 : 8;
   if (const char* t = std::getenv("SPENSE_TILE")) {
     const int v = std::atoi(t);
     if (v >= 0 && v < kNumPresets) pre = v;
@@ -326,6 +328,9 @@ static int plan_linear(const spense_layer* h, int64_t M, int32_t splits, LinearP
     S = units >= kCUs / 2 ? 1 : std::max<int64_t>(1, std::min<int64_t>(resident / units, max_splits));
   }
   p.splits = (int)S;
+  const int64_t grid = (int64_t)p.rgroups * p.mgroups * S;
+  p.xcd_remap = (p.mgroups > 1 && grid % 8 == 0) ? 1 : 0;
+  if (const char* x = std::getenv("SPENSE_XCD")) p.xcd_remap = (std::atoi(x) != 0 && grid % 8 == 0) ? 1 : 0;
   return SPENSE_OK;
 }
 

@@ -92,6 +92,7 @@ struct LinearPlan {
   int chunk;     // units per staged chunk of linear_stream_kernel
   int nr;        // row tiles per wave (linear_stream_kernel)
   int preset;    // index into SPENSE_TILE_PRESETS, or -1 (one row tile and m-tile per wave)
+  int xcd_remap; // 1: logical workgroup id = XCD-major remap of blockIdx (grid a multiple of 8)
 };
 
 // Blocked configurations of linear_stream_kernel for batches above 16 rows:
@@ -104,7 +105,12 @@ struct LinearPlan {
   X(4, 4, 2, 4, 4, 4)          \
   X(5, 4, 2, 2, 2, 4)          \
   X(6, 8, 2, 2, 2, 4)          \
-  X(7, 4, 1, 4, 8, 2)
+  X(7, 4, 1, 4, 8, 2)          \
+  X(8, 4, 4, 2, 2, 4)          \
+  X(9, 8, 4, 2, 2, 4)          \
+  X(10, 4, 4, 2, 2, 2)         \
+  X(11, 4, 4, 4, 4, 2)         \
+  X(12, 8, 2, 4, 4, 4)
 
 constexpr int kStreamChunk = 8;  // units per activation chunk of linear_stream_kernel
 

@@ -144,18 +144,23 @@ __device__ __forceinline__ void store_y(const LinearArgs& a, int64_t m, int64_t 
 // Writes Y (S == 1) or this split's partial; with S > 1 the last workgroup of
 // the tile adds the partials in split order.  acc: lane l, register r =
 // Y^T[n = 16rt + 4(l/16) + r][m = m0 + 16mt + l%16].
-// Epilogue of a wave's nr row tiles (rt0 ..) x mtiles m-tiles; acc[r * mtiles + t],
-// sc[r] = row_scales of row tile rt0 + r.
+// Epilogue of a wave's NR row tiles (rt0 ..) x MT m-tiles; acc[r * MT + t],
+// sc[r] = row_scales of row tile rt0 + r.  Compile-time counts keep every
+// accumulator index static (a dynamic index would move them to scratch).
+template <int NR, int MT>
 __device__ __forceinline__ void finish_tile(const LayerDesc& d, const LinearArgs& a, const f32x4* acc,
-                                            const f32x4* sc, int nr, int mtiles, int64_t rt0, int64_t m0, int s,
-                                            int S, int64_t cnt_index, int* last_flag) {
+                                            const f32x4* sc, int64_t rt0, int64_t m0, int s, int S,
+                                            int64_t cnt_index, int* last_flag) {
   const int lane = threadIdx.x & 63;
   const int nb = 4 * (lane >> 4);
   const int64_t NP = d.NT * 16;
+  constexpr int nr = NR, mtiles = MT;
   if (S > 1) {
+#pragma unroll
     for (int r = 0; r < nr; ++r) {
       const int64_t rt = rt0 + r;
       if (rt >= d.NT) break;
+#pragma unroll
       for (int mt = 0; mt < mtiles; ++mt) {
         const int64_t m = m0 + 16 * mt + (lane & 15);
         if (m < a.M) store_partial(a.ws + ((int64_t)s * a.M + m) * NP + rt * 16 + nb, acc[r * mtiles + mt]);
@@ -163,9 +168,11 @@ __device__ __forceinline__ void finish_tile(const LayerDesc& d, const LinearArgs
     }
     if (!arrive_last(a.counters + cnt_index, S, last_flag)) return;
   }
+#pragma unroll
   for (int r = 0; r < nr; ++r) {
     const int64_t rt = rt0 + r;
     if (rt >= d.NT) break;
+#pragma unroll
     for (int mt = 0; mt < mtiles; ++mt) {
       const int64_t m = m0 + 16 * mt + (lane & 15);
       if (m >= a.M) continue;
@@ -624,7 +631,7 @@ __global__ __launch_bounds__(NW * 64) void linear_decode_kernel(LayerDesc d, Lin
       if (k0 + i < total) consume(i, k0 + i);
   }
   const f32x4 acc = acc0 + acc1;
-  finish_tile(d, a, &acc, &sc, 1, 1, rt, 0, s, S, rg, &last_flag);
+  finish_tile<1, 1>(d, a, &acc, &sc, rt, 0, s, S, rg, &last_flag);
 }
 
 // ---------------------------------------------------------------------------
@@ -648,10 +655,16 @@ __global__ __launch_bounds__(NW * 64) void linear_stream_kernel(LayerDesc d, Lin
   constexpr bool kSplitAcc = NR == 1 && MT == 1;  // two accumulators when there is nothing to interleave
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int rg = blockIdx.x % p.rgroups;
+  // Workgroups are dealt to the 8 XCDs round-robin.  With several m-groups the
+  // order is remapped so that each XCD takes a contiguous run of logical ids,
+  // m-group fastest: the m-groups that share a weight slice run on one XCD at
+  // about the same time, and all but the first read it from that XCD's L2.
+  int b = blockIdx.x;
+  if (p.xcd_remap) b = (b % 8) * (gridDim.x / 8) + b / 8;
   const int S = p.splits;
-  const int s = (blockIdx.x / p.rgroups) % S;
-  const int mg = blockIdx.x / (p.rgroups * S);
+  const int mg = b % p.mgroups;
+  const int rg = (b / p.mgroups) % p.rgroups;
+  const int s = b / (p.mgroups * p.rgroups);
   const int64_t rt0 = ((int64_t)rg * NW + wave) * NR;
   const int64_t ms0 = d.n_sm * s / S, ms1 = d.n_sm * (s + 1) / S;
   const int64_t md0 = d.n_dm * s / S, md1 = d.n_dm * (s + 1) / S;
@@ -796,7 +809,7 @@ __global__ __launch_bounds__(NW * 64) void linear_stream_kernel(LayerDesc d, Lin
     }
   }
   if constexpr (kSplitAcc) acc[0] += acc1;
-  finish_tile(d, a, acc, sc, NR, MT, rt0, m0, s, S, (int64_t)mg * p.rgroups + rg, &last_flag);
+  finish_tile<NR, MT>(d, a, acc, sc, rt0, m0, s, S, (int64_t)mg * p.rgroups + rg, &last_flag);
 }
 
 // X'p[m][j] = X[m][pip[j]] (0 where pip[j] < 0), as a contiguous [M][K_p]
