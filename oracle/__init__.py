@@ -18,6 +18,10 @@ written from the definitions on the pages:
   * same page, Technical Summary 2.B "Dense Index Selection Strategies":
     SpenseGPT keeps the last p% of indices dense; SpenseGPT+ keeps a selected
     index set dense and permutes it into the contiguous dense block.
+  * same page, Technical Summary 2.A: the output-split variant splits the
+    output rows instead (dense rows, and rows that are 2:4 along K), with no
+    accumulation across the parts; the page uses it for the GLU gate and up
+    projections (``resolve_dense_rows``, ``pack_rows``, ``linear_rows_ref``).
   * same page, Technical Summary 1 "Problem Statement" (and the SlideSparse
     explainer's Technical summary 1): 2:4 means at most two nonzeros in every
     four consecutive weights.
@@ -33,12 +37,17 @@ from .spense import (  # noqa: F401
     DT_FP8,
     DenseSetError,
     Packed,
+    PackedRows,
     decode_values,
     decompress,
     dense_linear_ref,
     linear_ref,
+    linear_rows_ref,
     magnitude_key,
     pack,
+    pack_rows,
+    resolve_dense_rows,
     resolve_dense_set,
     unpack_bits,
+    unpack_rows_bits,
 )

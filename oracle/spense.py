@@ -251,3 +251,100 @@ def dense_linear_ref(X_bits: np.ndarray, xdtype: int, W_bits: np.ndarray, wdtype
         Y = Y * s[None, :]
         B = B * s[None, :]
     return Y, B
+
+
+# ---------------------------------------------------------------------------
+# Output-split form (Technical Summary 2.A "The Spense Format": the output is
+# split, one part from the sparse GEMM and the other from the dense GEMM; the
+# page uses it for the GLU gate and up projections).  The split runs over the
+# output rows: a set of dense rows keeps all its weights, every other row is
+# 2:4 along K in groups of four consecutive columns.  The two parts write
+# different outputs, so nothing is accumulated across them.  As for columns,
+# a chosen row set is moved into one contiguous block (Technical Summary 2.B:
+# permuting intermediate indices leaves the block's output unchanged, up to
+# the same permutation of the output columns).
+# ---------------------------------------------------------------------------
+def resolve_dense_rows(N: int, K: int, dense_rows=None, dense_fraction: Optional[float] = None):
+    """Return (rho, N_s, N_d): rho lists the sparse rows ascending, then the dense rows ascending.
+
+    A fraction p selects the last N_d = round-half-away(p*N) rows (the reading
+    used for dense columns).  Sparse rows need K to hold whole groups of four.
+    """
+    if N <= 0 or K <= 0:
+        raise DenseSetError("N and K must be positive")
+    if dense_rows is not None:
+        D = np.asarray(dense_rows, dtype=np.int64).ravel()
+        if D.size and (D.min() < 0 or D.max() >= N):
+            raise DenseSetError("dense row out of range")
+        if np.unique(D).size != D.size:
+            raise DenseSetError("duplicate dense row")
+        D = np.sort(D)
+    else:
+        if dense_fraction is None:
+            raise DenseSetError("need dense_rows or dense_fraction")
+        p = float(dense_fraction)
+        if not (0.0 <= p <= 1.0):
+            raise DenseSetError("dense_fraction outside [0, 1]")
+        N_d = int(math.floor(p * N + 0.5))
+        D = np.arange(N - N_d, N, dtype=np.int64)
+    N_d = int(D.size)
+    N_s = N - N_d
+    if N_s > 0 and K % 4 != 0:
+        raise DenseSetError("K must be a multiple of 4 when any row is sparse")
+    is_dense = np.zeros(N, dtype=bool)
+    is_dense[D] = True
+    rho = np.concatenate([np.nonzero(~is_dense)[0], D]).astype(np.int64)
+    return rho, N_s, N_d
+
+
+@dataclass
+class PackedRows:
+    """Canonical output-split form.
+
+    sparse  Packed of the sparse rows rho[:N_s] (all K columns 2:4, natural column order)
+    dense   [N_d, K] bit copies of W[rho[N_s:], :]
+    rho     [N] row order
+    """
+
+    sparse: Packed
+    dense: np.ndarray
+    rho: np.ndarray
+    N_s: int
+    N_d: int
+    dtype: int
+
+
+def pack_rows(W: np.ndarray, dtype: int, rho: np.ndarray, N_s: int) -> PackedRows:
+    """2:4 selection on the sparse rows (groups of four consecutive columns), dense rows copied."""
+    W = np.asarray(W)
+    N, K = W.shape
+    rho = np.asarray(rho, dtype=np.int64)
+    Ks = K if N_s > 0 else 0
+    sp = pack(W[rho[:N_s]], dtype, np.arange(K, dtype=np.int64), Ks)
+    dense = np.ascontiguousarray(W[rho[N_s:]])
+    return PackedRows(sparse=sp, dense=dense, rho=rho, N_s=N_s, N_d=N - N_s, dtype=dtype)
+
+
+def unpack_rows_bits(p: PackedRows) -> np.ndarray:
+    """Rebuild W with pruned positions (+0) in the natural row and column order."""
+    N = p.rho.size
+    K = p.dense.shape[1] if p.N_d else p.sparse.pi.size
+    out = np.zeros((N, K), dtype=_storage_dtype(p.dtype))
+    if p.N_s:
+        out[p.rho[: p.N_s]] = unpack_bits(p.sparse)
+    if p.N_d:
+        out[p.rho[p.N_s:]] = p.dense
+    return out
+
+
+def linear_rows_ref(X_bits: np.ndarray, xdtype: int, p: PackedRows, scales=None):
+    """Exact output-split layer output in float64 and its error scale (same definition as linear_ref)."""
+    Wp = decode_values(unpack_rows_bits(p), p.dtype)
+    X = decode_values(X_bits, xdtype)
+    Y = X @ Wp.T
+    B = np.abs(X) @ np.abs(Wp).T
+    if scales is not None:
+        s = np.asarray(scales, dtype=np.float32).astype(np.float64)
+        Y = Y * s[None, :]
+        B = B * s[None, :]
+    return Y, B

@@ -355,3 +355,137 @@ def test_scale_is_per_output_channel():
     assert np.array_equal(Y, Y1 * s.astype(np.float64)[None, :])
     # the scale is max|w|/448 of the unpruned row: every row holds a +-448 code
     assert np.all(np.max(oracle.magnitude_key(W, DT_FP8), axis=1) == 0x7E)
+
+
+# --------------------------------------------------------------------------
+# output-split form (dense rows | 2:4 rows)
+# --------------------------------------------------------------------------
+def test_dense_rows_resolution():
+    rho, N_s, N_d = oracle.resolve_dense_rows(10, 8, dense_fraction=0.25)
+    assert (N_s, N_d) == (7, 3) and rho.tolist() == list(range(10))  # round(2.5) = 3, half away from zero
+    rho, N_s, N_d = oracle.resolve_dense_rows(6, 8, dense_rows=[4, 1])
+    assert (N_s, N_d) == (4, 2) and rho.tolist() == [0, 2, 3, 5, 1, 4]
+    rho, N_s, N_d = oracle.resolve_dense_rows(3, 6, dense_fraction=1.0)  # no sparse row: K need not be a multiple of 4
+    assert (N_s, N_d) == (0, 3)
+    for bad in ([6], [-1], [2, 2]):
+        with pytest.raises(oracle.DenseSetError):
+            oracle.resolve_dense_rows(6, 8, dense_rows=bad)
+    with pytest.raises(oracle.DenseSetError):
+        oracle.resolve_dense_rows(6, 6, dense_rows=[0])
+
+
+@pytest.mark.parametrize("dtype", [DT_F32, DT_BF16, DT_FP8])
+def test_rows_fraction_one_is_dense_gemm(dtype):
+    rng = np.random.default_rng(41)
+    N, K, M = 24, 64, 3
+    W, s = synth.make_weight(N, K, dtype, rng)
+    xdt = DT_F32 if dtype == DT_F32 else DT_BF16
+    X = synth.make_x(M, K, xdt, rng)
+    rho, N_s, _ = oracle.resolve_dense_rows(N, K, dense_fraction=1.0)
+    Y, B = oracle.linear_rows_ref(X, xdt, oracle.pack_rows(W, dtype, rho, N_s), s)
+    Wt = torch.from_numpy(oracle.decode_values(W, dtype))
+    if s is not None:
+        Wt = Wt * torch.from_numpy(s.astype(np.float64))[:, None]
+    ref = torch.nn.functional.linear(torch.from_numpy(oracle.decode_values(X, xdt)), Wt).numpy()
+    assert np.all(np.abs(Y - ref) <= 1e-12 * B + 1e-300)
+
+
+@pytest.mark.parametrize("dtype", [DT_F32, DT_FP8])
+def test_rows_fraction_zero_is_pure_two_four(dtype):
+    rng = np.random.default_rng(42)
+    N, K, M = 12, 32, 2
+    W, s = synth.make_weight(N, K, dtype, rng)
+    xdt = DT_F32 if dtype == DT_F32 else DT_BF16
+    X = synth.make_x(M, K, xdt, rng)
+    rho, N_s, _ = oracle.resolve_dense_rows(N, K, dense_fraction=0.0)
+    Y, B = oracle.linear_rows_ref(X, xdt, oracle.pack_rows(W, dtype, rho, N_s), s)
+    keys = oracle.magnitude_key(W, dtype)
+    Wp = torch.tensor(prune_python(oracle.decode_values(W, dtype).tolist(), keys.tolist(), np.arange(K), K),
+                      dtype=torch.float64)
+    if s is not None:
+        Wp = Wp * torch.from_numpy(s.astype(np.float64))[:, None]
+    ref = torch.nn.functional.linear(torch.from_numpy(oracle.decode_values(X, xdt)), Wp).numpy()
+    assert np.all(np.abs(Y - ref) <= 1e-12 * B + 1e-300)
+
+
+def test_rows_split_column_by_column():
+    """Each output column is either the dense product of its row or the
+    input-split layer with no dense columns (pinned above) on that row."""
+    rng = np.random.default_rng(43)
+    N, K, M = 40, 96, 3
+    W, s = synth.make_weight(N, K, DT_FP8, rng)
+    X = synth.make_x(M, K, DT_BF16, rng)
+    D = synth.random_dense_set(N, 9, 44)
+    rho, N_s, _ = oracle.resolve_dense_rows(N, K, dense_rows=D)
+    Y, _ = oracle.linear_rows_ref(X, DT_BF16, oracle.pack_rows(W, DT_FP8, rho, N_s), s)
+    Yd, _ = oracle.dense_linear_ref(X, DT_BF16, W, DT_FP8, s)
+    pi, K_s, _ = oracle.resolve_dense_set(K, dense_fraction=0.0)
+    Ys, _ = oracle.linear_ref(X, DT_BF16, oracle.pack(W, DT_FP8, pi, K_s), s)
+    dense = np.zeros(N, dtype=bool)
+    dense[D] = True
+    assert np.array_equal(Y[:, dense], Yd[:, dense])
+    assert np.array_equal(Y[:, ~dense], Ys[:, ~dense])
+
+
+def test_rows_brute_force_every_dense_row_set_6x8():
+    rng = np.random.default_rng(45)
+    N, K, M = 6, 8, 2
+    W = rng.integers(-5, 6, size=(N, K)).astype(np.float32)
+    X = rng.integers(-4, 5, size=(M, K)).astype(np.float32)
+    keys = oracle.magnitude_key(W, DT_F32).tolist()
+    Xl = X.astype(np.float64).tolist()
+    count = 0
+    for nd in range(N + 1):
+        for D in itertools.combinations(range(N), nd):
+            rho, N_s, _ = oracle.resolve_dense_rows(N, K, dense_rows=list(D))
+            p = oracle.pack_rows(W, DT_F32, rho, N_s)
+            Y, _ = oracle.linear_rows_ref(X, DT_F32, p)
+            for n in range(N):
+                row = [float(v) for v in W[n]]
+                if n not in D:
+                    for g in range(K // 4):
+                        P = dominance_pair([keys[n][4 * g + t] for t in range(4)])
+                        for t in range(4):
+                            if t not in P:
+                                row[4 * g + t] = 0.0
+                for m in range(M):
+                    acc = 0.0
+                    for k in range(K):
+                        acc += Xl[m][k] * row[k]
+                    assert Y[m, n] == acc
+            count += 1
+    assert count == 2 ** N
+
+
+def test_rows_permutation_moves_outputs_only():
+    """Moving a chosen row set into a contiguous tail (rows permuted) permutes
+    the output columns the same way and changes nothing else."""
+    rng = np.random.default_rng(46)
+    N, K, M = 48, 64, 3
+    W = rng.integers(-8, 9, size=(N, K)).astype(np.float32)
+    X = rng.integers(-4, 5, size=(M, K)).astype(np.float32)
+    D = synth.random_dense_set(N, 12, 47)
+    rho, N_s, N_d = oracle.resolve_dense_rows(N, K, dense_rows=D)
+    Y1, _ = oracle.linear_rows_ref(X, DT_F32, oracle.pack_rows(W, DT_F32, rho, N_s))
+    rho2, N_s2, _ = oracle.resolve_dense_rows(N, K, dense_fraction=N_d / N)
+    Y2, _ = oracle.linear_rows_ref(X, DT_F32, oracle.pack_rows(W[rho], DT_F32, rho2, N_s2))
+    assert np.array_equal(Y1[:, rho], Y2)
+
+
+def test_rows_pack_round_trip():
+    rng = np.random.default_rng(48)
+    N, K = 20, 64
+    W, _ = synth.make_weight(N, K, DT_BF16, rng)
+    D = synth.random_dense_set(N, 5, 49)
+    rho, N_s, _ = oracle.resolve_dense_rows(N, K, dense_rows=D)
+    p = oracle.pack_rows(W, DT_BF16, rho, N_s)
+    U = oracle.unpack_rows_bits(p)
+    assert np.array_equal(U[D], W[D])
+    sp = np.setdiff1d(np.arange(N), D)
+    kept = (U[sp] != 0) | (W[sp] == 0)
+    assert np.all(kept.reshape(len(sp), K // 4, 4).sum(axis=2) >= 2)
+    nz = (U[sp] != 0).reshape(len(sp), K // 4, 4).sum(axis=2)
+    assert np.all(nz <= 2)
+    assert np.array_equal(U[sp][U[sp] != 0], W[sp][U[sp] != 0])
+    p2 = oracle.pack_rows(U, DT_BF16, rho, N_s)
+    assert np.array_equal(p2.sparse.vals, p.sparse.vals) and np.array_equal(p2.sparse.meta, p.sparse.meta)
