@@ -9,6 +9,8 @@ and every launch streams its weights from HBM.  The all-dense baseline (same
 kernels, dense fraction 1.0) is timed the same way for the speedup.
 
 Other workloads (``--workload``):
+  gateup_fp8_rows  the gate/up layer in output-split form: the last 25% of the rows
+                 dense, the others 2:4 along K, M in {1, 4, 16}
   down_fp8       FFN down W[5120, 25600] e4m3, 6400 chosen dense columns, M in {1, 8, 32, 64}
   layer32b_fp8   32B-class decoder linear set (QKV, O, gate+up, down), e4m3, dense
                  tail fraction in {0, 12.5, 25, 50}%, M = 32; one step = the four
@@ -51,6 +53,7 @@ METRIC = "Spense linear us + achieved HBM GB/s at decode M=1..64; speedup vs den
 
 SETS = {
     "gateup_fp8": ["gateup_fp8"],
+    "gateup_fp8_rows": ["gateup_fp8_rows"],
     "down_fp8": ["down_fp8"],
     "layer32b_fp8": ["layer32b_fp8_d0", "layer32b_fp8_d12p5", "layer32b_fp8_d25", "layer32b_fp8_d50"],
     "layer36b_fp8": ["layer36b_fp8"],
@@ -112,14 +115,22 @@ class Layer:
         def copies(info):  # enough rotated copies to stream more than twice the Infinity Cache
             return max(4, -(-2 * MALL_BYTES // info["device_bytes"]) + 1) if rotate else 1
 
+        if spec.form == "output":  # dense rows (the last N_d), 2:4 rows along K
+            rows = np.arange(spec.N - spec.N_d, spec.N, dtype=np.int32)
+
+            def pack():
+                return sdg.spense_pack_rows(Wd, wdt, scales=self.sd, dense_rows=rows)
+        else:
+            def pack():
+                return sdg.spense_pack(Wd, wdt, scales=self.sd, dense_cols=D)
+
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        h0 = sdg.spense_pack(Wd, wdt, scales=self.sd, dense_cols=D)
+        h0 = pack()
         self.pack_ms = (time.perf_counter() - t0) * 1e3
         info = sdg.spense_info(h0)
         self.wbytes = info["weight_bytes"]
-        self.handles = [h0] + [sdg.spense_pack(Wd, wdt, scales=self.sd, dense_cols=D)
-                               for _ in range(copies(info) - 1)]
+        self.handles = [h0] + [pack() for _ in range(copies(info) - 1)]
         hd0 = sdg.spense_pack(Wd, wdt, scales=self.sd, dense_fraction=1.0)
         dinfo = sdg.spense_info(hd0)
         self.dbytes = dinfo["weight_bytes"]
@@ -129,8 +140,11 @@ class Layer:
 
     def flops(self, M):
         """2 x nonzero multiply-adds: the algorithmic flops of the layer."""
-        K_s = self.spec.K - self.spec.K_d
-        return 2.0 * M * self.spec.N * (K_s / 2 + self.spec.K_d)
+        sp = self.spec
+        if sp.form == "output":
+            return 2.0 * M * sp.K * ((sp.N - sp.N_d) / 2 + sp.N_d)
+        K_s = sp.K - sp.K_d
+        return 2.0 * M * sp.N * (K_s / 2 + sp.K_d)
 
     def alg_bytes(self, M):
         sp = self.spec
@@ -340,14 +354,20 @@ def cpu_baseline(layers, Ms, single):
     if single:
         L = layers[0]
         W, s, X, D = L.host
-        pi, K_s, _ = oracle.resolve_dense_set(L.spec.K, dense_cols=D)
-        p = oracle.pack(W, L.spec.wdtype, pi, K_s)
+        if L.spec.form == "output":
+            rho, N_s, _ = oracle.resolve_dense_rows(L.spec.N, L.spec.K, dense_fraction=L.spec.N_d / L.spec.N)
+            p = oracle.pack_rows(W, L.spec.wdtype, rho, N_s)
+            run = oracle.linear_rows_ref
+        else:
+            pi, K_s, _ = oracle.resolve_dense_set(L.spec.K, dense_cols=D)
+            p = oracle.pack(W, L.spec.wdtype, pi, K_s)
+            run = oracle.linear_ref
         # repeat whole passes over the batch sizes until about 10 s of CPU work
         passes = 0
         t0 = time.perf_counter()
         while passes < 20 and (passes == 0 or time.perf_counter() - t0 < 10.0):
             for M in Ms:
-                oracle.linear_ref(X[:M], oracle.DT_BF16, p, s)
+                run(X[:M], oracle.DT_BF16, p, s)
             passes += 1
         dt = time.perf_counter() - t0
         return {"value": round(passes * len(Ms) * L.wbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(cores),

@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define SPENSE_ABI_VERSION 1
+#define SPENSE_ABI_VERSION 2
 
 /* Element types.  The numbering is fixed. */
 typedef enum spense_dtype {
@@ -70,6 +70,9 @@ typedef struct spense_layer_info {
   int64_t weight_bytes;   /* bytes the method must stream per call: kept values + 2-bit indices
                              + dense block = N*(K_s/2*b + K_s/8 + K_d*b), b = element bytes */
   int64_t device_bytes;   /* bytes of the device-resident packed form, padding included */
+  int32_t split;          /* 0: input-split layer (spense_pack); 1: output-split (spense_pack_rows) */
+  int64_t N_s, N_d;       /* output-split: 2:4 rows / dense rows (input-split: N and 0); for an
+                             output-split layer K_s = K when N_s > 0 and K_d = K when N_d > 0 */
 } spense_layer_info;
 
 /*
@@ -103,6 +106,30 @@ typedef struct spense_layer_info {
 int spense_pack(const void* W, int32_t wdtype, int64_t N, int64_t K, int64_t ldw, const float* scales,
                 const int32_t* dense_cols, int64_t n_dense, double dense_fraction, void* stream,
                 spense_handle* out);
+
+/*
+ * spense_pack_rows - build an output-split layer (once per weight).
+ *
+ * Output-split form (Technical Summary 2.A of the SpenseGPT explainer; the
+ * page uses it for the GLU gate and up projections): the output rows are
+ * split instead of the input columns.  Rows in the dense row set keep all
+ * their weights; every other row is 2:4 along K, in groups of four
+ * consecutive columns (natural column order), with the same magnitude rule
+ * and tie-break as spense_pack.  The two row classes produce different output
+ * columns, so nothing is accumulated across them.  The dense row set is
+ * `dense_rows` (any rows, order irrelevant) or, when dense_rows is NULL, the
+ * last N_d = round(dense_fraction*N) rows.  Arguments as for spense_pack,
+ * with dense_rows / n_dense naming rows in [0, N).
+ *
+ * wdtype must be SPENSE_BF16 or SPENSE_FP8_E4M3 (SPENSE_EUNSUPPORTED for
+ * SPENSE_F32).  K must be a multiple of 4 when any row is sparse
+ * (SPENSE_EINVAL otherwise).  spense_linear, spense_linear_splits, spense_info
+ * and spense_free accept the handle; both row classes run in one launch.
+ * Synchronises `stream` before returning.
+ */
+int spense_pack_rows(const void* W, int32_t wdtype, int64_t N, int64_t K, int64_t ldw, const float* scales,
+                     const int32_t* dense_rows, int64_t n_dense, double dense_fraction, void* stream,
+                     spense_handle* out);
 
 /*
  * spense_linear - Y = X . W_pruned^T (times the per-channel scales), the layer forward.
@@ -157,6 +184,21 @@ int spense_info(spense_handle h, spense_layer_info* info);
  */
 int spense_export(spense_handle h, void* vals, uint32_t* meta, uint8_t* mask, void* dense, int32_t* pi,
                   void* stream);
+
+/*
+ * spense_export_rows - canonical form of an output-split layer (for bit-exact checks).
+ *
+ *   vals   device pointer, [N_s, K/2]: kept values of the 2:4 rows, in rho order.
+ *   meta   device pointer, [N_s, ceil(K/32)] uint32, encoded as for spense_export.
+ *   mask   device pointer, [N_s, K] uint8, 1 on kept positions.
+ *   dense  device pointer, [N_d, K]: the dense rows, in rho order.
+ *   rho    host pointer, [N] int32 row order: the 2:4 rows ascending, then the dense rows ascending.
+ * Any pointer may be NULL to skip that part.  SPENSE_EINVAL for an input-split
+ * handle (and spense_export returns SPENSE_EINVAL for an output-split one).
+ * Synchronises `stream` before returning.
+ */
+int spense_export_rows(spense_handle h, void* vals, uint32_t* meta, uint8_t* mask, void* dense, int32_t* rho,
+                       void* stream);
 
 /* spense_free - release the handle and its device buffers (no launch may still use it). */
 int spense_free(spense_handle h);

@@ -46,6 +46,7 @@ class LayerInfo(ctypes.Structure):
         ("N", ctypes.c_int64), ("K", ctypes.c_int64), ("K_s", ctypes.c_int64), ("K_d", ctypes.c_int64),
         ("wdtype", ctypes.c_int32), ("gather", ctypes.c_int32),
         ("weight_bytes", ctypes.c_int64), ("device_bytes", ctypes.c_int64),
+        ("split", ctypes.c_int32), ("N_s", ctypes.c_int64), ("N_d", ctypes.c_int64),
     ]
 
 
@@ -59,6 +60,10 @@ def _lib():
     vp, i32, i64, f64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_double
     lib.spense_pack.argtypes = [vp, i32, i64, i64, i64, vp, vp, i64, f64, vp, ctypes.POINTER(vp)]
     lib.spense_pack.restype = ctypes.c_int
+    lib.spense_pack_rows.argtypes = [vp, i32, i64, i64, i64, vp, vp, i64, f64, vp, ctypes.POINTER(vp)]
+    lib.spense_pack_rows.restype = ctypes.c_int
+    lib.spense_export_rows.argtypes = [vp, vp, vp, vp, vp, vp, vp]
+    lib.spense_export_rows.restype = ctypes.c_int
     lib.spense_linear.argtypes = [vp, vp, i32, i64, i64, vp, i32, i64, vp]
     lib.spense_linear.restype = ctypes.c_int
     lib.spense_linear_splits.argtypes = [vp, vp, i32, i64, i64, vp, i32, i64, i32, vp]
@@ -138,6 +143,42 @@ def spense_pack(W, wdtype: Optional[int] = None, *, scales=None, dense_cols=None
                             _stream(stream), ctypes.byref(h))
     _check(st, "spense_pack")
     return h.value
+
+
+def spense_pack_rows(W, wdtype: Optional[int] = None, *, scales=None, dense_rows=None, dense_fraction: float = 0.0,
+                     N: Optional[int] = None, K: Optional[int] = None, ldw: Optional[int] = None,
+                     stream=None) -> int:
+    """Pack an output-split layer (dense rows | 2:4 rows); returns the opaque handle (an int)."""
+    if wdtype is None:
+        wdtype = dtype_of(W)
+    if N is None:
+        N = W.shape[0]
+    if K is None:
+        K = W.shape[1]
+    if ldw is None:
+        ldw = W.stride(0) if hasattr(W, "stride") else K
+    rows_ptr = None
+    n_dense = 0
+    if dense_rows is not None:
+        rows = np.ascontiguousarray(np.asarray(dense_rows, dtype=np.int32).ravel())
+        n_dense = rows.size
+        buf = rows if n_dense else np.zeros(1, dtype=np.int32)
+        rows_ptr = buf.ctypes.data
+    h = ctypes.c_void_p()
+    st = _lib().spense_pack_rows(_ptr(W), wdtype, N, K, ldw, _ptr(scales), rows_ptr, n_dense, float(dense_fraction),
+                                 _stream(stream), ctypes.byref(h))
+    _check(st, "spense_pack_rows")
+    return h.value
+
+
+def spense_export_rows(h: int, vals=None, meta=None, mask=None, dense=None, stream=None) -> np.ndarray:
+    """Write an output-split layer's canonical form into the given device tensors; returns rho (numpy int32)."""
+    info = spense_info(h)
+    rho = np.empty(info["N"], dtype=np.int32)
+    st = _lib().spense_export_rows(h, _ptr(vals), _ptr(meta), _ptr(mask), _ptr(dense), rho.ctypes.data,
+                                   _stream(stream))
+    _check(st, "spense_export_rows")
+    return rho
 
 
 def spense_linear(h: int, X, Y, *, xdtype: Optional[int] = None, ydtype: Optional[int] = None,

@@ -36,8 +36,17 @@ struct spense_layer {
   size_t xws_bytes = 0;
   int32_t* counters = nullptr;
   size_t n_counters = 0;
+  int32_t* ycol = nullptr;  // output column of each packed row, -1 on padding rows
+  int32_t* wrow = nullptr;  // W row of each packed row (parts of an output-split layer)
   int64_t weight_bytes = 0;
   int64_t device_bytes = 0;
+  // output-split layer (Technical Summary 2.A): no packed form of its own;
+  // part[0] holds the 2:4 rows (no dense columns), part[1] the dense rows (no
+  // sparse columns); either may be absent.  rho_host = [sparse rows | dense rows].
+  int split = 0;
+  spense_layer* part[2] = {nullptr, nullptr};
+  int64_t N_s = 0, N_d = 0;
+  std::vector<int32_t> rho_host;
 };
 
 namespace {
@@ -53,9 +62,13 @@ bool valid_dtype(int32_t t) { return t == SPENSE_F32 || t == SPENSE_BF16 || t ==
 
 int64_t elem_bytes(int32_t t) { return t == SPENSE_F32 ? 4 : t == SPENSE_BF16 ? 2 : 1; }
 
+void release(spense_layer* h);
 void release(spense_layer* h) {
   if (!h) return;
-  void* ptrs[] = {h->wpack, h->scales, h->pi, h->pip, h->vals32, h->meta32, h->dense32, h->ws, h->counters, h->xws};
+  release(h->part[0]);
+  release(h->part[1]);
+  void* ptrs[] = {h->wpack, h->scales, h->pi,      h->pip, h->vals32, h->meta32,
+                  h->dense32, h->ws,   h->counters, h->xws, h->ycol,   h->wrow};
   for (void* p : ptrs)
     if (p) (void)hipFree(p);
   delete h;
@@ -119,24 +132,19 @@ const char* spense_strerror(int status) {
   }
 }
 
-int spense_pack(const void* W, int32_t wdtype, int64_t N, int64_t K, int64_t ldw, const float* scales,
-                const int32_t* dense_cols, int64_t n_dense, double dense_fraction, void* stream, spense_handle* out) {
-  // ---- validation (host only) ----
-  if (!out) return SPENSE_EINVAL;
-  *out = nullptr;
-  if (!W || !valid_dtype(wdtype)) return SPENSE_EINVAL;
-  if (N < 1 || K < 1 || ldw < K) return SPENSE_EINVAL;
-  if (N > (int64_t(1) << 31) || K > (int64_t(1) << 31) || N * ldw > (int64_t(1) << 40)) return SPENSE_EINVAL;
-  if ((wdtype == SPENSE_FP8_E4M3) != (scales != nullptr)) return SPENSE_EINVAL;
-  std::vector<int32_t> pi;
-  int64_t K_s = 0, K_d = 0;
-  int rc = resolve_dense_set(K, dense_cols, n_dense, dense_fraction, pi, K_s, K_d);
-  if (rc != SPENSE_OK) return rc;
+}  // extern "C"
 
+namespace {
+
+// Packs the rows `rows` of W (host list of W row indices; empty = every row in
+// order) with column order pi; packed row n writes output column ycol[n]
+// (empty = n).  scales (device, fp8 only) are indexed by W row.  Synchronises s.
+int build_layer(const void* W, int32_t wdtype, int64_t N, int64_t K, int64_t ldw, const float* scales,
+                const std::vector<int32_t>& rows, std::vector<int32_t> pi, int64_t K_s, int64_t K_d,
+                const std::vector<int32_t>& ycol, hipStream_t s, spense_layer** out) {
   spense_layer* h = new (std::nothrow) spense_layer();
   if (!h) return SPENSE_ENOMEM;
   h->pi_host = std::move(pi);
-  hipStream_t s = (hipStream_t)stream;
   LayerDesc& d = h->d;
   d.N = N;
   d.K = K;
@@ -156,8 +164,15 @@ int spense_pack(const void* W, int32_t wdtype, int64_t N, int64_t K, int64_t ldw
   e = dev_alloc(&h->pi, (size_t)K * 4);
   if (e == hipSuccess) e = hipMemcpyAsync(h->pi, h->pi_host.data(), (size_t)K * 4, hipMemcpyHostToDevice, s);
   d.pi = h->pi;
+  if (!rows.empty()) {
+    if (e == hipSuccess) e = dev_alloc(&h->wrow, (size_t)N * 4);
+    if (e == hipSuccess) e = hipMemcpyAsync(h->wrow, rows.data(), (size_t)N * 4, hipMemcpyHostToDevice, s);
+    d.wrow = h->wrow;
+  }
 
   std::vector<int32_t> pip;
+  std::vector<float> sc_host;
+  std::vector<int32_t> ycol_host;
   if (wdtype != SPENSE_F32) {
     d.n_sm = (K_s + kMacro - 1) / kMacro;
     d.n_dm = (K_d + kMacro - 1) / kMacro;
@@ -179,19 +194,25 @@ int spense_pack(const void* W, int32_t wdtype, int64_t N, int64_t K, int64_t ldw
       e = hipMemcpyAsync(h->pip, pip.data(), (size_t)d.K_p * 4, hipMemcpyHostToDevice, s);
     d.wpack = h->wpack;
     d.pip = h->pip;
-    // per-row output scales, padded to whole row tiles; 1.0 for bf16 weights,
-    // so the kernels load and apply them unconditionally
-    const size_t sbytes = (size_t)(d.NT * kRowTile) * 4;
-    if (e == hipSuccess) e = dev_alloc(&h->scales, sbytes);
+    // per packed row: output scale (1.0 for bf16 weights) and output column,
+    // padded to whole row tiles, so the kernels load both unconditionally
+    const size_t tile_rows = (size_t)(d.NT * kRowTile);
+    sc_host.assign(tile_rows, wdtype == SPENSE_FP8_E4M3 ? 0.0f : 1.0f);
     if (wdtype == SPENSE_FP8_E4M3) {
-      if (e == hipSuccess) e = hipMemsetAsync(h->scales, 0, sbytes, s);
-      if (e == hipSuccess) e = hipMemcpyAsync(h->scales, scales, (size_t)N * 4, hipMemcpyDeviceToDevice, s);
-    } else {
-      const std::vector<float> ones((size_t)(d.NT * kRowTile), 1.0f);
-      if (e == hipSuccess) e = hipMemcpyAsync(h->scales, ones.data(), sbytes, hipMemcpyHostToDevice, s);
-      if (e == hipSuccess) e = hipStreamSynchronize(s);  // the host buffer is released on return
+      const int64_t Nw = rows.empty() ? N : (int64_t)(*std::max_element(rows.begin(), rows.end())) + 1;
+      std::vector<float> all((size_t)Nw);
+      if (e == hipSuccess) e = hipMemcpyAsync(all.data(), scales, (size_t)Nw * 4, hipMemcpyDeviceToHost, s);
+      if (e == hipSuccess) e = hipStreamSynchronize(s);
+      for (int64_t n = 0; n < N && e == hipSuccess; ++n) sc_host[(size_t)n] = all[(size_t)(rows.empty() ? n : rows[(size_t)n])];
     }
+    ycol_host.assign(tile_rows, -1);
+    for (int64_t n = 0; n < N; ++n) ycol_host[(size_t)n] = ycol.empty() ? (int32_t)n : ycol[(size_t)n];
+    if (e == hipSuccess) e = dev_alloc(&h->scales, tile_rows * 4);
+    if (e == hipSuccess) e = hipMemcpyAsync(h->scales, sc_host.data(), tile_rows * 4, hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = dev_alloc(&h->ycol, tile_rows * 4);
+    if (e == hipSuccess) e = hipMemcpyAsync(h->ycol, ycol_host.data(), tile_rows * 4, hipMemcpyHostToDevice, s);
     d.scales = h->scales;
+    d.ycol = h->ycol;
   } else {
     d.gather = 1;
     const size_t vbytes = (size_t)(N * (K_s / 2)) * 4, mbytes = (size_t)(N * d.meta_words) * 4,
@@ -205,11 +226,102 @@ int spense_pack(const void* W, int32_t wdtype, int64_t N, int64_t K, int64_t ldw
     d.dense32 = h->dense32;
   }
   if (e == hipSuccess) e = launch_pack(d, W, ldw, s);
+  // the host staging buffers above are released on return
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) {
     (void)hipStreamSynchronize(s);
     release(h);
     return e == hipErrorOutOfMemory ? (g_last_hip = (int)e, SPENSE_ENOMEM) : hip_fail(e);
+  }
+  *out = h;
+  return SPENSE_OK;
+}
+
+int validate_pack(const void* W, int32_t wdtype, int64_t N, int64_t K, int64_t ldw, const float* scales,
+                  spense_handle* out) {
+  if (!out) return SPENSE_EINVAL;
+  *out = nullptr;
+  if (!W || !valid_dtype(wdtype)) return SPENSE_EINVAL;
+  if (N < 1 || K < 1 || ldw < K) return SPENSE_EINVAL;
+  if (N > (int64_t(1) << 31) || K > (int64_t(1) << 31) || N * ldw > (int64_t(1) << 40)) return SPENSE_EINVAL;
+  if ((wdtype == SPENSE_FP8_E4M3) != (scales != nullptr)) return SPENSE_EINVAL;
+  return SPENSE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int spense_pack(const void* W, int32_t wdtype, int64_t N, int64_t K, int64_t ldw, const float* scales,
+                const int32_t* dense_cols, int64_t n_dense, double dense_fraction, void* stream, spense_handle* out) {
+  // ---- validation (host only) ----
+  int rc = validate_pack(W, wdtype, N, K, ldw, scales, out);
+  if (rc != SPENSE_OK) return rc;
+  std::vector<int32_t> pi;
+  int64_t K_s = 0, K_d = 0;
+  rc = resolve_dense_set(K, dense_cols, n_dense, dense_fraction, pi, K_s, K_d);
+  if (rc != SPENSE_OK) return rc;
+  return build_layer(W, wdtype, N, K, ldw, scales, {}, std::move(pi), K_s, K_d, {}, (hipStream_t)stream, out);
+}
+
+int spense_pack_rows(const void* W, int32_t wdtype, int64_t N, int64_t K, int64_t ldw, const float* scales,
+                     const int32_t* dense_rows, int64_t n_dense, double dense_fraction, void* stream,
+                     spense_handle* out) {
+  // ---- validation (host only) ----
+  int rc = validate_pack(W, wdtype, N, K, ldw, scales, out);
+  if (rc != SPENSE_OK) return rc;
+  if (wdtype == SPENSE_F32) return SPENSE_EUNSUPPORTED;
+  // the dense row set: rows resolve exactly like columns, with K = N; then
+  // K must hold whole 2:4 groups when any row is sparse
+  std::vector<int32_t> rho;
+  int64_t N_s = 0, N_d = 0;
+  std::vector<char> is_dense((size_t)N, 0);
+  if (dense_rows) {
+    if (n_dense < 0 || n_dense > N) return SPENSE_EINVAL;
+    for (int64_t i = 0; i < n_dense; ++i) {
+      const int32_t r = dense_rows[i];
+      if (r < 0 || r >= N || is_dense[(size_t)r]) return SPENSE_EINVAL;
+      is_dense[(size_t)r] = 1;
+    }
+    N_d = n_dense;
+  } else {
+    if (!(dense_fraction >= 0.0 && dense_fraction <= 1.0)) return SPENSE_EINVAL;
+    N_d = std::min<int64_t>(N, (int64_t)std::floor(dense_fraction * (double)N + 0.5));
+    for (int64_t r = N - N_d; r < N; ++r) is_dense[(size_t)r] = 1;
+  }
+  N_s = N - N_d;
+  if (N_s > 0 && K % 4 != 0) return SPENSE_EINVAL;
+  rho.resize((size_t)N);
+  int64_t ia = 0, ib = N_s;
+  for (int64_t r = 0; r < N; ++r) rho[(size_t)(is_dense[(size_t)r] ? ib++ : ia++)] = (int32_t)r;
+
+  spense_layer* h = new (std::nothrow) spense_layer();
+  if (!h) return SPENSE_ENOMEM;
+  h->split = 1;
+  h->N_s = N_s;
+  h->N_d = N_d;
+  h->rho_host = rho;
+  h->d.N = N;
+  h->d.K = K;
+  h->d.K_s = N_s > 0 ? K : 0;
+  h->d.K_d = N_d > 0 ? K : 0;
+  h->d.wdtype = wdtype;
+  (void)hipGetDevice(&h->device);
+  std::vector<int32_t> ident((size_t)K);
+  for (int64_t c = 0; c < K; ++c) ident[(size_t)c] = (int32_t)c;
+  hipStream_t s = (hipStream_t)stream;
+  for (int part = 0; part < 2; ++part) {
+    const int64_t n = part == 0 ? N_s : N_d;
+    if (n == 0) continue;
+    const std::vector<int32_t> sel(rho.begin() + (part == 0 ? 0 : N_s), rho.begin() + (part == 0 ? N_s : N));
+    rc = build_layer(W, wdtype, n, K, ldw, scales, sel, ident, part == 0 ? K : 0, part == 0 ? 0 : K, sel, s,
+                     &h->part[part]);
+    if (rc != SPENSE_OK) {
+      release(h);
+      return rc;
+    }
+    h->weight_bytes += h->part[part]->weight_bytes;
+    h->device_bytes += h->part[part]->device_bytes;
   }
   *out = h;
   return SPENSE_OK;
@@ -241,7 +353,11 @@ static int64_t stream_lds_bytes(int64_t M) { return 2 * M * (kStreamChunk * kMac
 constexpr int64_t kCUs = 256;             // compute units of the target GPU
 constexpr int64_t kLdsPerCU = 160 * 1024;  // LDS bytes per CU
 
-static int plan_linear(const spense_layer* h, int64_t M, int32_t splits, LinearPlan& p) {
+// NT_fill: row tiles launched in the same grid (the layer's own, or both row
+// classes of an output-split layer); the split count and the blocking are
+// chosen from it so that both classes get the same kernel shape.
+static int plan_linear(const spense_layer* h, int64_t M, int32_t splits, int64_t NT_fill, LinearPlan& p,
+                       bool force_chunked = false) {
   const LayerDesc& d = h->d;
   const int64_t steps = std::max<int64_t>(d.n_sm, d.n_dm);
   const int64_t max_splits = std::max<int64_t>(1, std::min<int64_t>(steps, 64));
@@ -270,12 +386,12 @@ static int plan_linear(const spense_layer* h, int64_t M, int32_t splits, LinearP
     }
     int64_t S = splits;
     if (S == 0) {
-      S = d.NT >= 1024 ? 1 : std::max<int64_t>(1, (1920 + d.NT - 1) / d.NT);
+      S = NT_fill >= 1024 ? 1 : std::max<int64_t>(1, (1920 + NT_fill - 1) / NT_fill);
       S = std::min<int64_t>(S, max_splits);
       if (ch == 0)  // single-shot staging requested: split until it fits
         while (S < max_splits && decode_lds_bytes(d, M, S) > 64 * 1024) ++S;
     }
-    p.chunked = (ch == 1 || decode_lds_bytes(d, M, S) > 64 * 1024) ? 1 : 0;
+    p.chunked = (force_chunked || ch == 1 || decode_lds_bytes(d, M, S) > 64 * 1024) ? 1 : 0;
     // chunked staging: two chunk buffers per workgroup bound the residency,
     // so smaller workgroups keep more waves per CU streaming
     if (p.chunked && !overridden) p.waves = 4;
@@ -302,7 +418,7 @@ static int plan_linear(const spense_layer* h, int64_t M, int32_t splits, LinearP
   // per wave halve the LDS reads per product but give fewer workgroups: used
   // when the row tiles alone still give at least one workgroup per two CUs;
   // otherwise one row tile per wave plus splits.
-  const int64_t wg_nr2 = (d.NT + 15) / 16 * ((M + 31) / 32);
+  const int64_t wg_nr2 = (NT_fill + 15) / 16 * ((M + 31) / 32);
   int pre = M <= 32 || wg_nr2 < kCUs / 2 ? 0 : M <= 64 ? 1 : M <= 128 ? 2 : 8;
   if (const char* t = std::getenv("SPENSE_TILE")) {
     const int v = std::atoi(t);
@@ -323,14 +439,70 @@ static int plan_linear(const spense_layer* h, int64_t M, int32_t splits, LinearP
   p.rgroups = (int)((d.NT + p.waves * p.nr - 1) / (p.waves * p.nr));
   int64_t S = splits;
   if (S == 0) {
-    const int64_t units = (int64_t)p.rgroups * p.mgroups;
+    const int64_t units = (NT_fill + p.waves * p.nr - 1) / (p.waves * p.nr) * p.mgroups;
     const int64_t resident = kCUs * std::max<int64_t>(1, kLdsPerCU / lds);
     S = units >= kCUs / 2 ? 1 : std::max<int64_t>(1, std::min<int64_t>(resident / units, max_splits));
   }
   p.splits = (int)S;
   const int64_t grid = (int64_t)p.rgroups * p.mgroups * S;
-  p.xcd_remap = (p.mgroups > 1 && grid % 8 == 0) ? 1 : 0;
+  p.xcd_remap = (p.mgroups > 1 && grid % 8 == 0) ? 1 : 0;  // decided per layer (the remap stays inside it)
   if (const char* x = std::getenv("SPENSE_XCD")) p.xcd_remap = (std::atoi(x) != 0 && grid % 8 == 0) ? 1 : 0;
+  return SPENSE_OK;
+}
+
+// Grows the handle's workspaces for this call (synchronising the stream
+// first: earlier launches may still read the old ones) and fills a.ws /
+// a.counters.  With gather, also writes X'p into the gather workspace and
+// points a at it.
+static int prepare_call(spense_layer* h, int64_t M, const LinearPlan& p, LinearArgs& a, bool gather_now,
+                        hipStream_t s) {
+  const LayerDesc& d = h->d;
+  if (gather_now) {
+    const size_t need = (size_t)M * (size_t)d.K_p * 2;
+    if (need > h->xws_bytes) {
+      hipError_t e = hipStreamSynchronize(s);
+      if (e != hipSuccess) return hip_fail(e);
+      if (h->xws) (void)hipFree(h->xws);
+      h->xws = nullptr;
+      h->xws_bytes = 0;
+      e = hipMalloc(&h->xws, need);
+      if (e != hipSuccess) return e == hipErrorOutOfMemory ? SPENSE_ENOMEM : hip_fail(e);
+      h->xws_bytes = need;
+    }
+    hipError_t e = launch_gather_x(d, a.X, M, a.ldx, h->xws, s);
+    if (e != hipSuccess) return hip_fail(e);
+    a.X = h->xws;
+    a.ldx = d.K_p;
+    a.gather = 0;
+  }
+  if (p.splits > 1) {
+    const size_t need = (size_t)p.splits * (size_t)M * (size_t)(d.NT * kRowTile) * 4;
+    const size_t need_cnt = (size_t)p.rgroups * (size_t)p.mgroups;
+    if (need > h->ws_bytes || need_cnt > h->n_counters) {
+      hipError_t e = hipStreamSynchronize(s);
+      if (e != hipSuccess) return hip_fail(e);
+      if (need > h->ws_bytes) {
+        if (h->ws) (void)hipFree(h->ws);
+        h->ws = nullptr;
+        h->ws_bytes = 0;
+        e = hipMalloc((void**)&h->ws, need);
+        if (e != hipSuccess) return e == hipErrorOutOfMemory ? SPENSE_ENOMEM : hip_fail(e);
+        h->ws_bytes = need;
+      }
+      if (need_cnt > h->n_counters) {
+        if (h->counters) (void)hipFree(h->counters);
+        h->counters = nullptr;
+        h->n_counters = 0;
+        e = hipMalloc((void**)&h->counters, need_cnt * 4);
+        if (e != hipSuccess) return e == hipErrorOutOfMemory ? SPENSE_ENOMEM : hip_fail(e);
+        e = launch_zero_i32(h->counters, (int64_t)need_cnt, s);
+        if (e != hipSuccess) return hip_fail(e);
+        h->n_counters = need_cnt;
+      }
+    }
+    a.ws = h->ws;
+    a.counters = h->counters;
+  }
   return SPENSE_OK;
 }
 
@@ -360,60 +532,69 @@ int spense_linear_splits(spense_handle h, const void* X, int32_t xdtype, int64_t
     hipError_t e = launch_linear(d, a, p, s);
     return e == hipSuccess ? SPENSE_OK : hip_fail(e);
   }
-  LinearPlan p{};
   const bool x_aligned = aligned16(X) && (ldx % 8) == 0;
-  a.gather = d.gather || !x_aligned;
-  int rc = plan_linear(h, M, splits, p);
-  if (rc != SPENSE_OK) return rc;
-  a.splits = p.splits;
-  if (p.chunked && a.gather) {
-    // the chunked kernels stage a contiguous X'p: gather it once into the handle's workspace
-    const size_t need = (size_t)M * (size_t)d.K_p * 2;
-    if (need > h->xws_bytes) {
-      hipError_t e = hipStreamSynchronize(s);  // earlier launches may still read the old workspace
-      if (e != hipSuccess) return hip_fail(e);
-      if (h->xws) (void)hipFree(h->xws);
-      h->xws = nullptr;
-      h->xws_bytes = 0;
-      e = hipMalloc(&h->xws, need);
-      if (e != hipSuccess) return e == hipErrorOutOfMemory ? SPENSE_ENOMEM : hip_fail(e);
-      h->xws_bytes = need;
-    }
-    hipError_t e = launch_gather_x(d, X, M, ldx, h->xws, s);
-    if (e != hipSuccess) return hip_fail(e);
-    a.X = h->xws;
-    a.ldx = d.K_p;
-    a.gather = 0;
+
+  // the layers of this call: the handle itself, or the row classes of an output-split layer
+  spense_layer* parts[2] = {h, nullptr};
+  int n_parts = 1;
+  if (h->split) {
+    n_parts = 0;
+    for (spense_layer* q : h->part)
+      if (q) parts[n_parts++] = q;
   }
-  if (p.splits > 1) {
-    const size_t need = (size_t)p.splits * (size_t)M * (size_t)(d.NT * kRowTile) * 4;
-    const size_t need_cnt = (size_t)p.rgroups * (size_t)p.mgroups;
-    if (need > h->ws_bytes || need_cnt > h->n_counters) {
-      hipError_t e = hipStreamSynchronize(s);  // earlier launches may still read the old workspace
-      if (e != hipSuccess) return hip_fail(e);
-      if (need > h->ws_bytes) {
-        if (h->ws) (void)hipFree(h->ws);
-        h->ws = nullptr;
-        h->ws_bytes = 0;
-        e = hipMalloc((void**)&h->ws, need);
-        if (e != hipSuccess) return e == hipErrorOutOfMemory ? SPENSE_ENOMEM : hip_fail(e);
-        h->ws_bytes = need;
-      }
-      if (need_cnt > h->n_counters) {
-        if (h->counters) (void)hipFree(h->counters);
-        h->counters = nullptr;
-        h->n_counters = 0;
-        e = hipMalloc((void**)&h->counters, need_cnt * 4);
-        if (e != hipSuccess) return e == hipErrorOutOfMemory ? SPENSE_ENOMEM : hip_fail(e);
-        e = launch_zero_i32(h->counters, (int64_t)need_cnt, s);
-        if (e != hipSuccess) return hip_fail(e);
-        h->n_counters = need_cnt;
-      }
-    }
-    a.ws = h->ws;
-    a.counters = h->counters;
+  int64_t NT_fill = 0;
+  for (int i = 0; i < n_parts; ++i) NT_fill += parts[i]->d.NT;
+  LinearPlan p[2]{};
+  LinearArgs aa[2]{a, a};
+  for (int i = 0; i < n_parts; ++i) {
+    aa[i].gather = parts[i]->d.gather || !x_aligned;
+    const int rc = plan_linear(parts[i], M, splits, NT_fill, p[i]);
+    if (rc != SPENSE_OK) return rc;
   }
-  hipError_t e = launch_linear(d, a, p, s);
+  if (n_parts == 2 && splits == 0) {
+    // Balance the two row classes: a dense row tile streams more bytes than a
+    // 2:4 one (e4m3, K = 5120: 80 KB vs 50 KB), so the heavier class gets
+    // proportionally more splits and its waves finish with the others.
+    int64_t tile_bytes[2], lightest = 0;
+    for (int i = 0; i < 2; ++i) {
+      const LayerDesc& q = parts[i]->d;
+      tile_bytes[i] = q.n_sm * (unit_bytes(q.wdtype) + kIdxBlock) + 2 * q.n_dm * unit_bytes(q.wdtype);
+      lightest = i == 0 ? tile_bytes[0] : std::min(lightest, tile_bytes[i]);
+    }
+    bool chunk_any = false;
+    int32_t S[2];
+    for (int i = 0; i < 2; ++i) {
+      const LayerDesc& q = parts[i]->d;
+      const int64_t max_s = std::max<int64_t>(1, std::min<int64_t>(std::max(q.n_sm, q.n_dm), 64));
+      const int64_t ratio = (2 * tile_bytes[i] + lightest) / (2 * lightest);  // rounded
+      S[i] = (int32_t)std::min<int64_t>(max_s, (int64_t)p[i].splits * std::max<int64_t>(1, ratio));
+      const int rc = plan_linear(parts[i], M, S[i], NT_fill, p[i]);
+      if (rc != SPENSE_OK) return rc;
+      chunk_any = chunk_any || p[i].chunked;
+    }
+    // both classes run in one grid, so they need the same kernel shape
+    if (chunk_any && !(p[0].chunked && p[1].chunked))
+      for (int i = 0; i < 2; ++i) {
+        const int rc = plan_linear(parts[i], M, S[i], NT_fill, p[i], true);
+        if (rc != SPENSE_OK) return rc;
+      }
+  }
+  for (int i = 0; i < n_parts; ++i) aa[i].splits = p[i].splits;
+  // The row classes of an output-split layer see the same activations in the
+  // same column order (identity, padded to whole 128-column steps), so one
+  // gathered copy serves both.
+  for (int i = 0; i < n_parts; ++i) {
+    const bool gather_now = p[i].chunked && aa[i].gather && i == 0;
+    const int rc = prepare_call(parts[i], M, p[i], aa[i], gather_now, s);
+    if (rc != SPENSE_OK) return rc;
+    if (i == 1 && p[1].chunked && aa[1].gather) {
+      aa[1].X = aa[0].X;
+      aa[1].ldx = aa[0].ldx;
+      aa[1].gather = 0;
+    }
+  }
+  hipError_t e = n_parts == 1 ? launch_linear(parts[0]->d, aa[0], p[0], s)
+                              : launch_linear2(parts[0]->d, aa[0], p[0], parts[1]->d, aa[1], p[1], s);
   return e == hipSuccess ? SPENSE_OK : hip_fail(e);
 }
 
@@ -430,14 +611,30 @@ int spense_info(spense_handle h, spense_layer_info* info) {
   info->K_s = h->d.K_s;
   info->K_d = h->d.K_d;
   info->wdtype = h->d.wdtype;
-  info->gather = h->d.wdtype == SPENSE_F32 ? 1 : h->d.gather;
+  info->gather = h->split ? (h->part[0] ? h->part[0] : h->part[1])->d.gather
+                          : (h->d.wdtype == SPENSE_F32 ? 1 : h->d.gather);
   info->weight_bytes = h->weight_bytes;
   info->device_bytes = h->device_bytes;
+  info->split = h->split;
+  info->N_s = h->split ? h->N_s : h->d.N;
+  info->N_d = h->split ? h->N_d : 0;
   return SPENSE_OK;
 }
 
+int spense_export_rows(spense_handle h, void* vals, uint32_t* meta, uint8_t* mask, void* dense, int32_t* rho,
+                       void* stream) {
+  if (!h || !h->split) return SPENSE_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  if (rho) std::memcpy(rho, h->rho_host.data(), (size_t)h->d.N * 4);
+  hipError_t e = hipSuccess;
+  if (h->part[0]) e = launch_export(h->part[0]->d, vals, meta, mask, nullptr, s);
+  if (e == hipSuccess && h->part[1]) e = launch_export(h->part[1]->d, nullptr, nullptr, nullptr, dense, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  return e == hipSuccess ? SPENSE_OK : hip_fail(e);
+}
+
 int spense_export(spense_handle h, void* vals, uint32_t* meta, uint8_t* mask, void* dense, int32_t* pi, void* stream) {
-  if (!h) return SPENSE_EINVAL;
+  if (!h || h->split) return SPENSE_EINVAL;
   hipStream_t s = (hipStream_t)stream;
   if (pi) std::memcpy(pi, h->pi_host.data(), (size_t)h->d.K * 4);
   hipError_t e = launch_export(h->d, vals, meta, mask, dense, s);

@@ -57,7 +57,9 @@ struct LayerDesc {
   int64_t tile_bytes;    // (n_sm + 2 n_dm) * unit_bytes + n_sm * kIdxBlock
   int64_t idx_off;       // offset of the index blocks within a row tile
   uint8_t* wpack;        // unit layout, NT * tile_bytes bytes
-  const float* scales;   // [NT * 16] (e4m3) or nullptr
+  const float* scales;   // [NT * 16] per packed row (1.0 for bf16 weights; 0 on padding rows)
+  const int32_t* ycol;   // [NT * 16] output column of each packed row, -1 on padding rows
+  const int32_t* wrow;   // [N] W row of each packed row, or nullptr for W's own row order (pack only)
   const int32_t* pi;     // [K]
   const int32_t* pip;    // [K_p] padded column map
   // fp32 canonical form
@@ -117,6 +119,9 @@ constexpr int kStreamChunk = 8;  // units per activation chunk of linear_stream_
 hipError_t launch_pack(const LayerDesc& d, const void* W, int64_t ldw, hipStream_t s);
 hipError_t launch_export(const LayerDesc& d, void* vals, uint32_t* meta, uint8_t* mask, void* dense, hipStream_t s);
 hipError_t launch_linear(const LayerDesc& d, const LinearArgs& a, const LinearPlan& p, hipStream_t s);
+// two layers with the same kernel shape in one grid (the row classes of an output-split layer)
+hipError_t launch_linear2(const LayerDesc& d0, const LinearArgs& a0, const LinearPlan& p0, const LayerDesc& d1,
+                          const LinearArgs& a1, const LinearPlan& p1, hipStream_t s);
 hipError_t launch_zero_i32(int32_t* p, int64_t n, hipStream_t s);
 // X'p = X[:, pip] as a contiguous [M][K_p] bf16 buffer
 hipError_t launch_gather_x(const LayerDesc& d, const void* X, int64_t M, int64_t ldx, void* Xp, hipStream_t s);

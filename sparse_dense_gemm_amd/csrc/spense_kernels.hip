@@ -7,6 +7,8 @@
 // spense_internal.h.
 #include "spense_internal.h"
 
+#include <algorithm>
+
 namespace spense {
 namespace {
 
@@ -130,10 +132,18 @@ __device__ __forceinline__ bool arrive_last(int32_t* cnt, int S, int* flag) {
   return *flag != 0;
 }
 
-// Scales of this lane's four output rows of row tile rt (rows rt*16 + 4(lane/16) + 0..3),
-// loaded when a kernel starts so that its epilogue does not wait on memory.
-__device__ __forceinline__ f32x4 row_scales(const LayerDesc& d, int64_t rt, int lane) {
-  return *(const f32x4*)(d.scales + rt * 16 + 4 * (lane >> 4));
+// Scales and output columns of this lane's four output rows of row tile rt
+// (packed rows rt*16 + 4(lane/16) + 0..3), loaded when a kernel starts so that
+// its epilogue does not wait on memory.  Column -1 marks a padding row.
+struct TileOut {
+  f32x4 sc;
+  u32x4 col;
+};
+__device__ __forceinline__ TileOut tile_out(const LayerDesc& d, int64_t rt, int lane) {
+  TileOut t;
+  t.sc = *(const f32x4*)(d.scales + rt * 16 + 4 * (lane >> 4));
+  t.col = *(const u32x4*)(d.ycol + rt * 16 + 4 * (lane >> 4));
+  return t;
 }
 
 __device__ __forceinline__ void store_y(const LinearArgs& a, int64_t m, int64_t n, float y) {
@@ -145,11 +155,11 @@ __device__ __forceinline__ void store_y(const LinearArgs& a, int64_t m, int64_t 
 // the tile adds the partials in split order.  acc: lane l, register r =
 // Y^T[n = 16rt + 4(l/16) + r][m = m0 + 16mt + l%16].
 // Epilogue of a wave's NR row tiles (rt0 ..) x MT m-tiles; acc[r * MT + t],
-// sc[r] = row_scales of row tile rt0 + r.  Compile-time counts keep every
+// to[r] = tile_out of row tile rt0 + r.  Compile-time counts keep every
 // accumulator index static (a dynamic index would move them to scratch).
 template <int NR, int MT>
 __device__ __forceinline__ void finish_tile(const LayerDesc& d, const LinearArgs& a, const f32x4* acc,
-                                            const f32x4* sc, int64_t rt0, int64_t m0, int s, int S,
+                                            const TileOut* to, int64_t rt0, int64_t m0, int s, int S,
                                             int64_t cnt_index, int* last_flag) {
   const int lane = threadIdx.x & 63;
   const int nb = 4 * (lane >> 4);
@@ -183,8 +193,8 @@ __device__ __forceinline__ void finish_tile(const LayerDesc& d, const LinearArgs
       }
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const int64_t n = rt * 16 + nb + q;
-        if (n < d.N) store_y(a, m, n, sum[q] * sc[r][q]);
+        const int col = (int)to[r].col[q];
+        if (col >= 0) store_y(a, m, col, sum[q] * to[r].sc[q]);
       }
     }
   }
@@ -249,6 +259,8 @@ __global__ void pack_sparse_kernel(LayerDesc d, const WT* __restrict__ W, int64_
   const int64_t i = rest % d.n_sm, rt = rest / d.n_sm;
   const int r = lane & 15, g = lane >> 4;
   const int64_t n = rt * 16 + r;
+  // packed row n holds W row wrow (a row subset of W for the parts of an output-split layer)
+  const int64_t wrow = n < d.N ? (d.wrow ? (int64_t)d.wrow[n] : n) : 0;
   uint32_t idx = 0;
   WT v[16];
 #pragma unroll
@@ -263,7 +275,7 @@ __global__ void pack_sparse_kernel(LayerDesc d, const WT* __restrict__ W, int64_
         uint32_t k[4];
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          w[t] = W[n * ldw + d.pi[4 * G + t]];
+          w[t] = W[wrow * ldw + d.pi[4 * G + t]];
           k[t] = mag_key(w[t]);
         }
         int i0, i1;
@@ -293,6 +305,8 @@ __global__ void pack_dense_kernel(LayerDesc d, const WT* __restrict__ W, int64_t
   const int64_t t = rest % units, rt = rest / units;
   const int r = lane & 15, g = lane >> 4;
   const int64_t n = rt * 16 + r;
+  // packed row n holds W row wrow (a row subset of W for the parts of an output-split layer)
+  const int64_t wrow = n < d.N ? (d.wrow ? (int64_t)d.wrow[n] : n) : 0;
   WT v[16];
 #pragma unroll
   for (int half = 0; half < 2; ++half)
@@ -301,7 +315,7 @@ __global__ void pack_dense_kernel(LayerDesc d, const WT* __restrict__ W, int64_t
 #pragma unroll
       for (int w = 0; w < 2; ++w) {
         const int64_t c = 64 * t + 4 * group_local(g, j) + 2 * half + w;
-        v[8 * half + 2 * j + w] = (n < d.N && c < d.K_d) ? W[n * ldw + d.pi[d.K_s + c]] : (WT)0;
+        v[8 * half + 2 * j + w] = (n < d.N && c < d.K_d) ? W[wrow * ldw + d.pi[d.K_s + c]] : (WT)0;
       }
   store_unit<WT>(d.wpack + rt * d.tile_bytes + (d.n_sm + t) * kUnit<WT>, lane, v);
 }
@@ -493,14 +507,14 @@ __device__ __forceinline__ u32x4 gather8(const LinearArgs& a, const LayerDesc& d
 // straight-line code and the in-order load counter stays P-1 units ahead.
 // ---------------------------------------------------------------------------
 template <typename WT, int NW, int P, bool GATHER>
-__global__ __launch_bounds__(NW * 64) void linear_decode_kernel(LayerDesc d, LinearArgs a, LinearPlan p) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t xs_dyn[];
-  __shared__ int last_flag;
+__device__ __forceinline__ void decode_body(const LayerDesc& d, const LinearArgs& a, const LinearPlan& p, int block,
+                                            uint16_t* xs_dyn, int* last_flag_p) {
+  int& last_flag = *last_flag_p;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar address math
-  const int rg = blockIdx.x % p.rgroups;
+  const int rg = block % p.rgroups;
   const int S = p.splits;
-  const int s = (blockIdx.x / p.rgroups) % S;
+  const int s = (block / p.rgroups) % S;
   const int64_t rt = (int64_t)rg * NW + wave;
   const bool active = rt < d.NT;
   const int64_t ms0 = d.n_sm * s / S, ms1 = d.n_sm * (s + 1) / S;
@@ -521,7 +535,7 @@ __global__ __launch_bounds__(NW * 64) void linear_decode_kernel(LayerDesc d, Lin
   auto unit_ptr = [&](int k) { return tile + (k + (k < ns ? sbase : dbase)) * kUnit<WT>; };
   auto idx_ptr = [&](int k) { return k < ns ? sidx + k * 256 : unit_ptr(k); };
 
-  const f32x4 sc = row_scales(d, active ? rt : 0, lane);
+  const TileOut to = tile_out(d, active ? rt : 0, lane);
 
   // Stage X'p[0..M)[split columns] in LDS once: sparse macro-steps, then
   // dense ones, in batches of kStageBatch 16-byte pieces per thread (all index
@@ -631,7 +645,26 @@ __global__ __launch_bounds__(NW * 64) void linear_decode_kernel(LayerDesc d, Lin
       if (k0 + i < total) consume(i, k0 + i);
   }
   const f32x4 acc = acc0 + acc1;
-  finish_tile<1, 1>(d, a, &acc, &sc, rt, 0, s, S, rg, &last_flag);
+  finish_tile<1, 1>(d, a, &acc, &to, rt, 0, s, S, rg, &last_flag);
+}
+
+template <typename WT, int NW, int P, bool GATHER>
+__global__ __launch_bounds__(NW * 64) void linear_decode_kernel(LayerDesc d, LinearArgs a, LinearPlan p) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t xs_dyn[];
+  __shared__ int last_flag;
+  decode_body<WT, NW, P, GATHER>(d, a, p, blockIdx.x, xs_dyn, &last_flag);
+}
+
+// Two layers in one grid (the two row classes of an output-split layer): the
+// first workgroups run layer 0, the rest layer 1, with the same kernel shape.
+template <typename WT, int NW, int P, bool GATHER>
+__global__ __launch_bounds__(NW * 64) void linear_decode2_kernel(LayerDesc d0, LinearArgs a0, LinearPlan p0,
+                                                                 LayerDesc d1, LinearArgs a1, LinearPlan p1) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t xs_dyn[];
+  __shared__ int last_flag;
+  const int g0 = p0.rgroups * p0.splits * p0.mgroups;
+  if ((int)blockIdx.x < g0) decode_body<WT, NW, P, GATHER>(d0, a0, p0, blockIdx.x, xs_dyn, &last_flag);
+  else decode_body<WT, NW, P, GATHER>(d1, a1, p1, blockIdx.x - g0, xs_dyn, &last_flag);
 }
 
 // ---------------------------------------------------------------------------
@@ -645,10 +678,10 @@ __global__ __launch_bounds__(NW * 64) void linear_decode_kernel(LayerDesc d, Lin
 // a chosen dense set the host gathers it into a workspace first).
 // ---------------------------------------------------------------------------
 template <typename WT, int NW, int NR, int P, int CH, int MT>
-__global__ __launch_bounds__(NW * 64) void linear_stream_kernel(LayerDesc d, LinearArgs a, LinearPlan p) {
+__device__ __forceinline__ void stream_body(const LayerDesc& d, const LinearArgs& a, const LinearPlan& p, int block,
+                                            int grid, uint16_t* xs_dyn, int* last_flag_p) {
   static_assert(CH % P == 0, "a chunk must hold whole rings");
-  extern __shared__ __attribute__((aligned(16))) uint16_t xs_dyn[];
-  __shared__ int last_flag;
+  int& last_flag = *last_flag_p;
   constexpr int kPitch2 = CH * 128 + 8;                      // staged row: CH unit slots of 128 columns + pad
   constexpr int kPieces = (16 * MT * CH * 16) / (NW * 64);  // 16-byte pieces per thread per chunk (full m-group)
   static_assert(kPieces * NW * 64 == 16 * MT * CH * 16, "pieces must divide evenly");
@@ -659,8 +692,8 @@ __global__ __launch_bounds__(NW * 64) void linear_stream_kernel(LayerDesc d, Lin
   // order is remapped so that each XCD takes a contiguous run of logical ids,
   // m-group fastest: the m-groups that share a weight slice run on one XCD at
   // about the same time, and all but the first read it from that XCD's L2.
-  int b = blockIdx.x;
-  if (p.xcd_remap) b = (b % 8) * (gridDim.x / 8) + b / 8;
+  int b = block;
+  if (p.xcd_remap) b = (b % 8) * (grid / 8) + b / 8;
   const int S = p.splits;
   const int mg = b % p.mgroups;
   const int rg = (b / p.mgroups) % p.rgroups;
@@ -693,9 +726,9 @@ __global__ __launch_bounds__(NW * 64) void linear_stream_kernel(LayerDesc d, Lin
     for (int r = 0; r < NR; ++r) load_unit<WT>(f[r], unit_ptr(r, k), idx_ptr(r, k) + 4 * lane, lane);
   };
 
-  f32x4 sc[NR];
+  TileOut to[NR];
 #pragma unroll
-  for (int r = 0; r < NR; ++r) sc[r] = row_scales(d, rt0 + r < d.NT ? rt0 + r : 0, lane);
+  for (int r = 0; r < NR; ++r) to[r] = tile_out(d, rt0 + r < d.NT ? rt0 + r : 0, lane);
 
   UnitFrag<WT> wr[P][NR];
   // every wave streams (waves whose row tiles are all past the end stream tile
@@ -809,7 +842,24 @@ __global__ __launch_bounds__(NW * 64) void linear_stream_kernel(LayerDesc d, Lin
     }
   }
   if constexpr (kSplitAcc) acc[0] += acc1;
-  finish_tile<NR, MT>(d, a, acc, sc, rt0, m0, s, S, (int64_t)mg * p.rgroups + rg, &last_flag);
+  finish_tile<NR, MT>(d, a, acc, to, rt0, m0, s, S, (int64_t)mg * p.rgroups + rg, &last_flag);
+}
+
+template <typename WT, int NW, int NR, int P, int CH, int MT>
+__global__ __launch_bounds__(NW * 64) void linear_stream_kernel(LayerDesc d, LinearArgs a, LinearPlan p) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t xs_dyn[];
+  __shared__ int last_flag;
+  stream_body<WT, NW, NR, P, CH, MT>(d, a, p, blockIdx.x, gridDim.x, xs_dyn, &last_flag);
+}
+
+template <typename WT, int NW, int NR, int P, int CH, int MT>
+__global__ __launch_bounds__(NW * 64) void linear_stream2_kernel(LayerDesc d0, LinearArgs a0, LinearPlan p0,
+                                                                 LayerDesc d1, LinearArgs a1, LinearPlan p1) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t xs_dyn[];
+  __shared__ int last_flag;
+  const int g0 = p0.rgroups * p0.splits * p0.mgroups;
+  if ((int)blockIdx.x < g0) stream_body<WT, NW, NR, P, CH, MT>(d0, a0, p0, blockIdx.x, g0, xs_dyn, &last_flag);
+  else stream_body<WT, NW, NR, P, CH, MT>(d1, a1, p1, blockIdx.x - g0, gridDim.x - g0, xs_dyn, &last_flag);
 }
 
 // X'p[m][j] = X[m][pip[j]] (0 where pip[j] < 0), as a contiguous [M][K_p]
@@ -877,13 +927,19 @@ hipError_t launch_export_units(const LayerDesc& d, void* vals, uint32_t* meta, u
   return hipGetLastError();
 }
 
-template <typename WT, int NW, int P>
-hipError_t launch_decode_t(const LayerDesc& d, const LinearArgs& a, const LinearPlan& p, hipStream_t s) {
-  const unsigned grid = (unsigned)((int64_t)p.rgroups * p.splits);
-  if (a.gather) linear_decode_kernel<WT, NW, P, true><<<grid, NW * 64, p.lds_bytes, s>>>(d, a, p);
-  else linear_decode_kernel<WT, NW, P, false><<<grid, NW * 64, p.lds_bytes, s>>>(d, a, p);
-  return hipGetLastError();
-}
+// One launch: layer 0 alone, or layers 0 and 1 in one grid (two == true).
+struct Launch {
+  const LayerDesc* d[2];
+  const LinearArgs* a[2];
+  const LinearPlan* p[2];
+  bool two;
+  unsigned grid() const {
+    unsigned g = (unsigned)((int64_t)p[0]->rgroups * p[0]->splits * p[0]->mgroups);
+    if (two) g += (unsigned)((int64_t)p[1]->rgroups * p[1]->splits * p[1]->mgroups);
+    return g;
+  }
+  int lds() const { return two ? std::max(p[0]->lds_bytes, p[1]->lds_bytes) : p[0]->lds_bytes; }
+};
 
 // Kernels that may need more than the default 64 KB of dynamic LDS opt in once.
 template <typename K>
@@ -892,31 +948,54 @@ hipError_t allow_lds(K kernel, int bytes) {
   return hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
 }
 
+template <typename WT, int NW, int P, bool GATHER>
+hipError_t launch_decode_k(const Launch& L, hipStream_t s) {
+  if (L.two) {
+    linear_decode2_kernel<WT, NW, P, GATHER><<<L.grid(), NW * 64, L.lds(), s>>>(*L.d[0], *L.a[0], *L.p[0], *L.d[1],
+                                                                              *L.a[1], *L.p[1]);
+  } else {
+    linear_decode_kernel<WT, NW, P, GATHER><<<L.grid(), NW * 64, L.lds(), s>>>(*L.d[0], *L.a[0], *L.p[0]);
+  }
+  return hipGetLastError();
+}
+
+template <typename WT, int NW, int P>
+hipError_t launch_decode_t(const Launch& L, hipStream_t s) {
+  if (L.a[0]->gather) return launch_decode_k<WT, NW, P, true>(L, s);
+  return launch_decode_k<WT, NW, P, false>(L, s);
+}
+
 template <typename WT, int NW, int NR, int P, int CH, int MT>
-hipError_t launch_stream_k(const LayerDesc& d, const LinearArgs& a, const LinearPlan& p, hipStream_t s) {
+hipError_t launch_stream_k(const Launch& L, hipStream_t s) {
+  const LinearPlan& p = *L.p[0];
   if (p.waves != NW || p.nr != NR || p.depth != P || p.chunk != CH || p.mt != MT) return hipErrorInvalidValue;
-  const unsigned grid = (unsigned)((int64_t)p.rgroups * p.splits * p.mgroups);
-  auto k = linear_stream_kernel<WT, NW, NR, P, CH, MT>;
-  hipError_t e = allow_lds(k, p.lds_bytes);
-  if (e != hipSuccess) return e;
-  k<<<grid, NW * 64, p.lds_bytes, s>>>(d, a, p);
+  hipError_t e;
+  if (L.two) {
+    auto k = linear_stream2_kernel<WT, NW, NR, P, CH, MT>;
+    if ((e = allow_lds(k, L.lds())) != hipSuccess) return e;
+    k<<<L.grid(), NW * 64, L.lds(), s>>>(*L.d[0], *L.a[0], *L.p[0], *L.d[1], *L.a[1], *L.p[1]);
+  } else {
+    auto k = linear_stream_kernel<WT, NW, NR, P, CH, MT>;
+    if ((e = allow_lds(k, L.lds())) != hipSuccess) return e;
+    k<<<L.grid(), NW * 64, L.lds(), s>>>(*L.d[0], *L.a[0], *L.p[0]);
+  }
   return hipGetLastError();
 }
 
 // single row tile and m-tile per wave: X'p contiguous (gathered beforehand when needed)
 template <typename WT, int NW, int P>
-hipError_t launch_stream_t(const LayerDesc& d, const LinearArgs& a, const LinearPlan& p, hipStream_t s) {
-  if (a.gather) return hipErrorInvalidValue;
-  return launch_stream_k<WT, NW, 1, P, kStreamChunk, 1>(d, a, p, s);
+hipError_t launch_stream_t(const Launch& L, hipStream_t s) {
+  if (L.a[0]->gather) return hipErrorInvalidValue;
+  return launch_stream_k<WT, NW, 1, P, kStreamChunk, 1>(L, s);
 }
 
-// blocked tiles (table kTilePresets): X'p contiguous, gathered beforehand when needed
+// blocked tiles (SPENSE_TILE_PRESETS): X'p contiguous, gathered beforehand when needed
 template <typename WT>
-hipError_t launch_stream_preset(const LayerDesc& d, const LinearArgs& a, const LinearPlan& p, hipStream_t s) {
-  if (a.gather) return hipErrorInvalidValue;
-  switch (p.preset) {
+hipError_t launch_stream_preset(const Launch& L, hipStream_t s) {
+  if (L.a[0]->gather) return hipErrorInvalidValue;
+  switch (L.p[0]->preset) {
 #define SPENSE_PRESET(i, nw, nr, pp, ch, mt) \
-  case i: return launch_stream_k<WT, nw, nr, pp, ch, mt>(d, a, p, s);
+  case i: return launch_stream_k<WT, nw, nr, pp, ch, mt>(L, s);
     SPENSE_TILE_PRESETS(SPENSE_PRESET)
 #undef SPENSE_PRESET
     default: return hipErrorInvalidValue;
@@ -924,22 +1003,29 @@ hipError_t launch_stream_preset(const LayerDesc& d, const LinearArgs& a, const L
 }
 
 template <typename WT>
-hipError_t launch_linear_units(const LayerDesc& d, const LinearArgs& a, const LinearPlan& p, hipStream_t s) {
-  if (p.chunked && p.preset >= 0) return launch_stream_preset<WT>(d, a, p, s);
+hipError_t launch_linear_units(const Launch& L, hipStream_t s) {
+  const LinearPlan& p = *L.p[0];
+  if (L.two) {  // both layers must run the same kernel shape
+    const LinearPlan& q = *L.p[1];
+    if (q.chunked != p.chunked || q.preset != p.preset || q.waves != p.waves || q.depth != p.depth ||
+        q.nr != p.nr || q.mt != p.mt || q.chunk != p.chunk || L.a[1]->gather != L.a[0]->gather)
+      return hipErrorInvalidValue;
+  }
+  if (p.chunked && p.preset >= 0) return launch_stream_preset<WT>(L, s);
   if (p.chunked) {
     switch (p.waves * 100 + p.depth) {
-      case 404: return launch_stream_t<WT, 4, 4>(d, a, p, s);
-      case 408: return launch_stream_t<WT, 4, 8>(d, a, p, s);
-      case 804: return launch_stream_t<WT, 8, 4>(d, a, p, s);
-      case 808: return launch_stream_t<WT, 8, 8>(d, a, p, s);
+      case 404: return launch_stream_t<WT, 4, 4>(L, s);
+      case 408: return launch_stream_t<WT, 4, 8>(L, s);
+      case 804: return launch_stream_t<WT, 8, 4>(L, s);
+      case 808: return launch_stream_t<WT, 8, 8>(L, s);
       default: return hipErrorInvalidValue;
     }
   }
   switch (p.waves * 100 + p.depth) {
-    case 404: return launch_decode_t<WT, 4, 4>(d, a, p, s);
-    case 408: return launch_decode_t<WT, 4, 8>(d, a, p, s);
-    case 804: return launch_decode_t<WT, 8, 4>(d, a, p, s);
-    case 808: return launch_decode_t<WT, 8, 8>(d, a, p, s);
+    case 404: return launch_decode_t<WT, 4, 4>(L, s);
+    case 408: return launch_decode_t<WT, 4, 8>(L, s);
+    case 804: return launch_decode_t<WT, 8, 4>(L, s);
+    case 808: return launch_decode_t<WT, 8, 8>(L, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -986,12 +1072,24 @@ hipError_t launch_export(const LayerDesc& d, void* vals, uint32_t* meta, uint8_t
 }
 
 hipError_t launch_linear(const LayerDesc& d, const LinearArgs& a, const LinearPlan& p, hipStream_t s) {
+  const Launch L{{&d, nullptr}, {&a, nullptr}, {&p, nullptr}, false};
   switch (d.wdtype) {
-    case DT_FP8: return launch_linear_units<uint8_t>(d, a, p, s);
-    case DT_BF16: return launch_linear_units<uint16_t>(d, a, p, s);
+    case DT_FP8: return launch_linear_units<uint8_t>(L, s);
+    case DT_BF16: return launch_linear_units<uint16_t>(L, s);
     case DT_F32:
       linear_f32_kernel<<<blocks_for(d.N, 4), 256, 0, s>>>(d, a);
       return hipGetLastError();
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_linear2(const LayerDesc& d0, const LinearArgs& a0, const LinearPlan& p0, const LayerDesc& d1,
+                          const LinearArgs& a1, const LinearPlan& p1, hipStream_t s) {
+  if (d0.wdtype != d1.wdtype) return hipErrorInvalidValue;
+  const Launch L{{&d0, &d1}, {&a0, &a1}, {&p0, &p1}, true};
+  switch (d0.wdtype) {
+    case DT_FP8: return launch_linear_units<uint8_t>(L, s);
+    case DT_BF16: return launch_linear_units<uint16_t>(L, s);
     default: return hipErrorInvalidValue;
   }
 }

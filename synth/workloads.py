@@ -27,6 +27,8 @@ class LayerSpec:
     xdtype: int
     dense: str  # "tail" or "random"
     layer_index: int = 0
+    form: str = "input"  # "input": dense columns (K_d of them); "output": dense rows (N_d of them), K_d = 0
+    N_d: int = 0
 
 
 @dataclass
@@ -62,6 +64,10 @@ def _build():
     w["gateup_fp8"] = Workload(
         "gateup_fp8", "32B-class FFN gate/up W[25600,5120] e4m3, dense tail 1280, M in {1,4,16}",
         [LayerSpec("gateup", 25600, 5120, 1280, DT_FP8, DT_BF16, "tail")], (1, 4, 16))
+    w["gateup_fp8_rows"] = Workload(
+        "gateup_fp8_rows", "32B-class FFN gate/up W[25600,5120] e4m3, output-split with the last 6400 rows dense, "
+        "M in {1,4,16}",
+        [LayerSpec("gateup_rows", 25600, 5120, 0, DT_FP8, DT_BF16, "tail", form="output", N_d=6400)], (1, 4, 16))
     w["down_fp8"] = Workload(
         "down_fp8", "32B-class FFN down W[5120,25600] e4m3, 6400 random dense columns, M in {1,8,32,64}",
         [LayerSpec("down", 5120, 25600, 6400, DT_FP8, DT_BF16, "random")], (1, 8, 32, 64))

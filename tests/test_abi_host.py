@@ -36,7 +36,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_strerror():
-    assert sdg.spense_abi_version() == 1
+    assert sdg.spense_abi_version() == 2
     lib = sdg._lib()
     for code in (0, -1, -2, -3, -4):
         assert lib.spense_strerror(code)
@@ -72,12 +72,42 @@ def test_pack_rejects_bad_arguments(kw):
     assert st == sdg.SPENSE_EINVAL and not h
 
 
+def _pack_rows(W=FAKE_PTR, wdt=sdg.DT_FP8, N=64, K=128, ldw=None, scales=FAKE_PTR, rows=None, frac=0.25):
+    lib = sdg._lib()
+    h = ctypes.c_void_p()
+    rows_ptr, n = None, 0
+    keep = None
+    if rows is not None:
+        keep = np.ascontiguousarray(np.asarray(rows, dtype=np.int32))
+        rows_ptr, n = (keep.ctypes.data if keep.size else np.zeros(1, np.int32).ctypes.data), keep.size
+    st = lib.spense_pack_rows(W, wdt, N, K, K if ldw is None else ldw, scales, rows_ptr, n, frac, None,
+                              ctypes.byref(h))
+    return st, h.value
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(W=None), sdg.SPENSE_EINVAL),
+    (dict(wdt=7), sdg.SPENSE_EINVAL),
+    (dict(N=0), sdg.SPENSE_EINVAL), (dict(K=0), sdg.SPENSE_EINVAL), (dict(ldw=100), sdg.SPENSE_EINVAL),
+    (dict(scales=None), sdg.SPENSE_EINVAL),
+    (dict(frac=1.5), sdg.SPENSE_EINVAL), (dict(frac=float("nan")), sdg.SPENSE_EINVAL),
+    (dict(K=130, frac=0.5), sdg.SPENSE_EINVAL),      # sparse rows need K % 4 == 0
+    (dict(rows=[3, 3]), sdg.SPENSE_EINVAL),          # duplicate row
+    (dict(rows=[64]), sdg.SPENSE_EINVAL), (dict(rows=[-1]), sdg.SPENSE_EINVAL),
+    (dict(wdt=sdg.DT_F32, scales=None), sdg.SPENSE_EUNSUPPORTED),  # no fp32 output-split
+])
+def test_pack_rows_rejects_bad_arguments(kw, want):
+    st, h = _pack_rows(**kw)
+    assert st == want and not h
+
+
 def test_linear_rejects_bad_arguments():
     lib = sdg._lib()
     assert lib.spense_linear(None, FAKE_PTR, sdg.DT_BF16, 1, 128, FAKE_PTR, sdg.DT_F32, 64, None) == sdg.SPENSE_EINVAL
     assert lib.spense_free(None) == sdg.SPENSE_EINVAL
     assert lib.spense_info(None, None) == sdg.SPENSE_EINVAL
     assert lib.spense_export(None, None, None, None, None, None, None) == sdg.SPENSE_EINVAL
+    assert lib.spense_export_rows(None, None, None, None, None, None, None) == sdg.SPENSE_EINVAL
 
 
 def test_binding_fails_loudly_without_library(monkeypatch):
