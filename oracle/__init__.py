@@ -22,6 +22,10 @@ written from the definitions on the pages:
     output rows instead (dense rows, and rows that are 2:4 along K), with no
     accumulation across the parts; the page uses it for the GLU gate and up
     projections (``resolve_dense_rows``, ``pack_rows``, ``linear_rows_ref``).
+  * same page, Technical Summary 2.A with 2.B: the GLU block runs gate and up
+    output-split and down input-split over one dense set of intermediate
+    indices (``glu_block_ref``; SiLU gate, as in the GLU models the page
+    evaluates).
   * same page, Technical Summary 1 "Problem Statement" (and the SlideSparse
     explainer's Technical summary 1): 2:4 means at most two nonzeros in every
     four consecutive weights.
@@ -41,6 +45,8 @@ from .spense import (  # noqa: F401
     decode_values,
     decompress,
     dense_linear_ref,
+    down_ref,
+    glu_block_ref,
     linear_ref,
     linear_rows_ref,
     magnitude_key,
@@ -48,6 +54,7 @@ from .spense import (  # noqa: F401
     pack_rows,
     resolve_dense_rows,
     resolve_dense_set,
+    silu,
     unpack_bits,
     unpack_rows_bits,
 )

@@ -348,3 +348,54 @@ def linear_rows_ref(X_bits: np.ndarray, xdtype: int, p: PackedRows, scales=None)
         Y = Y * s[None, :]
         B = B * s[None, :]
     return Y, B
+
+
+# ---------------------------------------------------------------------------
+# GLU MLP block (Technical Summary 2.A: output-split for the gate and up
+# projections, input-split for the down projection; Technical Summary 2.B:
+# the dense intermediate indices can be permuted into one contiguous block
+# without changing the block's output).  The gate nonlinearity is SiLU, as in
+# the GLU models the page evaluates; the page does not name it.
+# ---------------------------------------------------------------------------
+def silu(x: np.ndarray) -> np.ndarray:
+    """x * sigmoid(x) in float64."""
+    x = np.asarray(x, dtype=np.float64)
+    with np.errstate(over="ignore"):  # exp(-x) = inf for x << 0 gives the limit -0
+        return x / (1.0 + np.exp(-x))
+
+
+def glu_block_ref(X_bits: np.ndarray, xdtype: int, Wg_bits, Wu_bits, Wd_bits, dtype: int, dense_idx,
+                  s_g=None, s_u=None, s_d=None):
+    """Exact block output in float64.
+
+    D = dense_idx, a set of intermediate indices: rows D of W_gate and W_up
+    stay dense (output-split), columns D of W_down stay dense (input-split);
+    every other gate/up row is 2:4 along the hidden dimension and every other
+    down column group is 2:4 along the intermediate dimension in the order
+    [non-dense ascending | dense ascending].
+        G = X W_gate'^T (s_g), U = X W_up'^T (s_u), A = silu(G) * U,
+        Y = A W_down'^T (s_d)
+    Returns dict(G, U, A, Y, B_G, B_U, B_Y) with B_* = the |x||w| error scales
+    (B_Y taken over A).
+    """
+    I = Wg_bits.shape[0]
+    rho, I_s, _ = resolve_dense_rows(I, Wg_bits.shape[1], dense_rows=dense_idx)
+    G, B_G = linear_rows_ref(X_bits, xdtype, pack_rows(Wg_bits, dtype, rho, I_s), s_g)
+    U, B_U = linear_rows_ref(X_bits, xdtype, pack_rows(Wu_bits, dtype, rho, I_s), s_u)
+    A = silu(G) * U
+    pi, K_s, _ = resolve_dense_set(I, dense_cols=dense_idx)
+    Y, B_Y = down_ref(A, pack(Wd_bits, dtype, pi, K_s), s_d)
+    return dict(G=G, U=U, A=A, Y=Y, B_G=B_G, B_U=B_U, B_Y=B_Y, rho=rho, I_s=I_s)
+
+
+def down_ref(A: np.ndarray, p: Packed, scales=None):
+    """The down projection on float64 intermediate values A [M, I] (natural index order)."""
+    Wp = decompress(p)
+    A = np.asarray(A, dtype=np.float64)
+    Y = A @ Wp.T
+    B = np.abs(A) @ np.abs(Wp).T
+    if scales is not None:
+        s = np.asarray(scales, dtype=np.float32).astype(np.float64)
+        Y = Y * s[None, :]
+        B = B * s[None, :]
+    return Y, B

@@ -489,3 +489,67 @@ def test_rows_pack_round_trip():
     assert np.array_equal(U[sp][U[sp] != 0], W[sp][U[sp] != 0])
     p2 = oracle.pack_rows(U, DT_BF16, rho, N_s)
     assert np.array_equal(p2.sparse.vals, p.sparse.vals) and np.array_equal(p2.sparse.meta, p.sparse.meta)
+
+
+# --------------------------------------------------------------------------
+# GLU block (gate/up output-split, SiLU * up, down input-split)
+# --------------------------------------------------------------------------
+def test_silu_matches_torch():
+    x = np.concatenate([np.linspace(-60, 60, 2001), [-1e3, -80.0, 0.0, 1e-30, 80.0, 1e3]])
+    ref = torch.nn.functional.silu(torch.from_numpy(x)).numpy()
+    assert np.allclose(oracle.silu(x), ref, rtol=1e-15, atol=1e-300)
+
+
+def _glu_weights(H, I, dtype, seed):
+    rng = np.random.default_rng(seed)
+    Wg, sg = synth.make_weight(I, H, dtype, rng)
+    Wu, su = synth.make_weight(I, H, dtype, rng)
+    Wd, sd = synth.make_weight(H, I, dtype, rng)
+    X = synth.make_x(3, H, DT_BF16, rng)
+    return X, Wg, sg, Wu, su, Wd, sd
+
+
+def _torch_block(X, Wg, Wu, Wd, dtype, sg, su, sd):
+    def w(Wb, s):
+        t = torch.from_numpy(oracle.decode_values(Wb, dtype) if Wb.dtype != np.float64 else Wb)
+        return t * torch.from_numpy(s.astype(np.float64))[:, None] if s is not None else t
+    x = torch.from_numpy(oracle.decode_values(X, DT_BF16))
+    g = torch.nn.functional.linear(x, w(Wg, sg))
+    u = torch.nn.functional.linear(x, w(Wu, su))
+    a = torch.nn.functional.silu(g) * u
+    return torch.nn.functional.linear(a, w(Wd, sd)).numpy()
+
+
+@pytest.mark.parametrize("dtype", [DT_BF16, DT_FP8])
+def test_glu_all_dense_is_textbook_block(dtype):
+    H, I = 64, 96
+    X, Wg, sg, Wu, su, Wd, sd = _glu_weights(H, I, dtype, 51)
+    r = oracle.glu_block_ref(X, DT_BF16, Wg, Wu, Wd, dtype, np.arange(I), sg, su, sd)
+    ref = _torch_block(X, Wg, Wu, Wd, dtype, sg, su, sd)
+    assert np.all(np.abs(r["Y"] - ref) <= 1e-12 * np.abs(ref).max() + 1e-300)
+
+
+def test_glu_no_dense_index_is_pure_two_four_block():
+    H, I, dtype = 32, 48, DT_FP8
+    X, Wg, sg, Wu, su, Wd, sd = _glu_weights(H, I, dtype, 52)
+    r = oracle.glu_block_ref(X, DT_BF16, Wg, Wu, Wd, dtype, [], sg, su, sd)
+
+    def pruned(Wb, K):
+        keys = oracle.magnitude_key(Wb, dtype).tolist()
+        return np.array(prune_python(oracle.decode_values(Wb, dtype).tolist(), keys, np.arange(K), K))
+    ref = _torch_block(X, pruned(Wg, H), pruned(Wu, H), pruned(Wd, I), dtype, sg, su, sd)
+    assert np.all(np.abs(r["Y"] - ref) <= 1e-12 * np.abs(ref).max() + 1e-300)
+
+
+def test_glu_permuted_block_equals_original():
+    """Moving the chosen intermediate indices into a contiguous tail (gate/up
+    rows and down columns permuted by rho) leaves the block output unchanged."""
+    H, I, dtype = 64, 80, DT_FP8
+    X, Wg, sg, Wu, su, Wd, sd = _glu_weights(H, I, dtype, 53)
+    D = synth.random_dense_set(I, 20, 54)
+    r1 = oracle.glu_block_ref(X, DT_BF16, Wg, Wu, Wd, dtype, D, sg, su, sd)
+    rho = r1["rho"]
+    tail = np.arange(I - len(D), I)
+    r2 = oracle.glu_block_ref(X, DT_BF16, Wg[rho], Wu[rho], Wd[:, rho], dtype, tail, sg[rho], su[rho], sd)
+    assert np.allclose(r2["A"], r1["A"][:, rho], rtol=0, atol=0)
+    assert np.all(np.abs(r1["Y"] - r2["Y"]) <= 1e-12 * r1["B_Y"] + 1e-300)
