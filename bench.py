@@ -12,6 +12,10 @@ Other workloads (``--workload``):
   gateup_fp8_rows  the gate/up layer in output-split form: the last 25% of the rows
                  dense, the others 2:4 along K, M in {1, 4, 16}
   down_fp8       FFN down W[5120, 25600] e4m3, 6400 chosen dense columns, M in {1, 8, 32, 64}
+  glu32b_fp8     the whole GLU MLP block (H = 5120, I = 25600, e4m3): gate/up output-split and
+                 down input-split over 6400 chosen dense intermediate indices, permuted into a
+                 contiguous block at pack time; one step = one spense_glu call per batch size
+                 (two launches), against the all-dense block through the same path
   layer32b_fp8   32B-class decoder linear set (QKV, O, gate+up, down), e4m3, dense
                  tail fraction in {0, 12.5, 25, 50}%, M = 32; one step = the four
                  layers of every fraction
@@ -55,6 +59,7 @@ SETS = {
     "gateup_fp8": ["gateup_fp8"],
     "gateup_fp8_rows": ["gateup_fp8_rows"],
     "down_fp8": ["down_fp8"],
+    "glu32b_fp8": ["glu32b_fp8"],
     "layer32b_fp8": ["layer32b_fp8_d0", "layer32b_fp8_d12p5", "layer32b_fp8_d25", "layer32b_fp8_d50"],
     "layer36b_fp8": ["layer36b_fp8"],
     "layer36b_bf16": ["layer36b_bf16"],
@@ -168,6 +173,8 @@ def main():
 
     variants = SETS[args.workload]
     wls = [synth.WORKLOADS[v] for v in variants]
+    if wls[0].extra.get("glu"):
+        return run_glu(args, torch, sdg, synth, wls[0])
     Ms = tuple(int(m) for m in args.ms.split(",")) if args.ms else wls[0].Ms
     Mmax = max(Ms)
     dev = torch.device("cuda:0")
@@ -335,6 +342,113 @@ def main():
         out["per_layer_us"] = per_layer
     if variants_out:
         out["variants"] = variants_out
+    print(json.dumps(out))
+
+
+def run_glu(args, torch, sdg, synth, wl):
+    """The GLU block workload: spense_glu per batch size, all-dense block as the baseline."""
+    import oracle
+
+    gu, dn = wl.layers
+    H, I = dn.N, dn.K
+    Ms = tuple(int(m) for m in args.ms.split(",")) if args.ms else wl.Ms
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    t0 = time.time()
+    Wgu, sgu, X, _ = synth.layer_inputs(gu, max(Ms))
+    Wd, sd, _, D = synth.layer_inputs(dn, max(Ms))
+    gen_s = time.time() - t0
+    Wgu_d, Wd_d = torch.from_numpy(Wgu).to(dev), torch.from_numpy(Wd).to(dev)
+    sgu_d, sd_d = torch.from_numpy(sgu).to(dev), torch.from_numpy(sd).to(dev)
+    Xd = torch.from_numpy(X.view(np.int16)).to(dev).view(torch.bfloat16)
+    A = torch.empty((max(Ms), I), dtype=torch.bfloat16, device=dev)
+    Y = torch.empty((max(Ms), H), dtype=torch.bfloat16, device=dev)
+
+    def pack(**kw):
+        return sdg.spense_pack_glu(Wgu_d, Wd_d, gu.wdtype, H=H, I=I, s_gu=sgu_d, s_down=sd_d, **kw)
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    hs = [pack(dense_idx=D)]
+    pack_ms = (time.perf_counter() - t0) * 1e3
+    info = sdg.spense_info(hs[0])
+    n_copies = max(2, -(-2 * MALL_BYTES // info["device_bytes"]) + 1)
+    hs += [pack(dense_idx=D) for _ in range(n_copies - 1)]
+    hd = [pack(dense_fraction=1.0) for _ in range(n_copies)]
+    wbytes, dbytes = info["weight_bytes"], sdg.spense_info(hd[0])["weight_bytes"]
+    del Wgu_d, Wd_d
+
+    def step(handles, M, i):
+        sdg.spense_glu(handles[i % len(handles)], Xd[:M], A[:M], Y[:M], stream=stream)
+
+    for M in Ms:
+        for h in hs + hd:
+            step([h], M, 0)
+    for i in range(args.warmup):
+        for M in Ms:
+            step(hs, M, i)
+            step(hd, M, i)
+    torch.cuda.synchronize()
+    ev = {}
+    t_wall = time.perf_counter()
+    for M in Ms:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(args.steps):
+            step(hs, M, i)
+        e1.record(stream)
+        ev[M] = (e0, e1)
+    torch.cuda.synchronize()
+    wall_s = time.perf_counter() - t_wall
+    us = {M: a.elapsed_time(b) * 1e3 / args.steps for M, (a, b) in ev.items()}
+    dev_ = {}
+    for M in Ms:
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(args.steps):
+            step(hd, M, i)
+        e1.record(stream)
+        dev_[M] = (e0, e1)
+    torch.cuda.synchronize()
+    dus = {M: a.elapsed_time(b) * 1e3 / args.steps for M, (a, b) in dev_.items()}
+    for h in hs + hd:
+        sdg.spense_free(h)
+
+    def alg(M):  # weights + scales + X + A written and read + Y (bf16)
+        return wbytes + 4 * (2 * I + H) + 2 * M * H + 2 * 2 * M * I + 2 * M * H
+
+    per_m = {str(M): {"spense_us": round(us[M], 3), "dense_us": round(dus[M], 3),
+                      "speedup_vs_dense": round(dus[M] / us[M], 4),
+                      "weight_GBs": round(wbytes / us[M] / 1e3, 1),
+                      "weight_frac_of_peak": round(wbytes / us[M] / 1e3 / HBM_PEAK_GBS, 4),
+                      "dense_weight_GBs": round(dbytes / dus[M] / 1e3, 1)} for M in Ms}
+    total = sum(us.values())
+    ach = sum(alg(M) for M in Ms) / total / 1e3
+    cpu = None
+    if not args.no_cpu_baseline:
+        rows, M0 = 256, min(Ms)
+        t0 = time.perf_counter()
+        oracle.glu_block_ref(X[:M0], oracle.DT_BF16, Wgu[:rows], Wgu[I:I + rows], Wd[:, :rows], gu.wdtype,
+                             np.arange(rows - rows // 4, rows), sgu[:rows], sgu[I:I + rows], sd)
+        dt = time.perf_counter() - t0
+        nbytes = wbytes * rows / I
+        cpu = {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": os.cpu_count() or 1, "kind": "oracle",
+               "sample": f"block restricted to the first {rows} intermediate indices (last quarter dense), "
+                         f"M={M0} ({dt:.2f} s)"}
+    out = {
+        "metric": METRIC, "value": round(len(Ms) * wbytes / total / 1e3, 1), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(wall_s * 1e3 / args.steps, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "e4m3 weights x bf16 activations, fp32 accumulate", "data": "synthetic",
+        "config": {"workload": wl.title, "key": wl.key, "Ms": list(Ms), "H": H, "I": I, "I_d": int(len(D)),
+                   "weight_copies": n_copies},
+        "per_m": per_m, "speedup_vs_dense": round(sum(dus.values()) / total, 4),
+        "spense_weight_bytes": wbytes, "dense_weight_bytes": dbytes, "pack_ms_wall": round(pack_ms, 3),
+        "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None},
+        "cpu_baseline": cpu, "input_gen_s": round(gen_s, 2),
+    }
     print(json.dumps(out))
 
 

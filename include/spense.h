@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define SPENSE_ABI_VERSION 2
+#define SPENSE_ABI_VERSION 3
 
 /* Element types.  The numbering is fixed. */
 typedef enum spense_dtype {
@@ -70,9 +70,12 @@ typedef struct spense_layer_info {
   int64_t weight_bytes;   /* bytes the method must stream per call: kept values + 2-bit indices
                              + dense block = N*(K_s/2*b + K_s/8 + K_d*b), b = element bytes */
   int64_t device_bytes;   /* bytes of the device-resident packed form, padding included */
-  int32_t split;          /* 0: input-split layer (spense_pack); 1: output-split (spense_pack_rows) */
+  int32_t split;          /* 0: input-split layer (spense_pack); 1: output-split (spense_pack_rows);
+                             2: GLU block (spense_pack_glu) */
   int64_t N_s, N_d;       /* output-split: 2:4 rows / dense rows (input-split: N and 0); for an
-                             output-split layer K_s = K when N_s > 0 and K_d = K when N_d > 0 */
+                             output-split layer K_s = K when N_s > 0 and K_d = K when N_d > 0.
+                             GLU block: N = K = H, N_s / N_d = 2:4 / dense intermediate indices,
+                             K_s / K_d those of the down projection */
 } spense_layer_info;
 
 /*
@@ -130,6 +133,53 @@ int spense_pack(const void* W, int32_t wdtype, int64_t N, int64_t K, int64_t ldw
 int spense_pack_rows(const void* W, int32_t wdtype, int64_t N, int64_t K, int64_t ldw, const float* scales,
                      const int32_t* dense_rows, int64_t n_dense, double dense_fraction, void* stream,
                      spense_handle* out);
+
+/*
+ * spense_pack_glu - build a GLU MLP block (once per block).
+ *
+ * Technical Summary 2.A and 2.B of the SpenseGPT explainer: in a GLU MLP the
+ * gate and up projections are output-split and the down projection is
+ * input-split, over one dense set D of intermediate indices (rows D of gate
+ * and up, columns D of down keep all their weights); permuting the
+ * intermediate indices so that D becomes one contiguous block leaves the
+ * block's output unchanged.  That permutation rho = [other indices ascending
+ * | D ascending] is applied here at pack time, so spense_glu gathers nothing.
+ * Gate/up rows outside D are 2:4 along the hidden dimension; down columns
+ * outside D are 2:4 in groups of four consecutive indices of rho (same
+ * magnitude rule and tie-break as spense_pack).  The gate nonlinearity is
+ * SiLU (the pages do not name it; the GLU models they evaluate use it).
+ *
+ *   W_gu       device pointer, [2I, ld_gu] elements: rows [0, I) the gate
+ *              projection, rows [I, 2I) the up projection, each [I, H].
+ *   W_down     device pointer, [H, ld_down] elements: the down projection [H, I].
+ *   wdtype     SPENSE_BF16 or SPENSE_FP8_E4M3 (SPENSE_EUNSUPPORTED for SPENSE_F32).
+ *   H, I       hidden and intermediate sizes; ld_gu >= H, ld_down >= I.
+ *   s_gu, s_down  device pointers, [2I] and [H] float32 per-row scales; required
+ *              iff wdtype == SPENSE_FP8_E4M3, NULL otherwise.
+ *   dense_idx  host pointer to n_dense distinct intermediate indices in [0, I), or
+ *              NULL for the last round(dense_fraction*I) indices.
+ * I - |D| must be a multiple of 4, and so must H when I - |D| > 0
+ * (SPENSE_EINVAL otherwise).  Synchronises `stream` before returning.
+ */
+int spense_pack_glu(const void* W_gu, const void* W_down, int32_t wdtype, int64_t H, int64_t I, int64_t ld_gu,
+                    int64_t ld_down, const float* s_gu, const float* s_down, const int32_t* dense_idx,
+                    int64_t n_dense, double dense_fraction, void* stream, spense_handle* out);
+
+/*
+ * spense_glu - Y = down(silu(gate(X)) * up(X)), the GLU block forward.
+ *
+ *   X     device pointer, [M, ldx] bf16, ldx >= H.
+ *   A     device pointer, [M, lda] bf16, lda >= I: caller-owned workspace for the
+ *         intermediate silu(gate) * up, written in rho order (column j holds
+ *         intermediate index rho[j]; rho from spense_info's split layout:
+ *         the 2:4 indices ascending, then the dense ones ascending).
+ *   Y     device pointer, [M, ldy] elements of ydtype (SPENSE_F32 or SPENSE_BF16), ldy >= H.
+ * Two launches on `stream`: gate and up (both row classes in one grid, the
+ * SiLU * up product in its epilogue, rounded to bf16 into A), then down.
+ * Workspaces grow as for spense_linear.
+ */
+int spense_glu(spense_handle h, const void* X, int64_t M, int64_t ldx, void* A, int64_t lda, void* Y,
+               int32_t ydtype, int64_t ldy, void* stream);
 
 /*
  * spense_linear - Y = X . W_pruned^T (times the per-channel scales), the layer forward.

@@ -64,6 +64,10 @@ def _lib():
     lib.spense_pack_rows.restype = ctypes.c_int
     lib.spense_export_rows.argtypes = [vp, vp, vp, vp, vp, vp, vp]
     lib.spense_export_rows.restype = ctypes.c_int
+    lib.spense_pack_glu.argtypes = [vp, vp, i32, i64, i64, i64, i64, vp, vp, vp, i64, f64, vp, ctypes.POINTER(vp)]
+    lib.spense_pack_glu.restype = ctypes.c_int
+    lib.spense_glu.argtypes = [vp, vp, i64, i64, vp, i64, vp, i32, i64, vp]
+    lib.spense_glu.restype = ctypes.c_int
     lib.spense_linear.argtypes = [vp, vp, i32, i64, i64, vp, i32, i64, vp]
     lib.spense_linear.restype = ctypes.c_int
     lib.spense_linear_splits.argtypes = [vp, vp, i32, i64, i64, vp, i32, i64, i32, vp]
@@ -179,6 +183,33 @@ def spense_export_rows(h: int, vals=None, meta=None, mask=None, dense=None, stre
                                    _stream(stream))
     _check(st, "spense_export_rows")
     return rho
+
+
+def spense_pack_glu(W_gu, W_down, wdtype: int, *, H: int, I: int, s_gu=None, s_down=None, dense_idx=None,
+                    dense_fraction: float = 0.0, stream=None) -> int:
+    """Pack a GLU block: W_gu = [gate; up] as [2I, H], W_down [H, I]; returns the handle."""
+    idx_ptr, n_dense = None, 0
+    if dense_idx is not None:
+        idx = np.ascontiguousarray(np.asarray(dense_idx, dtype=np.int32).ravel())
+        n_dense = idx.size
+        buf = idx if n_dense else np.zeros(1, dtype=np.int32)
+        idx_ptr = buf.ctypes.data
+    ld_gu = W_gu.stride(0) if hasattr(W_gu, "stride") else H
+    ld_down = W_down.stride(0) if hasattr(W_down, "stride") else I
+    h = ctypes.c_void_p()
+    st = _lib().spense_pack_glu(_ptr(W_gu), _ptr(W_down), wdtype, H, I, ld_gu, ld_down, _ptr(s_gu), _ptr(s_down),
+                                idx_ptr, n_dense, float(dense_fraction), _stream(stream), ctypes.byref(h))
+    _check(st, "spense_pack_glu")
+    return h.value
+
+
+def spense_glu(h: int, X, A, Y, *, M: Optional[int] = None, stream=None) -> None:
+    """GLU block forward: A (bf16 [M, >= I]) receives silu(gate) * up in rho order, Y the block output."""
+    M = X.shape[0] if M is None else M
+    ydtype = dtype_of(Y)
+    st = _lib().spense_glu(h, _ptr(X), M, X.stride(0), _ptr(A), A.stride(0), _ptr(Y), ydtype, Y.stride(0),
+                           _stream(stream))
+    _check(st, "spense_glu")
 
 
 def spense_linear(h: int, X, Y, *, xdtype: Optional[int] = None, ydtype: Optional[int] = None,

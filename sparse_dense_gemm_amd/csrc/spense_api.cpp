@@ -43,8 +43,9 @@ struct spense_layer {
   // output-split layer (Technical Summary 2.A): no packed form of its own;
   // part[0] holds the 2:4 rows (no dense columns), part[1] the dense rows (no
   // sparse columns); either may be absent.  rho_host = [sparse rows | dense rows].
-  int split = 0;
+  int split = 0;  // 0 input-split layer, 1 output-split layer, 2 GLU block
   spense_layer* part[2] = {nullptr, nullptr};
+  spense_layer* down = nullptr;  // GLU block: the down projection (input-split, read in rho order)
   int64_t N_s = 0, N_d = 0;
   std::vector<int32_t> rho_host;
 };
@@ -67,6 +68,7 @@ void release(spense_layer* h) {
   if (!h) return;
   release(h->part[0]);
   release(h->part[1]);
+  release(h->down);
   void* ptrs[] = {h->wpack, h->scales, h->pi,      h->pip, h->vals32, h->meta32,
                   h->dense32, h->ws,   h->counters, h->xws, h->ycol,   h->wrow};
   for (void* p : ptrs)
@@ -327,6 +329,87 @@ int spense_pack_rows(const void* W, int32_t wdtype, int64_t N, int64_t K, int64_
   return SPENSE_OK;
 }
 
+int spense_pack_glu(const void* W_gu, const void* W_down, int32_t wdtype, int64_t H, int64_t I, int64_t ld_gu,
+                    int64_t ld_down, const float* s_gu, const float* s_down, const int32_t* dense_idx, int64_t n_dense,
+                    double dense_fraction, void* stream, spense_handle* out) {
+  // ---- validation (host only) ----
+  if (!out) return SPENSE_EINVAL;
+  *out = nullptr;
+  if (!W_gu || !W_down || !valid_dtype(wdtype)) return SPENSE_EINVAL;
+  if (wdtype == SPENSE_F32) return SPENSE_EUNSUPPORTED;
+  if (H < 1 || I < 1 || ld_gu < H || ld_down < I) return SPENSE_EINVAL;
+  if (H > (int64_t(1) << 30) || I > (int64_t(1) << 30) || 2 * I * ld_gu > (int64_t(1) << 40) ||
+      H * ld_down > (int64_t(1) << 40))
+    return SPENSE_EINVAL;
+  const bool fp8 = wdtype == SPENSE_FP8_E4M3;
+  if (fp8 != (s_gu != nullptr) || fp8 != (s_down != nullptr)) return SPENSE_EINVAL;
+  // one dense set of intermediate indices: gate/up rows and down columns
+  std::vector<int32_t> rho;
+  int64_t I_s = 0, I_d = 0;
+  int rc = resolve_dense_set(I, dense_idx, n_dense, dense_fraction, rho, I_s, I_d);
+  if (rc != SPENSE_OK) return rc;
+  if (I_s > 0 && H % 4 != 0) return SPENSE_EINVAL;
+
+  spense_layer* h = new (std::nothrow) spense_layer();
+  if (!h) return SPENSE_ENOMEM;
+  h->split = 2;
+  h->N_s = I_s;
+  h->N_d = I_d;
+  h->rho_host = rho;
+  h->d.N = H;
+  h->d.K = H;
+  h->d.wdtype = wdtype;
+  (void)hipGetDevice(&h->device);
+  hipStream_t s = (hipStream_t)stream;
+  // Gate/up: intermediate index i contributes W_gu rows i (gate) and I + i
+  // (up), packed next to each other so that one lane holds both results; the
+  // pair writes column j = position of i in rho of the intermediate.
+  std::vector<int32_t> ident((size_t)H);
+  for (int64_t c = 0; c < H; ++c) ident[(size_t)c] = (int32_t)c;
+  for (int part = 0; part < 2; ++part) {
+    const int64_t n = part == 0 ? I_s : I_d, j0 = part == 0 ? 0 : I_s;
+    if (n == 0) continue;
+    std::vector<int32_t> wrow((size_t)(2 * n)), ycol((size_t)(2 * n));
+    for (int64_t j = 0; j < n; ++j) {
+      const int32_t i = rho[(size_t)(j0 + j)];
+      wrow[(size_t)(2 * j)] = i;
+      wrow[(size_t)(2 * j + 1)] = (int32_t)(I + i);
+      ycol[(size_t)(2 * j)] = (int32_t)(j0 + j);
+      ycol[(size_t)(2 * j + 1)] = -1;
+    }
+    rc = build_layer(W_gu, wdtype, 2 * n, H, ld_gu, s_gu, wrow, ident, part == 0 ? H : 0, part == 0 ? 0 : H, ycol, s,
+                     &h->part[part]);
+    if (rc != SPENSE_OK) {
+      release(h);
+      return rc;
+    }
+    h->weight_bytes += h->part[part]->weight_bytes;
+    h->device_bytes += h->part[part]->device_bytes;
+  }
+  // Down: packed through rho (its dense columns become the contiguous tail),
+  // then read with the identity map, since the intermediate is already
+  // written in rho order: no runtime gather.
+  rc = build_layer(W_down, wdtype, H, I, ld_down, s_down, {}, rho, I_s, I_d, {}, s, &h->down);
+  if (rc != SPENSE_OK) {
+    release(h);
+    return rc;
+  }
+  LayerDesc& dd = h->down->d;
+  std::vector<int32_t> pipI((size_t)dd.K_p, -1);
+  for (int64_t j = 0; j < I_s; ++j) pipI[(size_t)j] = (int32_t)j;
+  for (int64_t j = 0; j < I_d; ++j) pipI[(size_t)(dd.K_sp + j)] = (int32_t)(I_s + j);
+  dd.gather = (I_s % kMacro == 0 && I_d % kMacro == 0) ? 0 : 1;
+  hipError_t e = hipMemcpy(h->down->pip, pipI.data(), (size_t)dd.K_p * 4, hipMemcpyHostToDevice);
+  if (e != hipSuccess) {
+    release(h);
+    return hip_fail(e);
+  }
+  h->weight_bytes += h->down->weight_bytes;
+  h->device_bytes += h->down->device_bytes;
+  *out = h;
+  return SPENSE_OK;
+}
+
 // Optional tuning override "waves,depth[,chunked]" (e.g. "8,4,1") for the decode kernels.
 static bool decode_override(int& waves, int& depth, int& chunked) {
   const char* e = std::getenv("SPENSE_DECODE");
@@ -506,46 +589,15 @@ static int prepare_call(spense_layer* h, int64_t M, const LinearPlan& p, LinearA
   return SPENSE_OK;
 }
 
-int spense_linear_splits(spense_handle h, const void* X, int32_t xdtype, int64_t M, int64_t ldx, void* Y,
-                         int32_t ydtype, int64_t ldy, int32_t splits, void* stream) {
-  if (!h || !X || !Y) return SPENSE_EINVAL;
-  const LayerDesc& d = h->d;
-  if (M < 1 || M > (int64_t(1) << 24) || ldx < d.K || ldy < d.N) return SPENSE_EINVAL;
-  if (!valid_dtype(xdtype) || !valid_dtype(ydtype)) return SPENSE_EINVAL;
-  if (ydtype == SPENSE_FP8_E4M3) return SPENSE_EUNSUPPORTED;
-  const int32_t want_x = d.wdtype == SPENSE_F32 ? SPENSE_F32 : SPENSE_BF16;
-  if (xdtype != want_x) return SPENSE_EUNSUPPORTED;
-  hipStream_t s = (hipStream_t)stream;
-
-  LinearArgs a{};
-  a.X = X;
-  a.M = M;
-  a.ldx = ldx;
-  a.Y = Y;
-  a.ldy = ldy;
-  a.ydtype = ydtype;
-  if (d.wdtype == SPENSE_F32) {
-    if (splits > 1) return SPENSE_EINVAL;
-    a.splits = 1;
-    LinearPlan p{};
-    p.mt = p.mgroups = p.rgroups = p.splits = 1;
-    hipError_t e = launch_linear(d, a, p, s);
-    return e == hipSuccess ? SPENSE_OK : hip_fail(e);
-  }
-  const bool x_aligned = aligned16(X) && (ldx % 8) == 0;
-
-  // the layers of this call: the handle itself, or the row classes of an output-split layer
-  spense_layer* parts[2] = {h, nullptr};
-  int n_parts = 1;
-  if (h->split) {
-    n_parts = 0;
-    for (spense_layer* q : h->part)
-      if (q) parts[n_parts++] = q;
-  }
+// Plans and launches one layer, or the two row classes of an output-split
+// layer in one grid.  `base` carries X, M, Y and the output type.
+static int run_layers(spense_layer* const* parts, int n_parts, int64_t M, int32_t splits, const LinearArgs& base,
+                      hipStream_t s) {
+  const bool x_aligned = aligned16(base.X) && (base.ldx % 8) == 0;
   int64_t NT_fill = 0;
   for (int i = 0; i < n_parts; ++i) NT_fill += parts[i]->d.NT;
   LinearPlan p[2]{};
-  LinearArgs aa[2]{a, a};
+  LinearArgs aa[2]{base, base};
   for (int i = 0; i < n_parts; ++i) {
     aa[i].gather = parts[i]->d.gather || !x_aligned;
     const int rc = plan_linear(parts[i], M, splits, NT_fill, p[i]);
@@ -598,6 +650,84 @@ int spense_linear_splits(spense_handle h, const void* X, int32_t xdtype, int64_t
   return e == hipSuccess ? SPENSE_OK : hip_fail(e);
 }
 
+// the layers one call runs: the handle itself, or the row classes of an output-split layer
+static int layer_parts(spense_layer* h, spense_layer* parts[2]) {
+  if (!h->split) {
+    parts[0] = h;
+    return 1;
+  }
+  int n = 0;
+  for (spense_layer* q : h->part)
+    if (q) parts[n++] = q;
+  return n;
+}
+
+int spense_linear_splits(spense_handle h, const void* X, int32_t xdtype, int64_t M, int64_t ldx, void* Y,
+                         int32_t ydtype, int64_t ldy, int32_t splits, void* stream) {
+  if (!h || !X || !Y) return SPENSE_EINVAL;
+  if (h->split == 2) return SPENSE_EINVAL;  // a GLU block runs through spense_glu
+  const LayerDesc& d = h->d;
+  if (M < 1 || M > (int64_t(1) << 24) || ldx < d.K || ldy < d.N) return SPENSE_EINVAL;
+  if (!valid_dtype(xdtype) || !valid_dtype(ydtype)) return SPENSE_EINVAL;
+  if (ydtype == SPENSE_FP8_E4M3) return SPENSE_EUNSUPPORTED;
+  const int32_t want_x = d.wdtype == SPENSE_F32 ? SPENSE_F32 : SPENSE_BF16;
+  if (xdtype != want_x) return SPENSE_EUNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+
+  LinearArgs a{};
+  a.X = X;
+  a.M = M;
+  a.ldx = ldx;
+  a.Y = Y;
+  a.ldy = ldy;
+  a.ydtype = ydtype;
+  if (d.wdtype == SPENSE_F32) {
+    if (splits > 1) return SPENSE_EINVAL;
+    a.splits = 1;
+    LinearPlan p{};
+    p.mt = p.mgroups = p.rgroups = p.splits = 1;
+    hipError_t e = launch_linear(d, a, p, s);
+    return e == hipSuccess ? SPENSE_OK : hip_fail(e);
+  }
+  spense_layer* parts[2] = {nullptr, nullptr};
+  const int n_parts = layer_parts(h, parts);
+  return run_layers(parts, n_parts, M, splits, a, s);
+}
+
+int spense_glu(spense_handle h, const void* X, int64_t M, int64_t ldx, void* A, int64_t lda, void* Y, int32_t ydtype,
+               int64_t ldy, void* stream) {
+  if (!h || h->split != 2 || !X || !A || !Y) return SPENSE_EINVAL;
+  const int64_t H = h->d.K, I = h->N_s + h->N_d;
+  if (M < 1 || M > (int64_t(1) << 24) || ldx < H || lda < I || ldy < H) return SPENSE_EINVAL;
+  if (ydtype != SPENSE_F32 && ydtype != SPENSE_BF16) return SPENSE_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  // gate/up (output-split) with the SiLU * up epilogue -> A [M, I] bf16, rho order
+  LinearArgs a{};
+  a.X = X;
+  a.M = M;
+  a.ldx = ldx;
+  a.Y = A;
+  a.ldy = lda;
+  a.ydtype = SPENSE_BF16;
+  a.glu = 1;
+  spense_layer* parts[2] = {nullptr, nullptr};
+  int n = 0;
+  for (spense_layer* q : h->part)
+    if (q) parts[n++] = q;
+  int rc = run_layers(parts, n, M, 0, a, s);
+  if (rc != SPENSE_OK) return rc;
+  // down (input-split, dense tail) on A
+  LinearArgs b{};
+  b.X = A;
+  b.M = M;
+  b.ldx = lda;
+  b.Y = Y;
+  b.ldy = ldy;
+  b.ydtype = ydtype;
+  spense_layer* dp[1] = {h->down};
+  return run_layers(dp, 1, M, 0, b, s);
+}
+
 int spense_linear(spense_handle h, const void* X, int32_t xdtype, int64_t M, int64_t ldx, void* Y, int32_t ydtype,
                   int64_t ldy, void* stream) {
   return spense_linear_splits(h, X, xdtype, M, ldx, Y, ydtype, ldy, 0, stream);
@@ -618,12 +748,17 @@ int spense_info(spense_handle h, spense_layer_info* info) {
   info->split = h->split;
   info->N_s = h->split ? h->N_s : h->d.N;
   info->N_d = h->split ? h->N_d : 0;
+  if (h->split == 2) {  // GLU block: K_s / K_d of the down projection, N_s / N_d intermediate indices
+    info->K_s = h->down->d.K_s;
+    info->K_d = h->down->d.K_d;
+    info->gather = 0;
+  }
   return SPENSE_OK;
 }
 
 int spense_export_rows(spense_handle h, void* vals, uint32_t* meta, uint8_t* mask, void* dense, int32_t* rho,
                        void* stream) {
-  if (!h || !h->split) return SPENSE_EINVAL;
+  if (!h || h->split != 1) return SPENSE_EINVAL;
   hipStream_t s = (hipStream_t)stream;
   if (rho) std::memcpy(rho, h->rho_host.data(), (size_t)h->d.N * 4);
   hipError_t e = hipSuccess;

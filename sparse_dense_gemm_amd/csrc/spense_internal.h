@@ -77,6 +77,7 @@ struct LinearArgs {
   int32_t ydtype;
   int32_t splits;
   int32_t gather;        // effective gather mode for this call
+  int32_t glu;           // 1: packed rows come in (gate, up) pairs; write silu(gate) * up at the pair's column
   float* ws;             // [splits][M][NT*16] fp32 partials (splits > 1)
   int32_t* counters;     // [row groups * m groups], zero between calls
 };

@@ -191,10 +191,21 @@ __device__ __forceinline__ void finish_tile(const LayerDesc& d, const LinearArgs
         sum = f32x4{0.f, 0.f, 0.f, 0.f};
         for (int s2 = 0; s2 < S; ++s2) sum += load_partial(a.ws + ((int64_t)s2 * a.M + m) * NP + rt * 16 + nb);
       }
+      if (a.glu) {
+        // rows (q, q+1) of this lane are the gate and up rows of one
+        // intermediate index; the gate row carries its output column
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int col = (int)to[r].col[q];
-        if (col >= 0) store_y(a, m, col, sum[q] * to[r].sc[q]);
+        for (int q = 0; q < 4; q += 2) {
+          const int col = (int)to[r].col[q];
+          const float g = sum[q] * to[r].sc[q], u = sum[q + 1] * to[r].sc[q + 1];
+          if (col >= 0) store_y(a, m, col, g / (1.0f + __expf(-g)) * u);
+        }
+      } else {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = (int)to[r].col[q];
+          if (col >= 0) store_y(a, m, col, sum[q] * to[r].sc[q]);
+        }
       }
     }
   }

@@ -68,6 +68,11 @@ def _build():
         "gateup_fp8_rows", "32B-class FFN gate/up W[25600,5120] e4m3, output-split with the last 6400 rows dense, "
         "M in {1,4,16}",
         [LayerSpec("gateup_rows", 25600, 5120, 0, DT_FP8, DT_BF16, "tail", form="output", N_d=6400)], (1, 4, 16))
+    w["glu32b_fp8"] = Workload(
+        "glu32b_fp8", "32B-class GLU MLP block H=5120, I=25600, e4m3: gate/up output-split and down input-split over "
+        "6400 chosen dense intermediate indices, M in {1,4,16}",
+        [LayerSpec("gate_up", 51200, 5120, 0, DT_FP8, DT_BF16, "tail", 0),
+         LayerSpec("down", 5120, 25600, 6400, DT_FP8, DT_BF16, "random", 1)], (1, 4, 16), extra={"glu": True})
     w["down_fp8"] = Workload(
         "down_fp8", "32B-class FFN down W[5120,25600] e4m3, 6400 random dense columns, M in {1,8,32,64}",
         [LayerSpec("down", 5120, 25600, 6400, DT_FP8, DT_BF16, "random")], (1, 8, 32, 64))

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_strerror():
-    assert sdg.spense_abi_version() == 2
+    assert sdg.spense_abi_version() == 3
     lib = sdg._lib()
     for code in (0, -1, -2, -3, -4):
         assert lib.spense_strerror(code)
@@ -115,3 +115,39 @@ def test_binding_fails_loudly_without_library(monkeypatch):
     monkeypatch.setattr(sdg, "LIB_PATH", "/nonexistent/libspense.so")
     with pytest.raises(RuntimeError, match="not built"):
         sdg.spense_abi_version()
+
+
+def _pack_glu(Wgu=FAKE_PTR, Wd=FAKE_PTR, wdt=sdg.DT_FP8, H=128, I=256, ldgu=None, ldd=None, sgu=FAKE_PTR,
+              sd=FAKE_PTR, idx=None, frac=0.25):
+    lib = sdg._lib()
+    h = ctypes.c_void_p()
+    idx_ptr, n = None, 0
+    keep = None
+    if idx is not None:
+        keep = np.ascontiguousarray(np.asarray(idx, dtype=np.int32))
+        idx_ptr, n = (keep.ctypes.data if keep.size else np.zeros(1, np.int32).ctypes.data), keep.size
+    st = lib.spense_pack_glu(Wgu, Wd, wdt, H, I, H if ldgu is None else ldgu, I if ldd is None else ldd, sgu, sd,
+                             idx_ptr, n, frac, None, ctypes.byref(h))
+    return st, h.value
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(Wgu=None), sdg.SPENSE_EINVAL), (dict(Wd=None), sdg.SPENSE_EINVAL),
+    (dict(wdt=sdg.DT_F32, sgu=None, sd=None), sdg.SPENSE_EUNSUPPORTED),
+    (dict(H=0), sdg.SPENSE_EINVAL), (dict(I=0), sdg.SPENSE_EINVAL),
+    (dict(ldgu=100), sdg.SPENSE_EINVAL), (dict(ldd=200), sdg.SPENSE_EINVAL),
+    (dict(sgu=None), sdg.SPENSE_EINVAL), (dict(sd=None), sdg.SPENSE_EINVAL),
+    (dict(wdt=sdg.DT_BF16), sdg.SPENSE_EINVAL),            # bf16 must not get scales
+    (dict(idx=[1, 2, 3]), sdg.SPENSE_EINVAL),              # I - 3 not a multiple of 4
+    (dict(idx=[5, 5, 6, 7]), sdg.SPENSE_EINVAL),           # duplicate index
+    (dict(H=130, frac=0.5), sdg.SPENSE_EINVAL),            # 2:4 gate/up rows need H % 4 == 0
+    (dict(frac=2.0), sdg.SPENSE_EINVAL),
+])
+def test_pack_glu_rejects_bad_arguments(kw, want):
+    st, h = _pack_glu(**kw)
+    assert st == want and not h
+
+
+def test_glu_rejects_bad_arguments():
+    lib = sdg._lib()
+    assert lib.spense_glu(None, FAKE_PTR, 1, 128, FAKE_PTR, 256, FAKE_PTR, sdg.DT_F32, 128, None) == sdg.SPENSE_EINVAL
