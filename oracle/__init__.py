@@ -26,6 +26,9 @@ written from the definitions on the pages:
     output-split and down input-split over one dense set of intermediate
     indices (``glu_block_ref``; SiLU gate, as in the GLU models the page
     evaluates).
+  * same page, Technical Summary 2.B "SpenseGPT+": a score per intermediate
+    index from |W_ij| * sqrt(H_jj) over gate, up and down, the top-scoring
+    indices kept dense (``glu_scores_ref``, ``select_dense_ref``).
   * same page, Technical Summary 1 "Problem Statement" (and the SlideSparse
     explainer's Technical summary 1): 2:4 means at most two nonzeros in every
     four consecutive weights.
@@ -47,6 +50,8 @@ from .spense import (  # noqa: F401
     dense_linear_ref,
     down_ref,
     glu_block_ref,
+    glu_scores_ref,
+    hessian_diag,
     linear_ref,
     linear_rows_ref,
     magnitude_key,
@@ -54,6 +59,7 @@ from .spense import (  # noqa: F401
     pack_rows,
     resolve_dense_rows,
     resolve_dense_set,
+    select_dense_ref,
     silu,
     unpack_bits,
     unpack_rows_bits,

@@ -399,3 +399,42 @@ def down_ref(A: np.ndarray, p: Packed, scales=None):
         Y = Y * s[None, :]
         B = B * s[None, :]
     return Y, B
+
+
+# ---------------------------------------------------------------------------
+# SpenseGPT+ dense index selection (Technical Summary 2.B): an importance score
+# per intermediate index of a GLU block, aggregated over the gate, up and down
+# projections; each weight scores S_ij = |W_ij| * sqrt(H_jj) (the magnitude of
+# the weight times that of its input), H = X^T X over calibration inputs of
+# that projection.  The top-scoring indices stay dense.  Readings: the
+# aggregation is a plain sum over the weights attached to index i (row i of
+# gate and up, column i of down); |W| is the dequantised magnitude (per-row
+# scale included); ties in the top-k go to the lower index.
+# ---------------------------------------------------------------------------
+def hessian_diag(X_bits: np.ndarray, xdtype: int) -> np.ndarray:
+    """diag(X^T X): the sum over calibration rows of each input column squared (float64)."""
+    X = decode_values(X_bits, xdtype)
+    return np.sum(X * X, axis=0)
+
+
+def glu_scores_ref(X_cal_bits, A_cal_bits, xdtype: int, Wg_bits, Wu_bits, Wd_bits, dtype: int,
+                   s_g=None, s_u=None, s_d=None) -> np.ndarray:
+    """score[i] = sum_j |Wg[i,j]| sqrt(Hx_jj) + sum_j |Wu[i,j]| sqrt(Hx_jj) + sum_n |Wd[n,i]| sqrt(Ha_ii).
+
+    X_cal [T, H]: calibration inputs of gate/up; A_cal [T, I]: calibration
+    inputs of down (the intermediate activations).  Returns float64 [I].
+    """
+    def mag(Wb, s):
+        Wv = np.abs(decode_values(Wb, dtype))
+        if s is not None:
+            Wv = Wv * np.abs(np.asarray(s, dtype=np.float32).astype(np.float64))[:, None]
+        return Wv
+    rx = np.sqrt(hessian_diag(X_cal_bits, xdtype))
+    ra = np.sqrt(hessian_diag(A_cal_bits, xdtype))
+    return mag(Wg_bits, s_g) @ rx + mag(Wu_bits, s_u) @ rx + mag(Wd_bits, s_d).sum(axis=0) * ra
+
+
+def select_dense_ref(score: np.ndarray, k: int) -> np.ndarray:
+    """The k highest scores, ties to the lower index; returned ascending."""
+    order = np.argsort(-np.asarray(score, dtype=np.float64), kind="stable")
+    return np.sort(order[:k])

@@ -553,3 +553,73 @@ def test_glu_permuted_block_equals_original():
     r2 = oracle.glu_block_ref(X, DT_BF16, Wg[rho], Wu[rho], Wd[:, rho], dtype, tail, sg[rho], su[rho], sd)
     assert np.allclose(r2["A"], r1["A"][:, rho], rtol=0, atol=0)
     assert np.all(np.abs(r1["Y"] - r2["Y"]) <= 1e-12 * r1["B_Y"] + 1e-300)
+
+
+# --------------------------------------------------------------------------
+# SpenseGPT+ scores and dense index selection
+# --------------------------------------------------------------------------
+
+def test_scores_closed_form():
+    """All-ones weights and constant calibration columns: every index scores
+    2 H sqrt(T) |v| + H sqrt(sum_t a_ti^2)."""
+    H, I, T = 8, 12, 5
+    one = np.full((I, H), 0x3F80, dtype=np.uint16)           # bf16 1.0
+    Wd = np.full((H, I), 0x3F80, dtype=np.uint16)
+    X = np.full((T, H), 0x4000, dtype=np.uint16)             # bf16 2.0
+    rng = np.random.default_rng(55)
+    A = synth.make_x(T, I, DT_BF16, rng)
+    a = oracle.decode_values(A, DT_BF16)
+    s = oracle.glu_scores_ref(X, A, DT_BF16, one, one, Wd, DT_BF16)
+    ref = 2 * H * np.sqrt(T) * 2.0 + H * np.sqrt((a * a).sum(axis=0))
+    assert np.allclose(s, ref, rtol=1e-14, atol=0)
+
+
+def test_scores_brute_force_loops_with_scales():
+    H, I, T = 4, 6, 3
+    rng = np.random.default_rng(56)
+    Wg, sg = synth.make_weight(I, H, DT_FP8, rng)
+    Wu, su = synth.make_weight(I, H, DT_FP8, rng)
+    Wd, sd = synth.make_weight(H, I, DT_FP8, rng)
+    X = synth.make_x(T, H, DT_BF16, rng)
+    A = synth.make_x(T, I, DT_BF16, rng)
+    s = oracle.glu_scores_ref(X, A, DT_BF16, Wg, Wu, Wd, DT_FP8, sg, su, sd)
+    x = oracle.decode_values(X, DT_BF16).tolist()
+    a = oracle.decode_values(A, DT_BF16).tolist()
+    g, u, dn = (oracle.decode_values(w, DT_FP8).tolist() for w in (Wg, Wu, Wd))
+    for i in range(I):
+        tot = 0.0
+        for j in range(H):
+            hjj = sum(x[t][j] ** 2 for t in range(T))
+            tot += abs(g[i][j] * float(sg[i])) * hjj ** 0.5 + abs(u[i][j] * float(su[i])) * hjj ** 0.5
+        hii = sum(a[t][i] ** 2 for t in range(T))
+        for n in range(H):
+            tot += abs(dn[n][i] * float(sd[n])) * hii ** 0.5
+        assert abs(s[i] - tot) <= 1e-12 * tot
+
+
+def test_scores_follow_index_permutation():
+    H, I, T = 16, 24, 7
+    rng = np.random.default_rng(57)
+    Wg, _ = synth.make_weight(I, H, DT_BF16, rng)
+    Wu, _ = synth.make_weight(I, H, DT_BF16, rng)
+    Wd, _ = synth.make_weight(H, I, DT_BF16, rng)
+    X = synth.make_x(T, H, DT_BF16, rng)
+    A = synth.make_x(T, I, DT_BF16, rng)
+    p = rng.permutation(I)
+    s = oracle.glu_scores_ref(X, A, DT_BF16, Wg, Wu, Wd, DT_BF16)
+    sp = oracle.glu_scores_ref(X, A[:, p], DT_BF16, Wg[p], Wu[p], Wd[:, p], DT_BF16)
+    assert np.allclose(sp, s[p], rtol=1e-15, atol=0)
+
+
+def test_select_dense_rank_definition():
+    """Top-k by the rank definition (count of strictly larger scores, plus equal
+    scores at lower indices), brute force over small integer score vectors."""
+    rng = np.random.default_rng(58)
+    for _ in range(200):
+        n = int(rng.integers(1, 12))
+        sc = rng.integers(0, 4, size=n).astype(np.float64)
+        k = int(rng.integers(0, n + 1))
+        rank = [sum(1 for j in range(n) if sc[j] > sc[i] or (sc[j] == sc[i] and j < i)) for i in range(n)]
+        want = sorted(i for i in range(n) if rank[i] < k)
+        assert oracle.select_dense_ref(sc, k).tolist() == want
+    assert oracle.select_dense_ref(np.array([1.0, 3.0, 3.0, 2.0, 3.0]), 2).tolist() == [1, 2]
