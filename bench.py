@@ -377,7 +377,6 @@ def run_glu(args, torch, sdg, synth, wl):
     hs += [pack(dense_idx=D) for _ in range(n_copies - 1)]
     hd = [pack(dense_fraction=1.0) for _ in range(n_copies)]
     wbytes, dbytes = info["weight_bytes"], sdg.spense_info(hd[0])["weight_bytes"]
-    del Wgu_d, Wd_d
 
     def step(handles, M, i):
         sdg.spense_glu(handles[i % len(handles)], Xd[:M], A[:M], Y[:M], stream=stream)
@@ -412,6 +411,34 @@ def run_glu(args, torch, sdg, synth, wl):
         dev_[M] = (e0, e1)
     torch.cuda.synchronize()
     dus = {M: a.elapsed_time(b) * 1e3 / args.steps for M, (a, b) in dev_.items()}
+
+    # SpenseGPT+ selection of the dense set (offline, before packing): scores
+    # from T calibration rows, their intermediate activations taken from the
+    # dense block itself, then the top-I_d selection
+    T = 512
+    Xc = torch.from_numpy(synth.make_x(T, H, synth.DT_BF16, np.random.default_rng(7)).view(np.int16)).to(dev).view(
+        torch.bfloat16)
+    Ac = torch.empty((T, I), dtype=torch.bfloat16, device=dev)
+    Yc = torch.empty((T, H), dtype=torch.bfloat16, device=dev)
+    sdg.spense_glu(hd[0], Xc, Ac, Yc, stream=stream)
+    score = torch.empty(I, dtype=torch.float32, device=dev)
+    reps, t_score, t_sel = 5, 0.0, 0.0
+    for r in range(reps + 1):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        sdg.spense_score_glu(Wgu_d, Wd_d, gu.wdtype, H=H, I=I, X_cal=Xc, A_cal=Ac, score=score, s_gu=sgu_d,
+                             s_down=sd_d, stream=stream)
+        t1 = time.perf_counter()
+        sel = sdg.spense_select_dense(score, int(len(D)), stream=stream)
+        t2 = time.perf_counter()
+        if r:  # the first call is a warmup
+            t_score += t1 - t0
+            t_sel += t2 - t1
+    score_bytes = Wgu.nbytes + Wd.nbytes + 2 * T * (H + I) * 2
+    scoring = {"T": T, "score_ms": round(t_score / reps * 1e3, 3), "select_ms": round(t_sel / reps * 1e3, 3),
+               "score_GBs": round(score_bytes / (t_score / reps) / 1e9, 1), "k": int(len(sel)),
+               "note": "host wall time per call (each call allocates scratch and synchronises)"}
+    del Wgu_d, Wd_d
     for h in hs + hd:
         sdg.spense_free(h)
 
@@ -447,7 +474,7 @@ def run_glu(args, torch, sdg, synth, wl):
         "spense_weight_bytes": wbytes, "dense_weight_bytes": dbytes, "pack_ms_wall": round(pack_ms, 3),
         "roofline": {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None},
-        "cpu_baseline": cpu, "input_gen_s": round(gen_s, 2),
+        "cpu_baseline": cpu, "input_gen_s": round(gen_s, 2), "spensegpt_plus_scoring": scoring,
     }
     print(json.dumps(out))
 

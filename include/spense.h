@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define SPENSE_ABI_VERSION 3
+#define SPENSE_ABI_VERSION 4
 
 /* Element types.  The numbering is fixed. */
 typedef enum spense_dtype {
@@ -180,6 +180,42 @@ int spense_pack_glu(const void* W_gu, const void* W_down, int32_t wdtype, int64_
  */
 int spense_glu(spense_handle h, const void* X, int64_t M, int64_t ldx, void* A, int64_t lda, void* Y,
                int32_t ydtype, int64_t ldy, void* stream);
+
+/*
+ * spense_score_glu - SpenseGPT+ importance score of every intermediate index of a GLU block.
+ *
+ * Technical Summary 2.B of the SpenseGPT explainer: each weight scores
+ * |W_ij| * sqrt(H_jj), H = X^T X over calibration inputs of its projection,
+ * and the scores are aggregated per intermediate index over the gate, up and
+ * down projections.  Here (the pages leave the aggregation open) it is the
+ * plain sum over the weights attached to index i:
+ *   score[i] = sum_j |Wg[i,j]| sqrt(Hx_jj) + sum_j |Wu[i,j]| sqrt(Hx_jj)
+ *            + sum_n |Wd[n,i]| sqrt(Ha_ii),
+ * |W| the dequantised magnitude (per-row scale included).
+ *
+ *   W_gu, W_down, wdtype, H, I, ld_gu, ld_down, s_gu, s_down: as for spense_pack_glu
+ *              (bf16 or e4m3 weights, the unpruned block).
+ *   X_cal      device pointer, [T, ld_x] bf16: calibration inputs of gate and up, ld_x >= H.
+ *   A_cal      device pointer, [T, ld_a] bf16: calibration inputs of down (the block's
+ *              intermediate activations), ld_a >= I.
+ *   score      device pointer, [I] float32 output.
+ * Reductions run in a fixed order (bitwise repeatable).  Offline step: it
+ * allocates scratch (hipMalloc) and synchronises `stream`.
+ */
+int spense_score_glu(const void* W_gu, const void* W_down, int32_t wdtype, int64_t H, int64_t I, int64_t ld_gu,
+                     int64_t ld_down, const float* s_gu, const float* s_down, const void* X_cal, int64_t T,
+                     int64_t ld_x, const void* A_cal, int64_t ld_a, float* score, void* stream);
+
+/*
+ * spense_select_dense - the dense set: the k indices with the highest scores.
+ *
+ *   score      device pointer, [n] float32 (for example from spense_score_glu).
+ *   dense_idx  host pointer, [k] int32 output, ascending; ready for spense_pack_glu.
+ * Index i is selected iff fewer than k indices j have score[j] > score[i] or
+ * score[j] == score[i] with j < i (ties go to the lower index).  0 <= k <= n.
+ * Allocates scratch (hipMalloc) and synchronises `stream`.
+ */
+int spense_select_dense(const float* score, int64_t n, int64_t k, int32_t* dense_idx, void* stream);
 
 /*
  * spense_linear - Y = X . W_pruned^T (times the per-channel scales), the layer forward.

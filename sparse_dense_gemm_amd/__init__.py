@@ -68,6 +68,10 @@ def _lib():
     lib.spense_pack_glu.restype = ctypes.c_int
     lib.spense_glu.argtypes = [vp, vp, i64, i64, vp, i64, vp, i32, i64, vp]
     lib.spense_glu.restype = ctypes.c_int
+    lib.spense_score_glu.argtypes = [vp, vp, i32, i64, i64, i64, i64, vp, vp, vp, i64, i64, vp, i64, vp, vp]
+    lib.spense_score_glu.restype = ctypes.c_int
+    lib.spense_select_dense.argtypes = [vp, i64, i64, vp, vp]
+    lib.spense_select_dense.restype = ctypes.c_int
     lib.spense_linear.argtypes = [vp, vp, i32, i64, i64, vp, i32, i64, vp]
     lib.spense_linear.restype = ctypes.c_int
     lib.spense_linear_splits.argtypes = [vp, vp, i32, i64, i64, vp, i32, i64, i32, vp]
@@ -210,6 +214,25 @@ def spense_glu(h: int, X, A, Y, *, M: Optional[int] = None, stream=None) -> None
     st = _lib().spense_glu(h, _ptr(X), M, X.stride(0), _ptr(A), A.stride(0), _ptr(Y), ydtype, Y.stride(0),
                            _stream(stream))
     _check(st, "spense_glu")
+
+
+def spense_score_glu(W_gu, W_down, wdtype: int, *, H: int, I: int, X_cal, A_cal, score, s_gu=None, s_down=None,
+                     stream=None) -> None:
+    """SpenseGPT+ scores of the intermediate indices of a GLU block into `score` (float32 [I], device)."""
+    ld_gu = W_gu.stride(0) if hasattr(W_gu, "stride") else H
+    ld_down = W_down.stride(0) if hasattr(W_down, "stride") else I
+    st = _lib().spense_score_glu(_ptr(W_gu), _ptr(W_down), wdtype, H, I, ld_gu, ld_down, _ptr(s_gu), _ptr(s_down),
+                                 _ptr(X_cal), X_cal.shape[0], X_cal.stride(0), _ptr(A_cal), A_cal.stride(0),
+                                 _ptr(score), _stream(stream))
+    _check(st, "spense_score_glu")
+
+
+def spense_select_dense(score, k: int, stream=None) -> np.ndarray:
+    """Indices of the k highest scores (ties to the lower index), ascending, as numpy int32."""
+    out = np.zeros(max(k, 1), dtype=np.int32)
+    st = _lib().spense_select_dense(_ptr(score), score.numel(), k, out.ctypes.data, _stream(stream))
+    _check(st, "spense_select_dense")
+    return out[:k]
 
 
 def spense_linear(h: int, X, Y, *, xdtype: Optional[int] = None, ydtype: Optional[int] = None,

@@ -14,7 +14,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libspense.so")
-SOURCES = [os.path.join(HERE, "csrc", "spense_kernels.hip"), os.path.join(HERE, "csrc", "spense_api.cpp")]
+SOURCES = [os.path.join(HERE, "csrc", f) for f in ("spense_kernels.hip", "spense_score.hip", "spense_api.cpp")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 # -packed-fp32-ops: keep the compiler from forming v_pk_{add,mul,fma}_f32.

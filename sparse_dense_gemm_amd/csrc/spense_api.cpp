@@ -733,6 +733,63 @@ int spense_linear(spense_handle h, const void* X, int32_t xdtype, int64_t M, int
   return spense_linear_splits(h, X, xdtype, M, ldx, Y, ydtype, ldy, 0, stream);
 }
 
+int spense_score_glu(const void* W_gu, const void* W_down, int32_t wdtype, int64_t H, int64_t I, int64_t ld_gu,
+                     int64_t ld_down, const float* s_gu, const float* s_down, const void* X_cal, int64_t T,
+                     int64_t ld_x, const void* A_cal, int64_t ld_a, float* score, void* stream) {
+  // ---- validation (host only) ----
+  if (!W_gu || !W_down || !X_cal || !A_cal || !score) return SPENSE_EINVAL;
+  if (wdtype != SPENSE_BF16 && wdtype != SPENSE_FP8_E4M3) return valid_dtype(wdtype) ? SPENSE_EUNSUPPORTED : SPENSE_EINVAL;
+  if (H < 1 || I < 1 || T < 1 || ld_gu < H || ld_down < I || ld_x < H || ld_a < I) return SPENSE_EINVAL;
+  if (H > (int64_t(1) << 30) || I > (int64_t(1) << 30) || T > (int64_t(1) << 30)) return SPENSE_EINVAL;
+  const bool fp8 = wdtype == SPENSE_FP8_E4M3;
+  if (fp8 != (s_gu != nullptr) || fp8 != (s_down != nullptr)) return SPENSE_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  // scratch: Hx [H], Ha [I], chunk partials, gate/up row scores [2I], down column sums [I]
+  constexpr int64_t kRows = 64;  // calibration rows per partial sum
+  const int64_t nchunks = std::max((T + kRows - 1) / kRows, (H + kColRows - 1) / kColRows);
+  const size_t n_floats = (size_t)(H + I + nchunks * std::max(H, I) + 2 * I + I);
+  float* tmp = nullptr;
+  hipError_t e = hipMalloc((void**)&tmp, n_floats * 4);
+  if (e != hipSuccess) return e == hipErrorOutOfMemory ? SPENSE_ENOMEM : hip_fail(e);
+  float* hx = tmp;
+  float* ha = hx + H;
+  float* partial = ha + I;
+  float* rowscore = partial + nchunks * std::max(H, I);
+  float* down_abs = rowscore + 2 * I;
+  e = launch_colsq(X_cal, T, H, ld_x, partial, kRows, hx, s);
+  if (e == hipSuccess) e = launch_colsq(A_cal, T, I, ld_a, partial, kRows, ha, s);
+  if (e == hipSuccess)
+    e = launch_glu_scores(wdtype, W_gu, W_down, H, I, ld_gu, ld_down, s_gu, s_down, hx, ha, rowscore, down_abs,
+                          partial, score, s);
+  const hipError_t e2 = hipStreamSynchronize(s);  // the scratch is released on return
+  (void)hipFree(tmp);
+  if (e == hipSuccess) e = e2;
+  return e == hipSuccess ? SPENSE_OK : hip_fail(e);
+}
+
+int spense_select_dense(const float* score, int64_t n, int64_t k, int32_t* dense_idx, void* stream) {
+  if (!score || n < 1 || n > (int64_t(1) << 30) || k < 0 || k > n || (k > 0 && !dense_idx)) return SPENSE_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t* sel = nullptr;  // [n] selection mask, then [n] int32 ranks (4-byte aligned)
+  const size_t off = ((size_t)n + 255) / 256 * 256;
+  hipError_t e = hipMalloc((void**)&sel, off + (size_t)n * 4);
+  if (e != hipSuccess) return e == hipErrorOutOfMemory ? SPENSE_ENOMEM : hip_fail(e);
+  std::vector<uint8_t> h_sel((size_t)n);
+  e = launch_rank_select(score, n, k, (int*)(sel + off), sel, s);
+  if (e == hipSuccess) e = hipMemcpyAsync(h_sel.data(), sel, (size_t)n, hipMemcpyDeviceToHost, s);
+  const hipError_t e2 = hipStreamSynchronize(s);
+  (void)hipFree(sel);
+  if (e == hipSuccess) e = e2;
+  if (e != hipSuccess) return hip_fail(e);
+  int64_t m = 0;
+  for (int64_t i = 0; i < n; ++i)
+    if (h_sel[(size_t)i]) {
+      if (m == k) return hip_fail(hipErrorUnknown);  // cannot happen: exactly k ranks are below k
+      dense_idx[m++] = (int32_t)i;
+    }
+  return m == k ? SPENSE_OK : hip_fail(hipErrorUnknown);
+}
+
 int spense_info(spense_handle h, spense_layer_info* info) {
   if (!h || !info) return SPENSE_EINVAL;
   std::memset(info, 0, sizeof(*info));

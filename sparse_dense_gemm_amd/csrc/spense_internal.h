@@ -124,6 +124,19 @@ hipError_t launch_linear(const LayerDesc& d, const LinearArgs& a, const LinearPl
 hipError_t launch_linear2(const LayerDesc& d0, const LinearArgs& a0, const LinearPlan& p0, const LayerDesc& d1,
                           const LinearArgs& a1, const LinearPlan& p1, hipStream_t s);
 hipError_t launch_zero_i32(int32_t* p, int64_t n, hipStream_t s);
+// SpenseGPT+ scoring (spense_score.hip): diag(X^T X) of a bf16 [T, C] matrix via
+// fixed-order chunk partials [C][ceil(T / rows_per_chunk)]; GLU index scores;
+// exact top-k selection (ties to the lower index) as a 0/1 mask
+hipError_t launch_colsq(const void* X, int64_t T, int64_t C, int64_t ld, float* partial, int64_t rows_per_chunk,
+                        float* out, hipStream_t s);
+constexpr int64_t kColRows = 64;  // rows per partial sum of the column reductions
+// partial: [I][ceil(H / kColRows)] scratch for the down-projection column sums
+hipError_t launch_glu_scores(int32_t wdtype, const void* W_gu, const void* W_down, int64_t H, int64_t I, int64_t ld_gu,
+                             int64_t ld_down, const float* s_gu, const float* s_down, const float* hx,
+                             const float* ha, float* rowscore, float* down_abs, float* partial, float* score,
+                             hipStream_t s);
+// rank: [n] int32 scratch
+hipError_t launch_rank_select(const float* score, int64_t n, int64_t k, int* rank, uint8_t* sel, hipStream_t s);
 // X'p = X[:, pip] as a contiguous [M][K_p] bf16 buffer
 hipError_t launch_gather_x(const LayerDesc& d, const void* X, int64_t M, int64_t ldx, void* Xp, hipStream_t s);
 

@@ -36,7 +36,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_strerror():
-    assert sdg.spense_abi_version() == 3
+    assert sdg.spense_abi_version() == 4
     lib = sdg._lib()
     for code in (0, -1, -2, -3, -4):
         assert lib.spense_strerror(code)
@@ -151,3 +151,22 @@ def test_pack_glu_rejects_bad_arguments(kw, want):
 def test_glu_rejects_bad_arguments():
     lib = sdg._lib()
     assert lib.spense_glu(None, FAKE_PTR, 1, 128, FAKE_PTR, 256, FAKE_PTR, sdg.DT_F32, 128, None) == sdg.SPENSE_EINVAL
+
+
+def test_score_and_select_reject_bad_arguments():
+    lib = sdg._lib()
+    P = FAKE_PTR
+    # null pointers, bad sizes, scale mismatch, fp32 weights
+    assert lib.spense_score_glu(None, P, sdg.DT_FP8, 64, 128, 64, 128, P, P, P, 4, 64, P, 128, P, None) == sdg.SPENSE_EINVAL
+    assert lib.spense_score_glu(P, P, sdg.DT_FP8, 0, 128, 64, 128, P, P, P, 4, 64, P, 128, P, None) == sdg.SPENSE_EINVAL
+    assert lib.spense_score_glu(P, P, sdg.DT_FP8, 64, 128, 64, 128, P, P, P, 0, 64, P, 128, P, None) == sdg.SPENSE_EINVAL
+    assert lib.spense_score_glu(P, P, sdg.DT_FP8, 64, 128, 64, 128, P, P, P, 4, 32, P, 128, P, None) == sdg.SPENSE_EINVAL
+    assert lib.spense_score_glu(P, P, sdg.DT_FP8, 64, 128, 64, 128, None, P, P, 4, 64, P, 128, P, None) == sdg.SPENSE_EINVAL
+    assert lib.spense_score_glu(P, P, sdg.DT_BF16, 64, 128, 64, 128, P, P, P, 4, 64, P, 128, P, None) == sdg.SPENSE_EINVAL
+    assert (lib.spense_score_glu(P, P, sdg.DT_F32, 64, 128, 64, 128, None, None, P, 4, 64, P, 128, P, None)
+            == sdg.SPENSE_EUNSUPPORTED)
+    out = np.zeros(4, dtype=np.int32)
+    assert lib.spense_select_dense(None, 8, 2, out.ctypes.data, None) == sdg.SPENSE_EINVAL
+    assert lib.spense_select_dense(P, 8, 9, out.ctypes.data, None) == sdg.SPENSE_EINVAL
+    assert lib.spense_select_dense(P, 8, -1, out.ctypes.data, None) == sdg.SPENSE_EINVAL
+    assert lib.spense_select_dense(P, 8, 2, None, None) == sdg.SPENSE_EINVAL
