@@ -29,6 +29,12 @@ written from the definitions on the pages:
   * same page, Technical Summary 2.B "SpenseGPT+": a score per intermediate
     index from |W_ij| * sqrt(H_jj) over gate, up and down, the top-scoring
     indices kept dense (``glu_scores_ref``, ``select_dense_ref``).
+  * same page, Technical Summary 4 "Experimental Results" (layers run in
+    FP8) with the SlideSparse explainer's Methodology 2.B "Activation
+    Lifting" and 2.C (per-token activation quantisation online, the column
+    re-ordering folded into it, then the 2:4 GEMM): the W8A8 form
+    (``e4m3_round``, ``quantize_tokens_ref``, ``linear_w8a8_ref``) with the
+    absmax per-token scale, the reading stated in ``spense.py``.
   * same page, Technical Summary 1 "Problem Statement" (and the SlideSparse
     explainer's Technical summary 1): 2:4 means at most two nonzeros in every
     four consecutive weights.
@@ -48,15 +54,18 @@ from .spense import (  # noqa: F401
     decode_values,
     decompress,
     dense_linear_ref,
+    e4m3_round,
     down_ref,
     glu_block_ref,
     glu_scores_ref,
     hessian_diag,
     linear_ref,
     linear_rows_ref,
+    linear_w8a8_ref,
     magnitude_key,
     pack,
     pack_rows,
+    quantize_tokens_ref,
     resolve_dense_rows,
     resolve_dense_set,
     select_dense_ref,

@@ -438,3 +438,67 @@ def select_dense_ref(score: np.ndarray, k: int) -> np.ndarray:
     """The k highest scores, ties to the lower index; returned ascending."""
     order = np.argsort(-np.asarray(score, dtype=np.float64), kind="stable")
     return np.sort(order[:k])
+
+
+# ---------------------------------------------------------------------------
+# W8A8: e4m3 weights times per-token e4m3 activations.  The SpenseGPT
+# explainer (Technical Summary 4, "Experimental Results") runs its layers in
+# FP8; the SlideSparse explainer (Methodology 2.B "Activation Lifting" and
+# 2.C "System integration") quantises activations per token online, folding
+# the activation column re-ordering into that same pass, ahead of the 2:4
+# sparse GEMM.  Neither page fixes the scale rule; the reading here is the
+# plain absmax one:
+#     s_x[m] = max_k |X[m, k]| / 448  (fp32 quotient; 448 = largest e4m3fn value),
+#              1 for an all-zero row,
+#     q[m, k] = the e4m3fn value nearest to the fp32 quotient X[m, k] / s_x[m],
+#              ties to the even code (mantissa LSB 0); magnitudes beyond 448
+#              saturate to 448; the sign is kept (a negative value that rounds
+#              to zero gives -0),
+# and the layer output is Y[m, n] = s_x[m] * s[n] * sum_k q[m, k] * Wp[n, k].
+# ---------------------------------------------------------------------------
+E4M3_MAX = 448.0
+# non-negative e4m3fn values, increasing with the code: 0x00 (zero), 0x01..0x07
+# (subnormals), 0x08..0x7E (normals); 0x7F is NaN
+_E4M3_POS = _E4M3_TABLE[:0x7F]
+
+
+def e4m3_round(v) -> np.ndarray:
+    """float32 values -> e4m3fn codes (uint8), round to nearest, ties to even, saturating."""
+    v = np.asarray(v, dtype=np.float32)
+    a = np.abs(v.astype(np.float64))
+    hi = np.clip(np.searchsorted(_E4M3_POS, a, side="left"), 0, 0x7E)
+    lo = np.clip(hi - 1, 0, 0x7E)
+    d_lo = a - _E4M3_POS[lo]
+    d_hi = _E4M3_POS[hi] - a
+    code = np.where(d_hi < d_lo, hi, np.where(d_lo < d_hi, lo, np.where(hi % 2 == 0, hi, lo)))
+    code = np.where(a >= E4M3_MAX, 0x7E, code)  # at or beyond the largest value (saturation)
+    code = code.astype(np.uint8) | np.where(np.signbit(v), np.uint8(0x80), np.uint8(0))
+    return np.where(np.isnan(v), np.uint8(0x7F), code).astype(np.uint8)
+
+
+def quantize_tokens_ref(X_bits: np.ndarray, xdtype: int = DT_BF16):
+    """Per-token e4m3 quantisation of X [M, K]: returns (codes uint8 [M, K], s_x float32 [M])."""
+    X = decode_values(X_bits, xdtype).astype(np.float32)  # exact for bf16
+    amax = np.max(np.abs(X), axis=1) if X.shape[1] else np.zeros(X.shape[0], np.float32)
+    sx = np.where(amax > 0, amax / np.float32(E4M3_MAX), np.float32(1.0)).astype(np.float32)
+    q = (X / sx[:, None]).astype(np.float32)  # fp32 quotients
+    return e4m3_round(q), sx
+
+
+def linear_w8a8_ref(codes: np.ndarray, sx: np.ndarray, p: Packed, scales=None):
+    """Exact W8A8 layer output in float64 and its error scale.
+
+        Y[m, n] = s_x[m] * s[n] * sum_k q[m, k] * Wp[n, k]
+        B[m, n] = s_x[m] * s[n] * sum_k |q[m, k] * Wp[n, k]|
+    Products of two e4m3 values carry at most 8 significant bits between 2^-18
+    and 2^18, so every partial sum over K < 2^15 terms is exact in float64 and
+    the sum does not depend on its order.
+    """
+    Wp = decompress(p)
+    Q = decode_values(codes, DT_FP8)
+    acc = Q @ Wp.T
+    absacc = np.abs(Q) @ np.abs(Wp).T
+    f = np.asarray(sx, dtype=np.float32).astype(np.float64)[:, None]
+    if scales is not None:
+        f = f * np.asarray(scales, dtype=np.float32).astype(np.float64)[None, :]
+    return acc * f, absacc * f

@@ -623,3 +623,130 @@ def test_select_dense_rank_definition():
         want = sorted(i for i in range(n) if rank[i] < k)
         assert oracle.select_dense_ref(sc, k).tolist() == want
     assert oracle.select_dense_ref(np.array([1.0, 3.0, 3.0, 2.0, 3.0]), 2).tolist() == [1, 2]
+
+
+# --------------------------------------------------------------------------
+# W8A8 (per-token e4m3 activations)
+# --------------------------------------------------------------------------
+def _e4m3_nearest_by_scan(v):
+    """Brute force over all 256 codes: nearest finite value, ties to the even
+    code, sign kept, saturating at 448 (independent of the oracle's search)."""
+    v = float(np.float32(v))
+    if v != v:
+        return 0x7F
+    a = min(abs(v), 448.0)
+    best, best_d = None, None
+    for c in range(0x7F):
+        d = abs(oracle.decode_values(np.uint8(c), DT_FP8) - a)
+        if best is None or d < best_d or (d == best_d and c % 2 == 0):
+            best, best_d = c, d
+    return best | (0x80 if np.signbit(np.float32(v)) else 0)
+
+
+def test_e4m3_round_matches_torch_cast():
+    """Inside the e4m3fn range the rounding is the library cast (round to nearest even)."""
+    bf = (np.arange(65536, dtype=np.uint32) << 16).view(np.float32)
+    rng = np.random.default_rng(41)
+    v = np.concatenate([bf[np.isfinite(bf) & (np.abs(bf) <= 448.0)],
+                        rng.uniform(-448, 448, 20000).astype(np.float32),
+                        (rng.uniform(-1, 1, 5000) * 2.0 ** rng.integers(-14, -5, 5000)).astype(np.float32)])
+    got = oracle.e4m3_round(v)
+    want = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(got, want)
+
+
+def test_e4m3_round_hand_cases_and_scan():
+    # worked by hand: 1.0625 lies halfway between 1.0 (0x38) and 1.125 (0x39):
+    # the even code 0x38 wins; 1.1875 halfway between 0x39 and 1.25 (0x3A): 0x3A;
+    # 2^-10 halfway between 0 and the smallest subnormal 2^-9 (0x01): 0x00;
+    # 3 * 2^-10 halfway between 0x01 and 0x02: 0x02; 440 between 416 (0x7D) and 448 (0x7E): 0x7E
+    cases = {1.0625: 0x38, 1.1875: 0x3A, 2.0 ** -10: 0x00, 3 * 2.0 ** -10: 0x02, 440.0: 0x7E,
+             -1.0625: 0xB8, -2.0 ** -12: 0x80, 448.0: 0x7E, 449.0: 0x7E, 1e6: 0x7E, -1e6: 0xFE}
+    for v, c in cases.items():
+        assert int(oracle.e4m3_round(np.float32(v))) == c, v
+    rng = np.random.default_rng(42)
+    for v in np.concatenate([rng.uniform(-460, 460, 300), rng.uniform(-0.02, 0.02, 100)]).astype(np.float32):
+        assert int(oracle.e4m3_round(v)) == _e4m3_nearest_by_scan(v), v
+
+
+def test_e4m3_round_trip_every_code():
+    codes = np.array([c for c in range(256) if c & 0x7F != 0x7F], dtype=np.uint8)
+    vals = oracle.decode_values(codes, DT_FP8).astype(np.float32)
+    assert np.array_equal(oracle.e4m3_round(vals), codes)
+
+
+def test_quantize_tokens_properties():
+    rng = np.random.default_rng(43)
+    X = synth.make_x(9, 300, DT_BF16, rng)
+    X[4] = 0  # an all-zero token
+    q, sx = oracle.quantize_tokens_ref(X, DT_BF16)
+    Xv = oracle.decode_values(X, DT_BF16)
+    amax = np.abs(Xv).max(axis=1)
+    for m in range(9):
+        if m == 4:
+            assert sx[m] == 1.0 and not np.any(q[m] & 0x7F)
+            continue
+        assert sx[m] == np.float32(amax[m]) / np.float32(448.0)
+        # the largest element of the token lands on +-448
+        k = int(np.argmax(np.abs(Xv[m])))
+        assert int(q[m, k]) & 0x7F == 0x7E
+        # every code is within half a step of the exact quotient (e4m3 step at
+        # magnitude a: 2^(floor(log2 a) - 3) for normals, 2^-9 for subnormals)
+        t = Xv[m] / float(sx[m])
+        a = np.maximum(np.abs(t), 2.0 ** -6)
+        step = 2.0 ** (np.floor(np.log2(a)) - 3)
+        err = np.abs(oracle.decode_values(q[m], DT_FP8) - t)
+        assert np.all(err <= step / 2 * (1 + 1e-6))
+
+
+@pytest.mark.parametrize("frac", [0.0, 0.25, 1.0])
+def test_w8a8_equals_w8a16_when_tokens_are_representable(frac):
+    """Tokens built as e4m3 values times a power of two whose largest magnitude
+    is 448 times that power quantise without loss (s_x is the power of two, the
+    quotients are exact e4m3 values); the W8A8 output then equals the W8A16
+    output of the same X exactly (both sums are exact in float64)."""
+    rng = np.random.default_rng(44)
+    M, N, K = 5, 24, 256
+    W, s = synth.make_weight(N, K, DT_FP8, rng)
+    finite = np.array([c for c in range(256) if c & 0x7F != 0x7F], dtype=np.uint8)
+    codes = rng.choice(finite, size=(M, K))
+    codes[:, 7] = 0x7E  # 448 in every token
+    codes[1, 7] = 0xFE  # or -448
+    e = rng.integers(-6, 3, size=M)
+    Xv = oracle.decode_values(codes, DT_FP8) * (2.0 ** e)[:, None]
+    X = torch.from_numpy(Xv.astype(np.float32)).to(torch.bfloat16).view(torch.uint16).numpy()
+    assert np.array_equal(oracle.decode_values(X, DT_BF16), Xv)  # exact in bf16
+    q, sx = oracle.quantize_tokens_ref(X, DT_BF16)
+    assert np.array_equal(sx, (2.0 ** e).astype(np.float32))
+    pi, K_s, _ = oracle.resolve_dense_set(K, dense_fraction=frac)
+    P = oracle.pack(W, DT_FP8, pi, K_s)
+    Y8, B8 = oracle.linear_w8a8_ref(q, sx, P, s)
+    Y16, B16 = oracle.linear_ref(X, DT_BF16, P, s)
+    assert np.array_equal(Y8, Y16) and np.array_equal(B8, B16)
+
+
+def test_w8a8_tiny_brute_force_loops():
+    """Triple loop over the decompressed weights with the scan quantiser above,
+    scales included: equal to the oracle (integer-valued sums, exact)."""
+    rng = np.random.default_rng(45)
+    M, N, K = 3, 4, 16
+    W, s = synth.make_weight(N, K, DT_FP8, rng)
+    X = synth.make_x(M, K, DT_BF16, rng)
+    D = [1, 6, 11, 12]
+    pi, K_s, _ = oracle.resolve_dense_set(K, dense_cols=D)
+    P = oracle.pack(W, DT_FP8, pi, K_s)
+    q, sx = oracle.quantize_tokens_ref(X, DT_BF16)
+    Y, B = oracle.linear_w8a8_ref(q, sx, P, s)
+    Wbits = oracle.unpack_bits(P)
+    Xv = oracle.decode_values(X, DT_BF16)
+    for m in range(M):
+        amax = max(abs(float(x)) for x in Xv[m])
+        sxm = np.float32(amax) / np.float32(448.0) if amax > 0 else np.float32(1.0)
+        qm = [_e4m3_nearest_by_scan(np.float32(Xv[m, k]) / sxm) for k in range(K)]
+        assert qm == [int(c) for c in q[m]]
+        for n in range(N):
+            acc = 0.0
+            for k in range(K):
+                acc += float(oracle.decode_values(np.uint8(qm[k]), DT_FP8)) * float(
+                    oracle.decode_values(Wbits[n, k], DT_FP8))
+            assert Y[m, n] == acc * (float(sxm) * float(np.float32(s[n])))
