@@ -22,6 +22,11 @@ Other workloads (``--workload``):
   layer36b_fp8   36B-class decoder linear set, e4m3, 25% chosen dense columns per
                  layer, M in {128, 2048}
   layer36b_bf16  the same with bf16 weights
+  layer36b_w8a8  the layer36b_fp8 set in W8A8 form: activations quantised per token to
+                 e4m3 (absmax / 448) in the same pass that re-orders their columns, then
+                 the fp8 structured-sparse product; one step = spense_linear_w8a8 per
+                 layer (quantisation included), against the all-dense layers through the
+                 same path
 A layer set streams more than the Infinity Cache per pass, so its packed
 weights are not rotated.
 
@@ -48,6 +53,7 @@ HBM_PEAK_GBS = 8000.0
 # multiply-adds of a dense one in the same time, so 2.5 PFLOP/s is also its
 # peak on the nonzero multiply-adds that the algorithmic flops count.
 MFMA_PEAK_TFLOPS = 2500.0
+FP8_PEAK_TFLOPS = 5000.0  # dense e4m3 matrix peak (W8A8)
 MALL_BYTES = 256 << 20
 CSRC = os.path.join(ROOT, "sparse_dense_gemm_amd", "csrc")
 # the kernels and the launch planner that picks them decide the HBM traffic
@@ -63,7 +69,9 @@ SETS = {
     "layer32b_fp8": ["layer32b_fp8_d0", "layer32b_fp8_d12p5", "layer32b_fp8_d25", "layer32b_fp8_d50"],
     "layer36b_fp8": ["layer36b_fp8"],
     "layer36b_bf16": ["layer36b_bf16"],
+    "layer36b_w8a8": ["layer36b_fp8"],
 }
+A8_SETS = {"layer36b_w8a8"}  # run through spense_linear_w8a8
 HEADLINE_VARIANT = {"layer32b_fp8": "layer32b_fp8_d25"}
 
 
@@ -187,10 +195,18 @@ def main():
     sets = [[Layer(sdg, torch, dev, spec, Mmax, rotate=single) for spec in wl.layers] for wl in wls]
     gen_s = time.time() - t0
 
+    a8 = args.workload in A8_SETS
+
+    def call(h, X, Y):
+        if a8:
+            sdg.spense_linear_w8a8(h, X, Y, splits=args.splits, stream=stream)
+        else:
+            sdg.spense_linear_splits(h, X, Y, args.splits, stream=stream)
+
     def run_set(layers, M, i, dense):
         for L in layers:
             hs = L.dhandles if dense else L.handles
-            sdg.spense_linear_splits(hs[i % len(hs)], L.Xd[:M], L.Y[:M], args.splits, stream=stream)
+            call(hs[i % len(hs)], L.Xd[:M], L.Y[:M])
 
     # ---- prime: every packed copy once at every batch size (a handle sizes its
     # split-K and gather workspaces on first use), then the warmup steps ----
@@ -198,7 +214,7 @@ def main():
         for layers in sets:
             for L in layers:
                 for h in L.handles + L.dhandles:
-                    sdg.spense_linear_splits(h, L.Xd[:M], L.Y[:M], args.splits, stream=stream)
+                    call(h, L.Xd[:M], L.Y[:M])
     for i in range(args.warmup):
         for M in Ms:
             for layers in sets:
@@ -244,7 +260,7 @@ def main():
             for i in range(args.steps):
                 for j, L in enumerate(layers):
                     evs[i][j].record(stream)
-                    sdg.spense_linear_splits(L.handles[0], L.Xd[:M], L.Y[:M], args.splits, stream=stream)
+                    call(L.handles[0], L.Xd[:M], L.Y[:M])
                 evs[i][-1].record(stream)
             torch.cuda.synchronize()
             per_layer[str(M)] = {L.spec.name: round(sum(e[j].elapsed_time(e[j + 1]) for e in evs) * 1e3 / args.steps, 3)
@@ -281,8 +297,9 @@ def main():
         # prefill batches dominate the step and are bound by the matrix units
         t_big = sum(spense_us[(hv, M)] for M in big)
         ach = sum(sum(L.flops(M) for L in head) for M in big) / t_big / 1e6
-        roofline = {"bound": "mfma", "achieved": round(ach, 1), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(ach / MFMA_PEAK_TFLOPS, 4), "traffic": None, "batch_sizes": big}
+        peak = FP8_PEAK_TFLOPS if a8 else MFMA_PEAK_TFLOPS
+        roofline = {"bound": "mfma", "achieved": round(ach, 1), "peak": peak, "unit": "TFLOP/s",
+                    "frac": round(ach / peak, 4), "traffic": None, "batch_sizes": big}
     else:
         ach = sum(sum(L.alg_bytes(M) for L in head) for M in Ms) / total_us / 1e3
         traffic = load_traffic() if args.workload == "gateup_fp8" and not args.ms else None
@@ -298,7 +315,7 @@ def main():
                                **{f"M{M}_speedup_vs_dense": round(dense_us[M] / spense_us[(vi, M)], 4) for M in Ms}}
 
     pack_ms = round(sum(L.pack_ms for L in head), 3)
-    cpu = None if args.no_cpu_baseline else cpu_baseline(head, Ms, single)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(head, Ms, single, a8)
     for layers in sets:
         for L in layers:
             L.free(sdg)
@@ -308,6 +325,8 @@ def main():
                  "M in {" + ",".join(map(str, Ms)) + "}")
     else:
         wdesc = wls[hv].title + (f" (batch sizes {list(Ms)})" if args.ms else "")
+        if a8:
+            wdesc += ", W8A8: per-token e4m3 activations"
     cfg = {"workload": wdesc, "key": args.workload, "Ms": list(Ms), "splits": args.splits or "auto"}
     if single:
         cfg.update({"N": head[0].spec.N, "K": head[0].spec.K, "K_d": head[0].spec.K_d,
@@ -326,7 +345,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": ("e4m3" if head[0].spec.wdtype == synth.DT_FP8 else "bf16")
-        + " weights x bf16 activations, fp32 accumulate",
+        + (" weights x per-token e4m3 activations" if a8 else " weights x bf16 activations") + ", fp32 accumulate",
         "data": "synthetic",
         "config": cfg,
         "per_m": per_m,
@@ -479,7 +498,7 @@ def run_glu(args, torch, sdg, synth, wl):
     print(json.dumps(out))
 
 
-def cpu_baseline(layers, Ms, single):
+def cpu_baseline(layers, Ms, single, a8=False):
     """The oracle, as it stands, on the same layer(s): one packed form, then the
     float64 layer output.  A single layer: whole passes over the batch sizes
     until about 10 s of CPU work.  A layer set: the first 256 output rows of
@@ -521,11 +540,17 @@ def cpu_baseline(layers, Ms, single):
         pi, K_s, _ = oracle.resolve_dense_set(L.spec.K, dense_cols=D)
         p = oracle.pack(W[:rows], L.spec.wdtype, pi, K_s)
         t0 = time.perf_counter()
-        oracle.linear_ref(X[:M], oracle.DT_BF16, p, None if s is None else s[:rows])
+        if a8:
+            q, sx = oracle.quantize_tokens_ref(X[:M], oracle.DT_BF16)
+            oracle.linear_w8a8_ref(q, sx, p, s[:rows])
+        else:
+            oracle.linear_ref(X[:M], oracle.DT_BF16, p, None if s is None else s[:rows])
         dt += time.perf_counter() - t0
         nbytes += L.wbytes * rows / L.spec.N
+    what = "quantize_tokens_ref + linear_w8a8_ref" if a8 else "linear_ref"
     return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"first {rows} output rows of each layer, M={M} ({dt:.1f} s); pack excluded"}
+            "sample": f"oracle {what} on the first {rows} output rows of each layer, M={M} ({dt:.1f} s); "
+                      "pack excluded"}
 
 
 if __name__ == "__main__":

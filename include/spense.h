@@ -42,7 +42,7 @@
 extern "C" {
 #endif
 
-#define SPENSE_ABI_VERSION 4
+#define SPENSE_ABI_VERSION 5
 
 /* Element types.  The numbering is fixed. */
 typedef enum spense_dtype {
@@ -251,6 +251,50 @@ int spense_linear(spense_handle h, const void* X, int32_t xdtype, int64_t M, int
  */
 int spense_linear_splits(spense_handle h, const void* X, int32_t xdtype, int64_t M, int64_t ldx, void* Y,
                          int32_t ydtype, int64_t ldy, int32_t splits, void* stream);
+
+/*
+ * spense_quantize_tokens - per-token e4m3 quantisation of bf16 activations.
+ *
+ * The SpenseGPT explainer runs its layers in FP8 (Technical Summary 4,
+ * "Experimental Results"); the SlideSparse explainer quantises activations
+ * per token online, ahead of the 2:4 GEMM (Methodology 2.B "Activation
+ * Lifting", 2.C).  The scale rule is not given there; this library uses the
+ * absmax rule:
+ *   sx[m]     = max_k |X[m][k]| / 448 as an fp32 quotient (448 is the largest
+ *               e4m3fn value), or 1 for an all-zero row;
+ *   Xq[m][k]  = the e4m3fn code nearest to the fp32 quotient X[m][k] / sx[m],
+ *               ties to the even code, sign kept (within range by construction).
+ *
+ *   X    device pointer, [M, ldx] bf16, finite values, ldx >= K.
+ *   Xq   device pointer, [M, ldq] e4m3 codes (uint8), ldq >= K; written.
+ *   sx   device pointer, [M] float32; written.
+ * 1 <= M <= 2^24, K >= 1 (SPENSE_EINVAL otherwise).  Asynchronous on `stream`.
+ */
+int spense_quantize_tokens(const void* X, int64_t M, int64_t K, int64_t ldx, uint8_t* Xq, int64_t ldq, float* sx,
+                           void* stream);
+
+/*
+ * spense_linear_w8a8 - Y = sx[m] * s[n] * sum_k Xq[m][k] * Wp[n][k]: the layer
+ * with e4m3 weights and per-token e4m3 activations.
+ *
+ * The activations are quantised as spense_quantize_tokens does; the same pass
+ * writes them in the layer's packed column order (the dense-set permutation
+ * rides on the quantisation, as the SlideSparse explainer folds its activation
+ * re-ordering into per-token quantisation), into the handle's workspace.
+ * Products of two e4m3 values are exact in fp32; the sum runs in fp32 in a
+ * fixed order (bitwise repeatable).
+ *
+ *   h      an input-split layer packed from SPENSE_FP8_E4M3 weights
+ *          (SPENSE_EUNSUPPORTED for other weight types and for output-split
+ *          layers and GLU blocks).
+ *   X      device pointer, [M, ldx] bf16, finite values, ldx >= K.
+ *   Y      device pointer, [M, ldy] of ydtype (SPENSE_F32 or SPENSE_BF16 RNE), ldy >= N.
+ *   splits split-K factor as for spense_linear_splits (0: automatic).
+ * Grows the handle's workspaces on first use at a larger M (synchronising
+ * `stream`); otherwise asynchronous.  One call in flight per handle.
+ */
+int spense_linear_w8a8(spense_handle h, const void* X, int64_t M, int64_t ldx, void* Y, int32_t ydtype, int64_t ldy,
+                       int32_t splits, void* stream);
 
 /* spense_info - sizes of a packed layer (host-side, no synchronisation). */
 int spense_info(spense_handle h, spense_layer_info* info);

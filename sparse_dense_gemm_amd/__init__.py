@@ -75,6 +75,10 @@ def _lib():
     lib.spense_linear.argtypes = [vp, vp, i32, i64, i64, vp, i32, i64, vp]
     lib.spense_linear.restype = ctypes.c_int
     lib.spense_linear_splits.argtypes = [vp, vp, i32, i64, i64, vp, i32, i64, i32, vp]
+    lib.spense_quantize_tokens.restype = ctypes.c_int
+    lib.spense_quantize_tokens.argtypes = [vp, i64, i64, i64, vp, i64, vp, vp]
+    lib.spense_linear_w8a8.restype = ctypes.c_int
+    lib.spense_linear_w8a8.argtypes = [vp, vp, i64, i64, vp, i32, i64, i32, vp]
     lib.spense_linear_splits.restype = ctypes.c_int
     lib.spense_info.argtypes = [vp, ctypes.POINTER(LayerInfo)]
     lib.spense_info.restype = ctypes.c_int
@@ -256,6 +260,36 @@ def spense_linear_splits(h: int, X, Y, splits: int, *, xdtype: Optional[int] = N
         ldy = Y.stride(0)
     st = _lib().spense_linear_splits(h, _ptr(X), xdtype, M, ldx, _ptr(Y), ydtype, ldy, splits, _stream(stream))
     _check(st, "spense_linear")
+
+
+def spense_quantize_tokens(X, Xq, sx, *, M: Optional[int] = None, K: Optional[int] = None,
+                           ldx: Optional[int] = None, ldq: Optional[int] = None, stream=None) -> None:
+    """Per-token e4m3 codes of bf16 X into Xq (uint8 [M, K]) and the token scales into sx (float32 [M])."""
+    if M is None:
+        M = X.shape[0]
+    if K is None:
+        K = X.shape[1]
+    if ldx is None:
+        ldx = X.stride(0)
+    if ldq is None:
+        ldq = Xq.stride(0)
+    st = _lib().spense_quantize_tokens(_ptr(X), M, K, ldx, _ptr(Xq), ldq, _ptr(sx), _stream(stream))
+    _check(st, "spense_quantize_tokens")
+
+
+def spense_linear_w8a8(h: int, X, Y, *, splits: int = 0, ydtype: Optional[int] = None, M: Optional[int] = None,
+                       ldx: Optional[int] = None, ldy: Optional[int] = None, stream=None) -> None:
+    """Y = (per-token e4m3 X) . W^T on an e4m3 input-split layer (asynchronous on the stream)."""
+    if ydtype is None:
+        ydtype = dtype_of(Y)
+    if M is None:
+        M = X.shape[0]
+    if ldx is None:
+        ldx = X.stride(0)
+    if ldy is None:
+        ldy = Y.stride(0)
+    st = _lib().spense_linear_w8a8(h, _ptr(X), M, ldx, _ptr(Y), ydtype, ldy, splits, _stream(stream))
+    _check(st, "spense_linear_w8a8")
 
 
 def spense_info(h: int) -> dict:

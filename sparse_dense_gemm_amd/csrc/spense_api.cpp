@@ -32,7 +32,8 @@ struct spense_layer {
   float* dense32 = nullptr;
   float* ws = nullptr;
   size_t ws_bytes = 0;
-  void* xws = nullptr;  // gathered activations [M][K_p] bf16 (chunked staging of a chosen dense set)
+  void* xws = nullptr;  // activations in X'p order: gathered bf16 [M][K_p] (chunked staging of a chosen
+                        // dense set), or W8A8 e4m3 codes [M][K_p] followed by the token scales [M]
   size_t xws_bytes = 0;
   int32_t* counters = nullptr;
   size_t n_counters = 0;
@@ -430,8 +431,12 @@ static int64_t decode_lds_bytes(const LayerDesc& d, int64_t M, int64_t S) {
   return M * (steps * kMacro + 8) * 2;
 }
 
-// dynamic LDS of the chunked decode kernel: two chunk buffers
-static int64_t stream_lds_bytes(int64_t M) { return 2 * M * (kStreamChunk * kMacro + 8) * 2; }
+// dynamic LDS of the chunked kernels: two chunk buffers of `rows` staged rows,
+// each CH unit slots of 128 columns plus a 16-byte pad (xbytes: 2 for bf16
+// activations, 1 for e4m3 codes)
+static int64_t stream_lds_bytes(int64_t rows, int64_t chunk, int xbytes) {
+  return 2 * rows * (chunk * kMacro * xbytes + 16);
+}
 
 constexpr int64_t kCUs = 256;             // compute units of the target GPU
 constexpr int64_t kLdsPerCU = 160 * 1024;  // LDS bytes per CU
@@ -440,7 +445,7 @@ constexpr int64_t kLdsPerCU = 160 * 1024;  // LDS bytes per CU
 // classes of an output-split layer); the split count and the blocking are
 // chosen from it so that both classes get the same kernel shape.
 static int plan_linear(const spense_layer* h, int64_t M, int32_t splits, int64_t NT_fill, LinearPlan& p,
-                       bool force_chunked = false) {
+                       bool force_chunked = false, int xbytes = 2) {
   const LayerDesc& d = h->d;
   const int64_t steps = std::max<int64_t>(d.n_sm, d.n_dm);
   const int64_t max_splits = std::max<int64_t>(1, std::min<int64_t>(steps, 64));
@@ -480,7 +485,7 @@ static int plan_linear(const spense_layer* h, int64_t M, int32_t splits, int64_t
     if (p.chunked && !overridden) p.waves = 4;
     p.rgroups = (int)((d.NT + p.waves - 1) / p.waves);
     p.splits = (int)S;
-    p.lds_bytes = (int)(p.chunked ? stream_lds_bytes(M) : decode_lds_bytes(d, M, S));
+    p.lds_bytes = (int)(p.chunked ? stream_lds_bytes(M, kStreamChunk, xbytes) : decode_lds_bytes(d, M, S));
     return SPENSE_OK;
   }
   // More than 16 rows: the chunked streaming kernel with register-blocked
@@ -495,17 +500,36 @@ static int plan_linear(const spense_layer* h, int64_t M, int32_t splits, int64_t
 #undef SPENSE_PRESET
   };
   constexpr int kNumPresets = (int)(sizeof(kPresets) / sizeof(kPresets[0]));
-  // Two m-tiles per wave up to 128 rows (four need more LDS per workgroup
-  // than they save there); beyond, four m-tiles and four row tiles per wave
-  // (each staged activation fragment feeds four products).  Two row tiles
-  // per wave halve the LDS reads per product but give fewer workgroups: used
-  // when the row tiles alone still give at least one workgroup per two CUs;
-  // otherwise one row tile per wave plus splits.
-  const int64_t wg_nr2 = (NT_fill + 15) / 16 * ((M + 31) / 32);
-  int pre = M <= 32 || wg_nr2 < kCUs / 2 ? 0 : M <= 64 ? 1 : M <= 128 ? 2 : 8;
+  // The largest blocking that still gives about 150 workgroups (measured on
+  // the 36B-class layers for M = 32..2048, both activation types: within 2%
+  // of the best preset per shape in total).  Eight waves per workgroup with
+  // four row tiles and four m-tiles each when there are enough tiles (ring
+  // depth 2 and two-unit chunks for bf16 activations; depth 4 and four-unit
+  // chunks for e4m3 codes, whose fragments take half the registers), then
+  // eight waves with two row tiles, then two m-tiles; at M <= 32 one m-group
+  // of two m-tiles with two row tiles per wave, or a single row tile.
+  auto workgroups = [&](int i) {
+    const Preset& c = kPresets[i];
+    return (NT_fill + c.nw * c.nr - 1) / (c.nw * c.nr) * ((M + 16 * c.mt - 1) / (16 * c.mt));
+  };
+  constexpr int64_t kEnough = 150;
+  int pre;
+  if (M <= 32) {
+    pre = workgroups(2) >= kEnough ? 2 : 7;
+  } else {
+    pre = 0;
+    for (int c : {xbytes == 1 ? 14 : 9, 12, 2})
+      if (workgroups(c) >= kEnough) {
+        pre = c;
+        break;
+      }
+  }
   if (const char* t = std::getenv("SPENSE_TILE")) {
+    // a forced preset whose two staging buffers would not fit in one CU's LDS is ignored
     const int v = std::atoi(t);
-    if (v >= 0 && v < kNumPresets) pre = v;
+    if (v >= 0 && v < kNumPresets &&
+        stream_lds_bytes(std::min<int64_t>(M, 16 * kPresets[v].mt), kPresets[v].ch, xbytes) <= kLdsPerCU)
+      pre = v;
   }
   const Preset& q = kPresets[pre];
   p.chunked = 1;
@@ -517,7 +541,7 @@ static int plan_linear(const spense_layer* h, int64_t M, int32_t splits, int64_t
   p.mt = q.mt;
   p.mgroups = (int)((M + 16 * p.mt - 1) / (16 * p.mt));
   const int64_t rows = std::min<int64_t>(M, 16 * p.mt);
-  const int64_t lds = 2 * rows * (p.chunk * kMacro + 8) * 2;
+  const int64_t lds = stream_lds_bytes(rows, p.chunk, xbytes);
   p.lds_bytes = (int)lds;
   p.rgroups = (int)((d.NT + p.waves * p.nr - 1) / (p.waves * p.nr));
   int64_t S = splits;
@@ -525,6 +549,9 @@ static int plan_linear(const spense_layer* h, int64_t M, int32_t splits, int64_t
     const int64_t units = (NT_fill + p.waves * p.nr - 1) / (p.waves * p.nr) * p.mgroups;
     const int64_t resident = kCUs * std::max<int64_t>(1, kLdsPerCU / lds);
     S = units >= kCUs / 2 ? 1 : std::max<int64_t>(1, std::min<int64_t>(resident / units, max_splits));
+    // each split writes and reads back fp32 partials of the whole output
+    // (8 M N bytes); keep that below half the packed weight bytes
+    S = std::max<int64_t>(1, std::min<int64_t>(S, d.tile_bytes / (256 * M)));
   }
   p.splits = (int)S;
   const int64_t grid = (int64_t)p.rgroups * p.mgroups * S;
@@ -692,6 +719,60 @@ int spense_linear_splits(spense_handle h, const void* X, int32_t xdtype, int64_t
   spense_layer* parts[2] = {nullptr, nullptr};
   const int n_parts = layer_parts(h, parts);
   return run_layers(parts, n_parts, M, splits, a, s);
+}
+
+int spense_quantize_tokens(const void* X, int64_t M, int64_t K, int64_t ldx, uint8_t* Xq, int64_t ldq, float* sx,
+                           void* stream) {
+  if (!X || !Xq || !sx) return SPENSE_EINVAL;
+  if (M < 1 || M > (int64_t(1) << 24) || K < 1 || ldx < K || ldq < K) return SPENSE_EINVAL;
+  const hipError_t e = launch_quantize_tokens(X, M, K, ldx, nullptr, K, Xq, ldq, sx, (hipStream_t)stream);
+  return e == hipSuccess ? SPENSE_OK : hip_fail(e);
+}
+
+int spense_linear_w8a8(spense_handle h, const void* X, int64_t M, int64_t ldx, void* Y, int32_t ydtype, int64_t ldy,
+                       int32_t splits, void* stream) {
+  if (!h || !X || !Y) return SPENSE_EINVAL;
+  if (h->split != 0) return SPENSE_EUNSUPPORTED;  // input-split layers only
+  const LayerDesc& d = h->d;
+  if (d.wdtype != SPENSE_FP8_E4M3) return SPENSE_EUNSUPPORTED;
+  if (M < 1 || M > (int64_t(1) << 24) || ldx < d.K || ldy < d.N) return SPENSE_EINVAL;
+  if (ydtype != SPENSE_F32 && ydtype != SPENSE_BF16) return SPENSE_EINVAL;
+  hipStream_t s = (hipStream_t)stream;
+  LinearPlan p{};
+  int rc = plan_linear(h, M, splits, d.NT, p, true, 1);
+  if (rc != SPENSE_OK) return rc;
+  // workspace: the codes [M][K_p] in X'p order, then the token scales [M]
+  const size_t codes = ((size_t)M * (size_t)d.K_p + 255) / 256 * 256;
+  const size_t need = codes + (size_t)M * 4;
+  if (need > h->xws_bytes) {
+    hipError_t e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_fail(e);
+    if (h->xws) (void)hipFree(h->xws);
+    h->xws = nullptr;
+    h->xws_bytes = 0;
+    e = hipMalloc(&h->xws, need);
+    if (e != hipSuccess) return e == hipErrorOutOfMemory ? SPENSE_ENOMEM : hip_fail(e);
+    h->xws_bytes = need;
+  }
+  uint8_t* q = (uint8_t*)h->xws;
+  float* sx = (float*)(q + codes);
+  // quantise and re-order the columns into X'p in one pass
+  hipError_t e = launch_quantize_tokens(X, M, d.K, ldx, d.pip, d.K_p, q, d.K_p, sx, s);
+  if (e != hipSuccess) return hip_fail(e);
+  LinearArgs a{};
+  a.X = q;
+  a.M = M;
+  a.ldx = d.K_p;
+  a.Y = Y;
+  a.ldy = ldy;
+  a.ydtype = ydtype;
+  a.splits = p.splits;
+  a.a8 = 1;
+  a.xscale = sx;
+  rc = prepare_call(h, M, p, a, false, s);
+  if (rc != SPENSE_OK) return rc;
+  e = launch_linear(d, a, p, s);
+  return e == hipSuccess ? SPENSE_OK : hip_fail(e);
 }
 
 int spense_glu(spense_handle h, const void* X, int64_t M, int64_t ldx, void* A, int64_t lda, void* Y, int32_t ydtype,

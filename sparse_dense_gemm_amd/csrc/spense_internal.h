@@ -78,6 +78,8 @@ struct LinearArgs {
   int32_t splits;
   int32_t gather;        // effective gather mode for this call
   int32_t glu;           // 1: packed rows come in (gate, up) pairs; write silu(gate) * up at the pair's column
+  int32_t a8;            // 1: X is e4m3 codes [M][K_p] in X'p order, with per-token scales xscale (W8A8)
+  const float* xscale;   // [M] (a8 only)
   float* ws;             // [splits][M][NT*16] fp32 partials (splits > 1)
   int32_t* counters;     // [row groups * m groups], zero between calls
 };
@@ -113,7 +115,11 @@ struct LinearPlan {
   X(9, 8, 4, 2, 2, 4)          \
   X(10, 4, 4, 2, 2, 2)         \
   X(11, 4, 4, 4, 4, 2)         \
-  X(12, 8, 2, 4, 4, 4)
+  X(12, 8, 2, 4, 4, 4)         \
+  X(13, 4, 4, 4, 4, 4)         \
+  X(14, 8, 4, 4, 4, 4)         \
+  X(15, 4, 4, 2, 2, 8)         \
+  X(16, 4, 2, 4, 4, 8)
 
 constexpr int kStreamChunk = 8;  // units per activation chunk of linear_stream_kernel
 
@@ -137,6 +143,11 @@ hipError_t launch_glu_scores(int32_t wdtype, const void* W_gu, const void* W_dow
                              hipStream_t s);
 // rank: [n] int32 scratch
 hipError_t launch_rank_select(const float* score, int64_t n, int64_t k, int* rank, uint8_t* sel, hipStream_t s);
+// Per-token e4m3 quantisation of bf16 X [M][K]: sx[m] = max|X[m]| / 448 (1 for
+// an all-zero row), Q[m][j] = e4m3 RNE of X[m][src] / sx[m] for j < Kout with
+// src = pip ? pip[j] : j (pip[j] < 0: code 0)
+hipError_t launch_quantize_tokens(const void* X, int64_t M, int64_t K, int64_t ldx, const int32_t* pip, int64_t Kout,
+                                  uint8_t* Q, int64_t ldq, float* sx, hipStream_t s);
 // X'p = X[:, pip] as a contiguous [M][K_p] bf16 buffer
 hipError_t launch_gather_x(const LayerDesc& d, const void* X, int64_t M, int64_t ldx, void* Xp, hipStream_t s);
 

@@ -157,7 +157,8 @@ __device__ __forceinline__ void store_y(const LinearArgs& a, int64_t m, int64_t 
 // Epilogue of a wave's NR row tiles (rt0 ..) x MT m-tiles; acc[r * MT + t],
 // to[r] = tile_out of row tile rt0 + r.  Compile-time counts keep every
 // accumulator index static (a dynamic index would move them to scratch).
-template <int NR, int MT>
+// XS: also multiply by the per-token activation scale a.xscale[m] (W8A8).
+template <int NR, int MT, bool XS = false>
 __device__ __forceinline__ void finish_tile(const LayerDesc& d, const LinearArgs& a, const f32x4* acc,
                                             const TileOut* to, int64_t rt0, int64_t m0, int s, int S,
                                             int64_t cnt_index, int* last_flag) {
@@ -199,6 +200,13 @@ __device__ __forceinline__ void finish_tile(const LayerDesc& d, const LinearArgs
           const int col = (int)to[r].col[q];
           const float g = sum[q] * to[r].sc[q], u = sum[q + 1] * to[r].sc[q + 1];
           if (col >= 0) store_y(a, m, col, g / (1.0f + __expf(-g)) * u);
+        }
+      } else if constexpr (XS) {
+        const float xs = a.xscale[m];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = (int)to[r].col[q];
+          if (col >= 0) store_y(a, m, col, sum[q] * to[r].sc[q] * xs);
         }
       } else {
 #pragma unroll
@@ -885,6 +893,266 @@ __global__ void gather_x_kernel(LayerDesc d, const uint16_t* __restrict__ X, int
       gather8_from(X + mrow * ldx, *(const u32x4*)(d.pip + col), *(const u32x4*)(d.pip + col + 4));
 }
 
+// ---------------------------------------------------------------------------
+// W8A8: e4m3 weights times per-token e4m3 activations on
+// v_smfmac_f32_16x16x128_fp8_fp8 (one instruction per unit; no widening of
+// the weights).  The activations arrive quantised in X'p order ([M][K_p]
+// codes, quantize_tokens_kernel) and pass through the same double-buffered
+// LDS chunks as in stream_body, one byte per column.
+//
+// Operand layout of the fp8 instruction (16 rows x 128 columns of a 2:4
+// step): lane l (row l % 16, lane group h = l / 16) gives 16 stored values,
+// bytes 2j, 2j+1 (j < 8) for group j of its 32-column slice, positions from
+// nibble j of the index word; B lane l (column l % 16) gives 32 activations,
+// and A byte pair j of lane group h pairs with B lane group
+// 2(h & 1) + (j >= 4), bytes 16(h >> 1) + 4(j & 3) + pos.  For the unit
+// layout (the A operands of the bf16 instruction pair, see
+// spense_internal.h), B lane group h then needs the 32 staged columns at
+// base = 64(h & 1) + 32(h >> 1) of a sparse unit (32(h >> 1) of a dense
+// unit, whose fixed index word 0xEEEE4444 picks positions 0,1 of groups 0-3
+// and 2,3 of groups 4-7) with the middle two 8-column quarters swapped.
+// ---------------------------------------------------------------------------
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ i32x8 lds_b8(const uint8_t* p) {
+  const i32x4 q0 = *(const i32x4*)p, q1 = *(const i32x4*)(p + 16);
+  return __builtin_shufflevector(q0, q1, 0, 1, 4, 5, 2, 3, 6, 7);
+}
+
+__device__ __forceinline__ f32x4 smfmac_fp8(const u32x4& a, const i32x8& b, const f32x4& c, int idx) {
+  return __builtin_amdgcn_smfmac_f32_16x16x128_fp8_fp8(__builtin_bit_cast(i32x4, a), b, c, idx, 0, 0);
+}
+
+template <int NW, int NR, int P, int CH, int MT>
+__device__ __forceinline__ void stream8_body(const LayerDesc& d, const LinearArgs& a, const LinearPlan& p, int block,
+                                             int grid, uint8_t* xs_dyn, int* last_flag_p) {
+  static_assert(CH % P == 0, "a chunk must hold whole rings");
+  int& last_flag = *last_flag_p;
+  constexpr int kPitch = CH * 128 + 16;                    // staged row bytes: CH unit slots of 128 columns + pad
+  constexpr int kPieces = (16 * MT * CH * 8) / (NW * 64);  // 16-byte pieces per thread per chunk (full m-group)
+  static_assert(kPieces * NW * 64 == 16 * MT * CH * 8, "pieces must divide evenly");
+  constexpr bool kSplitAcc = NR == 1 && MT == 1;  // alternate two accumulators when nothing else interleaves
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  int b = block;
+  if (p.xcd_remap) b = (b % 8) * (grid / 8) + b / 8;
+  const int S = p.splits;
+  const int mg = b % p.mgroups;
+  const int rg = (b / p.mgroups) % p.rgroups;
+  const int s = b / (p.mgroups * p.rgroups);
+  const int64_t rt0 = ((int64_t)rg * NW + wave) * NR;
+  const int64_t ms0 = d.n_sm * s / S, ms1 = d.n_sm * (s + 1) / S;
+  const int64_t md0 = d.n_dm * s / S, md1 = d.n_dm * (s + 1) / S;
+  const int ns = (int)(ms1 - ms0), nd = (int)(md1 - md0);
+  const int total = ns + 2 * nd;  // units
+  const int nchunks = (total + CH - 1) / CH;
+  const int64_t m0 = (int64_t)mg * 16 * MT;
+  const int mloc = (int)(a.M - m0 < 16 * MT ? a.M - m0 : 16 * MT);
+  const int rows = (int)(a.M < 16 * MT ? a.M : 16 * MT);
+  const int m = lane & 15, g = lane >> 4;
+  const int64_t sbase = ms0, dbase = d.n_sm + 2 * md0 - ns;
+  const uint8_t* tile[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) tile[r] = d.wpack + (rt0 + r < d.NT ? rt0 + r : 0) * d.tile_bytes;
+  uint8_t* xbuf0 = xs_dyn;
+  uint8_t* xbuf1 = xs_dyn + rows * kPitch;
+  const uint8_t* X = (const uint8_t*)a.X + m0 * a.ldx;
+
+  auto unit_ptr = [&](int r, int k) { return tile[r] + (k + (k < ns ? sbase : dbase)) * 1024; };
+  auto idx_ptr = [&](int r, int k) { return k < ns ? tile[r] + d.idx_off + (ms0 + k) * 256 : unit_ptr(r, k); };
+  auto load_step = [&](UnitFrag<uint8_t>(&f)[NR], int k) {
+#pragma unroll
+    for (int r = 0; r < NR; ++r) load_unit<uint8_t>(f[r], unit_ptr(r, k), idx_ptr(r, k) + 4 * lane, lane);
+  };
+
+  TileOut to[NR];
+#pragma unroll
+  for (int r = 0; r < NR; ++r) to[r] = tile_out(d, rt0 + r < d.NT ? rt0 + r : 0, lane);
+
+  UnitFrag<uint8_t> wr[P][NR];
+  const bool stream = total > 0;
+  if (stream) {
+#pragma unroll
+    for (int i = 0; i < P; ++i) load_step(wr[i], i < total ? i : total - 1);
+  }
+
+  // piece e of a chunk: row = e / (8 CH), unit slot j = (e / 8) % CH, 16-column
+  // group c16 = e % 8 (a dense unit has 4).  Same fixed-count load scheme as
+  // stream_body: pieces outside the batch or the split read column 0 of the
+  // m-group's first row and are dropped.
+  u32x4 xv[kPieces];
+  auto issue_chunk = [&](int c) {
+#pragma unroll
+    for (int i = 0; i < kPieces; ++i) {
+      const int e = threadIdx.x + i * NW * 64;
+      const int row = e / (8 * CH);
+      const int j = (e / 8) % CH, c16 = e % 8;
+      const int k = c * CH + j;
+      const bool ok = row < mloc && k < total && (k < ns || c16 < 4);
+      const uint32_t rowoff = ok ? (uint32_t)(row * a.ldx) : 0u;
+      const int64_t col = !ok ? 0 : k < ns ? 128 * (ms0 + k) + 16 * c16 : d.K_sp + 128 * md0 + 64 * (k - ns) + 16 * c16;
+      xv[i] = *(const u32x4*)(X + rowoff + (uint32_t)col);
+    }
+  };
+  auto write_chunk = [&](uint8_t* buf) {
+#pragma unroll
+    for (int i = 0; i < kPieces; ++i) {
+      const int e = threadIdx.x + i * NW * 64;
+      const int row = e / (8 * CH);
+      if (row < mloc) *(u32x4*)(buf + row * kPitch + 128 * ((e / 8) % CH) + 16 * (e % 8)) = xv[i];
+    }
+  };
+
+  issue_chunk(0);
+  write_chunk(xbuf0);
+  __syncthreads();
+
+  f32x4 acc[NR * MT], acc1 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int t = 0; t < NR * MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  // activation rows beyond the batch read row 0 (their output columns are never stored)
+  int xoff[MT];
+#pragma unroll
+  for (int t = 0; t < MT; ++t) xoff[t] = (16 * t + m < mloc ? 16 * t + m : 0) * kPitch + 32 * (g >> 1);
+  const int sp_off = 64 * (g & 1);
+  auto consume = [&](const UnitFrag<uint8_t>(&f)[NR], int k, int j, const uint8_t* xb) {
+    const bool sp = k < ns;
+    const int off = 128 * j + (sp ? sp_off : 0);
+    if constexpr (kSplitAcc) {
+      const i32x8 B = lds_b8(xb + xoff[0] + off);
+      const int idx = sp ? (int)f[0].idx : (int)kDenseIdx;
+      if (j & 1) acc1 = smfmac_fp8(f[0].a, B, acc1, idx);
+      else acc[0] = smfmac_fp8(f[0].a, B, acc[0], idx);
+    } else {
+      int idx[NR];
+#pragma unroll
+      for (int r = 0; r < NR; ++r) idx[r] = sp ? (int)f[r].idx : (int)kDenseIdx;
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        const i32x8 B = lds_b8(xb + xoff[t] + off);
+#pragma unroll
+        for (int r = 0; r < NR; ++r) acc[r * MT + t] = smfmac_fp8(f[r].a, B, acc[r * MT + t], idx[r]);
+      }
+    }
+  };
+  const int nfull = total / CH;
+  for (int c = 0; c < nfull; ++c) {
+    const bool more = c + 1 < nchunks;
+    if (more) issue_chunk(c + 1);
+    const uint8_t* xb = (c & 1) ? xbuf1 : xbuf0;
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const int k = c * CH + j;
+      consume(wr[j % P], k, j, xb);
+      load_step(wr[j % P], k + P < total ? k + P : total - 1);
+    }
+    if (more) write_chunk((c & 1) ? xbuf0 : xbuf1);
+    __syncthreads();
+  }
+  if (nfull < nchunks) {
+    const int c = nfull;
+    const uint8_t* xb = (c & 1) ? xbuf1 : xbuf0;
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const int k = c * CH + j;
+      if (k < total) {
+        consume(wr[j % P], k, j, xb);
+        if (k + P < total) load_step(wr[j % P], k + P);
+      }
+    }
+  }
+  if constexpr (kSplitAcc) acc[0] += acc1;
+  finish_tile<NR, MT, true>(d, a, acc, to, rt0, m0, s, S, (int64_t)mg * p.rgroups + rg, &last_flag);
+}
+
+template <int NW, int NR, int P, int CH, int MT>
+__global__ __launch_bounds__(NW * 64) void linear_stream8_kernel(LayerDesc d, LinearArgs a, LinearPlan p) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t xs8_dyn[];
+  __shared__ int last_flag;
+  stream8_body<NW, NR, P, CH, MT>(d, a, p, blockIdx.x, gridDim.x, xs8_dyn, &last_flag);
+}
+
+// Per-token e4m3 quantisation, one workgroup of 256 threads per token: the
+// largest magnitude of the row (a max reduction, exact in any order), the
+// scale max/448 as an fp32 quotient (1 for an all-zero row), then each code
+// as the round-to-nearest-even e4m3 conversion of the fp32 quotient x / s
+// (within range by construction: |x / s| <= 448 up to the quotient's own
+// rounding, which still rounds to 448).  Output column j reads column
+// pip[j] when a column map is given (the X'p order of a layer; -1: zero).
+// With STAGE the row is kept in LDS between the two passes (the re-ordering
+// then gathers from LDS); otherwise the second pass reads it again.
+template <bool STAGE>
+__global__ __launch_bounds__(256) void quantize_tokens_kernel(const uint16_t* __restrict__ X, int64_t K, int64_t ldx,
+                                                              const int32_t* __restrict__ pip, int64_t Kout,
+                                                              uint8_t* __restrict__ Q, int64_t ldq,
+                                                              float* __restrict__ sx) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t xrow[];
+  __shared__ float wmax[4];
+  const int64_t mrow = blockIdx.x;
+  const uint16_t* x = X + mrow * ldx;
+  const int tid = threadIdx.x;
+  float amax = 0.f;
+  if (((uintptr_t)x % 16) == 0 && K % 8 == 0) {
+    // four 16-byte loads in flight per thread
+    for (int64_t k0 = 8 * (int64_t)tid; k0 < K; k0 += 4 * 8 * 256) {
+      u32x4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t k = k0 + u * 8 * 256;
+        v[u] = k < K ? *(const u32x4*)(x + k) : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t k = k0 + u * 8 * 256;
+        if (STAGE && k < K) *(u32x4*)(xrow + k) = v[u];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          amax = fmaxf(amax, __uint_as_float((v[u][q] & 0x7FFFu) << 16));
+          amax = fmaxf(amax, __uint_as_float((v[u][q] >> 16 & 0x7FFFu) << 16));
+        }
+      }
+    }
+  } else {
+    for (int64_t k = tid; k < K; k += 256) {
+      const uint16_t v = x[k];
+      if (STAGE) xrow[k] = v;
+      amax = fmaxf(amax, __uint_as_float((uint32_t)(v & 0x7FFFu) << 16));
+    }
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
+  if ((tid & 63) == 0) wmax[tid >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  const float scale = amax > 0.f ? amax / 448.0f : 1.0f;
+  if (tid == 0) sx[mrow] = scale;
+  const uint16_t* src_row = STAGE ? xrow : x;
+  uint8_t* q = Q + mrow * ldq;
+  const bool vec_out = ((uintptr_t)q % 4) == 0;
+  for (int64_t j0 = 4 * (int64_t)tid; j0 < Kout; j0 += 4 * 256) {
+    int src[4];
+    if (pip && j0 + 4 <= Kout) {
+      const u32x4 p4 = *(const u32x4*)(pip + j0);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) src[t] = (int)p4[t];
+    } else {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) src[t] = j0 + t < Kout ? (pip ? pip[j0 + t] : (int)(j0 + t)) : -1;
+    }
+    float v[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) v[t] = src[t] >= 0 ? __uint_as_float((uint32_t)src_row[src[t]] << 16) / scale : 0.f;
+    int w = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+    w = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], w, true);
+    if (vec_out && j0 + 4 <= Kout) {
+      *(uint32_t*)(q + j0) = (uint32_t)w;
+    } else {
+      for (int t = 0; t < 4 && j0 + t < Kout; ++t) q[j0 + t] = (uint8_t)((uint32_t)w >> (8 * t));
+    }
+  }
+}
+
 // fp32 weights: VALU, one wave per output row, lanes stride over groups and dense columns.
 __global__ __launch_bounds__(256) void linear_f32_kernel(LayerDesc d, LinearArgs a) {
   const int lane = threadIdx.x & 63;
@@ -1041,7 +1309,51 @@ hipError_t launch_linear_units(const Launch& L, hipStream_t s) {
   }
 }
 
+template <int NW, int NR, int P, int CH, int MT>
+hipError_t launch_stream8_k(const LayerDesc& d, const LinearArgs& a, const LinearPlan& p, hipStream_t s) {
+  if (p.waves != NW || p.nr != NR || p.depth != P || p.chunk != CH || p.mt != MT) return hipErrorInvalidValue;
+  auto k = linear_stream8_kernel<NW, NR, P, CH, MT>;
+  const hipError_t e = allow_lds(k, p.lds_bytes);
+  if (e != hipSuccess) return e;
+  const unsigned grid = (unsigned)((int64_t)p.rgroups * p.splits * p.mgroups);
+  k<<<grid, NW * 64, p.lds_bytes, s>>>(d, a, p);
+  return hipGetLastError();
+}
+
+// W8A8: e4m3 weights, activations already quantised into X'p order
+hipError_t launch_linear8(const LayerDesc& d, const LinearArgs& a, const LinearPlan& p, hipStream_t s) {
+  if (d.wdtype != DT_FP8 || !p.chunked || a.gather || !a.xscale) return hipErrorInvalidValue;
+  if (p.preset >= 0) {
+    switch (p.preset) {
+#define SPENSE_PRESET(i, nw, nr, pp, ch, mt) \
+  case i: return launch_stream8_k<nw, nr, pp, ch, mt>(d, a, p, s);
+      SPENSE_TILE_PRESETS(SPENSE_PRESET)
+#undef SPENSE_PRESET
+      default: return hipErrorInvalidValue;
+    }
+  }
+  switch (p.waves * 100 + p.depth) {
+    case 404: return launch_stream8_k<4, 1, 4, kStreamChunk, 1>(d, a, p, s);
+    case 408: return launch_stream8_k<4, 1, 8, kStreamChunk, 1>(d, a, p, s);
+    case 804: return launch_stream8_k<8, 1, 4, kStreamChunk, 1>(d, a, p, s);
+    case 808: return launch_stream8_k<8, 1, 8, kStreamChunk, 1>(d, a, p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
 }  // namespace
+
+hipError_t launch_quantize_tokens(const void* X, int64_t M, int64_t K, int64_t ldx, const int32_t* pip, int64_t Kout,
+                                  uint8_t* Q, int64_t ldq, float* sx, hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  // rows up to 32768 columns are kept in LDS between the passes (64 KB)
+  if (K <= 32768)
+    quantize_tokens_kernel<true><<<(unsigned)M, 256, (size_t)K * 2, s>>>((const uint16_t*)X, K, ldx, pip, Kout, Q,
+                                                                        ldq, sx);
+  else
+    quantize_tokens_kernel<false><<<(unsigned)M, 256, 0, s>>>((const uint16_t*)X, K, ldx, pip, Kout, Q, ldq, sx);
+  return hipGetLastError();
+}
 
 hipError_t launch_pack(const LayerDesc& d, const void* W, int64_t ldw, hipStream_t s) {
   switch (d.wdtype) {
@@ -1083,6 +1395,7 @@ hipError_t launch_export(const LayerDesc& d, void* vals, uint32_t* meta, uint8_t
 }
 
 hipError_t launch_linear(const LayerDesc& d, const LinearArgs& a, const LinearPlan& p, hipStream_t s) {
+  if (a.a8) return launch_linear8(d, a, p, s);
   const Launch L{{&d, nullptr}, {&a, nullptr}, {&p, nullptr}, false};
   switch (d.wdtype) {
     case DT_FP8: return launch_linear_units<uint8_t>(L, s);

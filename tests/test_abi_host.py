@@ -36,7 +36,7 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_strerror():
-    assert sdg.spense_abi_version() == 4
+    assert sdg.spense_abi_version() == 5
     lib = sdg._lib()
     for code in (0, -1, -2, -3, -4):
         assert lib.spense_strerror(code)
@@ -170,3 +170,18 @@ def test_score_and_select_reject_bad_arguments():
     assert lib.spense_select_dense(P, 8, 9, out.ctypes.data, None) == sdg.SPENSE_EINVAL
     assert lib.spense_select_dense(P, 8, -1, out.ctypes.data, None) == sdg.SPENSE_EINVAL
     assert lib.spense_select_dense(P, 8, 2, None, None) == sdg.SPENSE_EINVAL
+
+
+def test_w8a8_entry_points_reject_bad_arguments():
+    lib = sdg._lib()
+    P = FAKE_PTR
+    E = sdg.SPENSE_EINVAL
+    assert lib.spense_quantize_tokens(None, 4, 64, 64, P, 64, P, None) == E
+    assert lib.spense_quantize_tokens(P, 4, 64, 64, None, 64, P, None) == E
+    assert lib.spense_quantize_tokens(P, 4, 64, 64, P, 64, None, None) == E
+    assert lib.spense_quantize_tokens(P, 0, 64, 64, P, 64, P, None) == E
+    assert lib.spense_quantize_tokens(P, 4, 0, 64, P, 64, P, None) == E
+    assert lib.spense_quantize_tokens(P, 4, 64, 63, P, 64, P, None) == E
+    assert lib.spense_quantize_tokens(P, 4, 64, 64, P, 32, P, None) == E
+    assert lib.spense_quantize_tokens(P, (1 << 24) + 1, 64, 64, P, 64, P, None) == E
+    assert lib.spense_linear_w8a8(None, P, 1, 128, P, sdg.DT_F32, 64, 0, None) == E
