@@ -20,6 +20,10 @@ ARCH = "gfx950"
 # -packed-fp32-ops: keep the compiler from forming v_pk_{add,mul,fma}_f32.
 FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-unused-function",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-I", os.path.join(ROOT, "include")]
+# The linear kernels rely on fully unrolled epilogue loops over register-
+# blocked accumulator tiles (up to 64 16x16 tiles per wave); above the default
+# size limit of a forced unroll the tile array would live in scratch memory.
+EXTRA = {"spense_kernels.hip": ["-mllvm", "-pragma-unroll-threshold=200000"]}
 
 
 def _run(cmd):
@@ -36,14 +40,23 @@ def _run(cmd):
 def build(verbose: bool = False) -> str:
     objdir = os.path.join(ROOT, "_build")
     os.makedirs(objdir, exist_ok=True)
-    objs = []
-    for src in SOURCES:
+    objs, procs = [], []
+    for src in SOURCES:  # the translation units compile in parallel
         obj = os.path.join(objdir, os.path.basename(src) + ".o")
-        cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+        cmd = [HIPCC, *FLAGS, *EXTRA.get(os.path.basename(src), []), "-c", src, "-o", obj]
         if verbose:
             print(" ".join(cmd))
-        _run(cmd)
+        procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.PIPE, text=True)))
         objs.append(obj)
+    for cmd, pr in procs:
+        out, err = pr.communicate()
+        if pr.returncode != 0:
+            sys.stderr.write(out + err)
+            raise RuntimeError("command failed: " + " ".join(cmd))
+        noise = "is not a recognized feature for this target"
+        msg = "\n".join(l for l in (out + err).splitlines() if noise not in l)
+        if msg.strip():
+            sys.stderr.write(msg + "\n")
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:

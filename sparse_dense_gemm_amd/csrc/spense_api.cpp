@@ -116,6 +116,9 @@ int resolve_dense_set(int64_t K, const int32_t* dense_cols, int64_t n_dense, dou
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// output rows that may be written four columns at a time
+int32_t y_vec_ok(const void* Y, int64_t ldy) { return aligned16(Y) && ldy % 4 == 0 ? 1 : 0; }
+
 }  // namespace
 
 extern "C" {
@@ -439,6 +442,9 @@ static int64_t stream_lds_bytes(int64_t rows, int64_t chunk, int xbytes) {
 }
 
 constexpr int64_t kCUs = 256;             // compute units of the target GPU
+// activation leading dimensions (elements) the streaming kernels address with
+// 32-bit offsets (128 staged rows of bf16)
+constexpr int64_t kMaxLd = int64_t(1) << 23;
 constexpr int64_t kLdsPerCU = 160 * 1024;  // LDS bytes per CU
 
 // NT_fill: row tiles launched in the same grid (the layer's own, or both row
@@ -447,6 +453,9 @@ constexpr int64_t kLdsPerCU = 160 * 1024;  // LDS bytes per CU
 static int plan_linear(const spense_layer* h, int64_t M, int32_t splits, int64_t NT_fill, LinearPlan& p,
                        bool force_chunked = false, int xbytes = 2) {
   const LayerDesc& d = h->d;
+  // the streaming kernels address a wave's row tiles and a staged m-group of
+  // activations with 32-bit offsets
+  if (d.tile_bytes >= (int64_t(1) << 29) || d.K_p >= kMaxLd) return SPENSE_EUNSUPPORTED;
   const int64_t steps = std::max<int64_t>(d.n_sm, d.n_dm);
   const int64_t max_splits = std::max<int64_t>(1, std::min<int64_t>(steps, 64));
   if (splits < 0 || splits > max_splits) return SPENSE_EINVAL;
@@ -501,13 +510,13 @@ static int plan_linear(const spense_layer* h, int64_t M, int32_t splits, int64_t
   };
   constexpr int kNumPresets = (int)(sizeof(kPresets) / sizeof(kPresets[0]));
   // The largest blocking that still gives about 150 workgroups (measured on
-  // the 36B-class layers for M = 32..2048, both activation types: within 2%
-  // of the best preset per shape in total).  Eight waves per workgroup with
-  // four row tiles and four m-tiles each when there are enough tiles (ring
-  // depth 2 and two-unit chunks for bf16 activations; depth 4 and four-unit
-  // chunks for e4m3 codes, whose fragments take half the registers), then
-  // eight waves with two row tiles, then two m-tiles; at M <= 32 one m-group
-  // of two m-tiles with two row tiles per wave, or a single row tile.
+  // the 36B-class layers for M = 32..2048, both activation types: within a
+  // few percent of the best preset per shape in total).  Eight waves per
+  // workgroup with four m-tiles each when there are enough tiles (four row
+  // tiles per wave for bf16 activations, two for e4m3 codes, whose smaller
+  // staged rows let more workgroups share a CU), then eight waves with two
+  // row tiles and a deeper ring, then two m-tiles; at M <= 32 one m-group of
+  // two m-tiles with two row tiles per wave, or a single row tile.
   auto workgroups = [&](int i) {
     const Preset& c = kPresets[i];
     return (NT_fill + c.nw * c.nr - 1) / (c.nw * c.nr) * ((M + 16 * c.mt - 1) / (16 * c.mt));
@@ -518,7 +527,7 @@ static int plan_linear(const spense_layer* h, int64_t M, int32_t splits, int64_t
     pre = workgroups(2) >= kEnough ? 2 : 7;
   } else {
     pre = 0;
-    for (int c : {xbytes == 1 ? 14 : 9, 12, 2})
+    for (int c : {xbytes == 1 ? 6 : 9, 12, 2})
       if (workgroups(c) >= kEnough) {
         pre = c;
         break;
@@ -695,6 +704,7 @@ int spense_linear_splits(spense_handle h, const void* X, int32_t xdtype, int64_t
   if (h->split == 2) return SPENSE_EINVAL;  // a GLU block runs through spense_glu
   const LayerDesc& d = h->d;
   if (M < 1 || M > (int64_t(1) << 24) || ldx < d.K || ldy < d.N) return SPENSE_EINVAL;
+  if (ldx >= kMaxLd) return SPENSE_EUNSUPPORTED;
   if (!valid_dtype(xdtype) || !valid_dtype(ydtype)) return SPENSE_EINVAL;
   if (ydtype == SPENSE_FP8_E4M3) return SPENSE_EUNSUPPORTED;
   const int32_t want_x = d.wdtype == SPENSE_F32 ? SPENSE_F32 : SPENSE_BF16;
@@ -707,6 +717,7 @@ int spense_linear_splits(spense_handle h, const void* X, int32_t xdtype, int64_t
   a.ldx = ldx;
   a.Y = Y;
   a.ldy = ldy;
+  a.yvec = y_vec_ok(Y, ldy);
   a.ydtype = ydtype;
   if (d.wdtype == SPENSE_F32) {
     if (splits > 1) return SPENSE_EINVAL;
@@ -736,6 +747,7 @@ int spense_linear_w8a8(spense_handle h, const void* X, int64_t M, int64_t ldx, v
   const LayerDesc& d = h->d;
   if (d.wdtype != SPENSE_FP8_E4M3) return SPENSE_EUNSUPPORTED;
   if (M < 1 || M > (int64_t(1) << 24) || ldx < d.K || ldy < d.N) return SPENSE_EINVAL;
+  if (d.K_p >= kMaxLd) return SPENSE_EUNSUPPORTED;
   if (ydtype != SPENSE_F32 && ydtype != SPENSE_BF16) return SPENSE_EINVAL;
   hipStream_t s = (hipStream_t)stream;
   LinearPlan p{};
@@ -765,6 +777,7 @@ int spense_linear_w8a8(spense_handle h, const void* X, int64_t M, int64_t ldx, v
   a.ldx = d.K_p;
   a.Y = Y;
   a.ldy = ldy;
+  a.yvec = y_vec_ok(Y, ldy);
   a.ydtype = ydtype;
   a.splits = p.splits;
   a.a8 = 1;
@@ -780,6 +793,7 @@ int spense_glu(spense_handle h, const void* X, int64_t M, int64_t ldx, void* A, 
   if (!h || h->split != 2 || !X || !A || !Y) return SPENSE_EINVAL;
   const int64_t H = h->d.K, I = h->N_s + h->N_d;
   if (M < 1 || M > (int64_t(1) << 24) || ldx < H || lda < I || ldy < H) return SPENSE_EINVAL;
+  if (ldx >= kMaxLd || lda >= kMaxLd) return SPENSE_EUNSUPPORTED;
   if (ydtype != SPENSE_F32 && ydtype != SPENSE_BF16) return SPENSE_EINVAL;
   hipStream_t s = (hipStream_t)stream;
   // gate/up (output-split) with the SiLU * up epilogue -> A [M, I] bf16, rho order
@@ -789,6 +803,7 @@ int spense_glu(spense_handle h, const void* X, int64_t M, int64_t ldx, void* A, 
   a.ldx = ldx;
   a.Y = A;
   a.ldy = lda;
+  a.yvec = y_vec_ok(A, lda);
   a.ydtype = SPENSE_BF16;
   a.glu = 1;
   spense_layer* parts[2] = {nullptr, nullptr};
@@ -804,6 +819,7 @@ int spense_glu(spense_handle h, const void* X, int64_t M, int64_t ldx, void* A, 
   b.ldx = lda;
   b.Y = Y;
   b.ldy = ldy;
+  b.yvec = y_vec_ok(Y, ldy);
   b.ydtype = ydtype;
   spense_layer* dp[1] = {h->down};
   return run_layers(dp, 1, M, 0, b, s);

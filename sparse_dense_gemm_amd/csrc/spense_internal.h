@@ -78,6 +78,7 @@ struct LinearArgs {
   int32_t splits;
   int32_t gather;        // effective gather mode for this call
   int32_t glu;           // 1: packed rows come in (gate, up) pairs; write silu(gate) * up at the pair's column
+  int32_t yvec;          // 1: Y is 16-byte aligned and ldy % 4 == 0 (four consecutive columns in one store)
   int32_t a8;            // 1: X is e4m3 codes [M][K_p] in X'p order, with per-token scales xscale (W8A8)
   const float* xscale;   // [M] (a8 only)
   float* ws;             // [splits][M][NT*16] fp32 partials (splits > 1)
@@ -119,7 +120,9 @@ struct LinearPlan {
   X(13, 4, 4, 4, 4, 4)         \
   X(14, 8, 4, 4, 4, 4)         \
   X(15, 4, 4, 2, 2, 8)         \
-  X(16, 4, 2, 4, 4, 8)
+  X(16, 4, 2, 4, 4, 8)         \
+  X(17, 4, 8, 2, 2, 8)         \
+  X(18, 4, 8, 2, 2, 4)
 
 constexpr int kStreamChunk = 8;  // units per activation chunk of linear_stream_kernel
 

@@ -151,6 +151,18 @@ __device__ __forceinline__ void store_y(const LinearArgs& a, int64_t m, int64_t 
   else ((uint16_t*)a.Y)[m * a.ldy + n] = (uint16_t)bf16_rne(y);
 }
 
+// Y[m][n..n+3] = y in one store: n % 4 == 0, Y 16-byte aligned, ldy % 4 == 0
+__device__ __forceinline__ void store_y4(const LinearArgs& a, int64_t m, int64_t n, const f32x4& y) {
+  if (a.ydtype == DT_F32) {
+    *(f32x4*)((float*)a.Y + m * a.ldy + n) = y;
+  } else {
+    uint2 v;
+    v.x = bf16_rne(y[0]) | (bf16_rne(y[1]) << 16);
+    v.y = bf16_rne(y[2]) | (bf16_rne(y[3]) << 16);
+    *(uint2*)((uint16_t*)a.Y + m * a.ldy + n) = v;
+  }
+}
+
 // Writes Y (S == 1) or this split's partial; with S > 1 the last workgroup of
 // the tile adds the partials in split order.  acc: lane l, register r =
 // Y^T[n = 16rt + 4(l/16) + r][m = m0 + 16mt + l%16].
@@ -201,18 +213,25 @@ __device__ __forceinline__ void finish_tile(const LayerDesc& d, const LinearArgs
           const float g = sum[q] * to[r].sc[q], u = sum[q + 1] * to[r].sc[q + 1];
           if (col >= 0) store_y(a, m, col, g / (1.0f + __expf(-g)) * u);
         }
-      } else if constexpr (XS) {
-        const float xs = a.xscale[m];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = (int)to[r].col[q];
-          if (col >= 0) store_y(a, m, col, sum[q] * to[r].sc[q] * xs);
-        }
       } else {
+        f32x4 y;
+        if constexpr (XS) {
+          const float xs = a.xscale[m];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int col = (int)to[r].col[q];
-          if (col >= 0) store_y(a, m, col, sum[q] * to[r].sc[q]);
+          for (int q = 0; q < 4; ++q) y[q] = sum[q] * to[r].sc[q] * xs;
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) y[q] = sum[q] * to[r].sc[q];
+        }
+        // the lane's four rows are usually four consecutive output columns
+        // (every input-split layer): one 8- or 16-byte store instead of four
+        const u32x4 c = to[r].col;
+        if (a.yvec && (int)c.x >= 0 && (c.x & 3u) == 0 && c.y == c.x + 1 && c.z == c.x + 2 && c.w == c.x + 3) {
+          store_y4(a, m, c.x, y);
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if ((int)c[q] >= 0) store_y(a, m, c[q], y[q]);
         }
       }
     }
@@ -692,19 +711,80 @@ __global__ __launch_bounds__(NW * 64) void linear_decode2_kernel(LayerDesc d0, L
 // grow with the split width.  One barrier per chunk; it waits on LDS only, so
 // the weight ring stays in flight across it.  Each wave owns NR consecutive
 // 16-row tiles and MT m-tiles of 16 activation rows: every weight unit loaded
-// from HBM feeds MT pairs of products, and every activation fragment read
-// from LDS feeds NR of them.  Activations are read as a contiguous X'p (for
-// a chosen dense set the host gathers it into a workspace first).
+// from HBM feeds MT products (pairs of products for bf16 activations), and
+// every activation fragment read from LDS feeds NR of them.  Activations are
+// read as a contiguous X'p (for a chosen dense set the host gathers, or
+// quantises, it into a workspace first).
+//
+// All global loads are buffer loads: the wave's weight units at a per-wave
+// resource plus a uniform (scalar) offset and the lane's fixed 16-byte slot,
+// the activation pieces at a per-thread offset that is computed once per
+// chunk.  No per-load 64-bit address arithmetic, and pieces outside the batch
+// or the split take an offset beyond the resource, which reads zero.
+//
+// W8A8 (A8): e4m3 activation codes on v_smfmac_f32_16x16x128_fp8_fp8, one
+// instruction per unit and no widening of the weights.  Operand layout of
+// that instruction (16 rows x 128 columns of a 2:4 step): lane l (row l % 16,
+// lane group h = l / 16) gives 16 stored values, bytes 2j, 2j+1 (j < 8) for
+// group j of its 32-column slice, positions from nibble j of the index word;
+// B lane l (column l % 16) gives 32 activations, and A byte pair j of lane
+// group h pairs with B lane group 2(h & 1) + (j >= 4), bytes
+// 16(h >> 1) + 4(j & 3) + pos.  For the unit layout (the A operands of the
+// bf16 instruction pair, see spense_internal.h), B lane group h then needs
+// the 32 staged columns at base = 64(h & 1) + 32(h >> 1) of a sparse unit
+// (32(h >> 1) of a dense unit, whose fixed index word 0xEEEE4444 picks
+// positions 0,1 of groups 0-3 and 2,3 of groups 4-7) with the middle two
+// 8-column quarters swapped; the swap is done when the chunk is staged, so a
+// fragment is 32 contiguous bytes of LDS.
 // ---------------------------------------------------------------------------
-template <typename WT, int NW, int NR, int P, int CH, int MT>
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+
+// Raw buffer resource over [base, base + bytes): a load at an offset beyond
+// `bytes` returns zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+constexpr uint32_t kOutOfRange = 0x80000000u;  // beyond every resource built here (all below 2 GB)
+
+__device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+}
+__device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
+}
+
+// 32 contiguous bytes of LDS as one B operand
+__device__ __forceinline__ bf16x16 lds_b16(const uint8_t* p) {
+  return as_bf16x16(*(const u32x4*)p, *(const u32x4*)(p + 16));
+}
+__device__ __forceinline__ i32x8 lds_b8(const uint8_t* p) {
+  const i32x4 q0 = *(const i32x4*)p, q1 = *(const i32x4*)(p + 16);
+  return __builtin_shufflevector(q0, q1, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ __forceinline__ f32x4 smfmac_fp8(const u32x4& a, const i32x8& b, const f32x4& c, int idx) {
+  return __builtin_amdgcn_smfmac_f32_16x16x128_fp8_fp8(__builtin_bit_cast(i32x4, a), b, c, idx, 0, 0);
+}
+
+template <typename WT, bool A8, int NW, int NR, int P, int CH, int MT>
 __device__ __forceinline__ void stream_body(const LayerDesc& d, const LinearArgs& a, const LinearPlan& p, int block,
-                                            int grid, uint16_t* xs_dyn, int* last_flag_p) {
+                                            int grid, uint8_t* xs, int* last_flag_p) {
   static_assert(CH % P == 0, "a chunk must hold whole rings");
+  static_assert(!A8 || sizeof(WT) == 1, "W8A8 takes e4m3 weights");
+  constexpr int XB = A8 ? 1 : 2;           // bytes per staged activation
+  constexpr int kSlot = 128 * XB;          // bytes of one unit slot (128 columns)
+  constexpr int kPitch = CH * kSlot + 16;  // staged row: CH unit slots + pad
+  constexpr int kPPU = kSlot / 16;         // 16-byte pieces per unit slot
+  constexpr int kPPR = CH * kPPU;          // pieces per staged row
+  constexpr int kThreads = NW * 64;
+  static_assert(kThreads % kPPR == 0, "every piece of a thread sits at the same slot position");
+  constexpr int kRowStep = kThreads / kPPR;  // rows between a thread's pieces
+  constexpr int kPieces = 16 * MT / kRowStep;
+  static_assert(kPieces * kRowStep == 16 * MT, "pieces must divide evenly");
+  constexpr bool kSplitAcc = NR == 1 && MT == 1;  // alternate two accumulators when nothing else interleaves
+  constexpr uint32_t UB = sizeof(WT) == 1 ? 1024u : 2048u;
   int& last_flag = *last_flag_p;
-  constexpr int kPitch2 = CH * 128 + 8;                      // staged row: CH unit slots of 128 columns + pad
-  constexpr int kPieces = (16 * MT * CH * 16) / (NW * 64);  // 16-byte pieces per thread per chunk (full m-group)
-  static_assert(kPieces * NW * 64 == 16 * MT * CH * 16, "pieces must divide evenly");
-  constexpr bool kSplitAcc = NR == 1 && MT == 1;  // two accumulators when there is nothing to interleave
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   // Workgroups are dealt to the 8 XCDs round-robin.  With several m-groups the
@@ -727,69 +807,103 @@ __device__ __forceinline__ void stream_body(const LayerDesc& d, const LinearArgs
   const int mloc = (int)(a.M - m0 < 16 * MT ? a.M - m0 : 16 * MT);  // activation rows of this m-group
   const int rows = (int)(a.M < 16 * MT ? a.M : 16 * MT);            // rows of one staged buffer
   const int m = lane & 15, g = lane >> 4;
-  const int64_t sbase = ms0, dbase = d.n_sm + 2 * md0 - ns;
-  // row tiles past the end read tile 0 (valid memory); their results are never stored
-  const uint8_t* tile[NR];
-#pragma unroll
-  for (int r = 0; r < NR; ++r) tile[r] = d.wpack + (rt0 + r < d.NT ? rt0 + r : 0) * d.tile_bytes;
-  uint16_t* xbuf0 = xs_dyn;
-  uint16_t* xbuf1 = xs_dyn + rows * kPitch2;
-  const uint16_t* X = (const uint16_t*)a.X + m0 * a.ldx;
 
-  auto unit_ptr = [&](int r, int k) { return tile[r] + (k + (k < ns ? sbase : dbase)) * kUnit<WT>; };
-  auto idx_ptr = [&](int r, int k) { return k < ns ? tile[r] + d.idx_off + (ms0 + k) * 256 : unit_ptr(r, k); };
-  // first column of unit k in the split's column list: sparse units 128 wide, dense units 64
-  auto unit_lcol = [&](int k) { return k < ns ? 128 * k : 128 * ns + 64 * (k - ns); };
-  auto load_step = [&](UnitFrag<WT>(&f)[NR], int k) {
+  // weights: one resource from the wave's first row tile (the last tile for a
+  // wave wholly past the end); row tiles past the end read that first tile
+  // (their results are never stored)
+  const int64_t bt = rt0 < d.NT ? rt0 : d.NT - 1;
+  const int64_t ntile = d.NT - bt < NR ? d.NT - bt : NR;
+  const __amdgpu_buffer_rsrc_t wres = make_rsrc(d.wpack + bt * d.tile_bytes, (uint32_t)(ntile * d.tile_bytes));
+  uint32_t roff[NR];
 #pragma unroll
-    for (int r = 0; r < NR; ++r) load_unit<WT>(f[r], unit_ptr(r, k), idx_ptr(r, k) + 4 * lane, lane);
+  for (int r = 0; r < NR; ++r) roff[r] = rt0 + r < d.NT ? (uint32_t)(r * d.tile_bytes) : 0u;
+  const uint32_t s_unit0 = (uint32_t)(ms0 * UB);                              // sparse unit 0 of the split
+  const uint32_t d_unit0 = (uint32_t)((d.n_sm + 2 * md0) * UB) - (uint32_t)ns * UB;  // + k * UB for dense k
+  const uint32_t s_idx0 = (uint32_t)(d.idx_off + ms0 * kIdxBlock);
+  auto load_step = [&](UnitFrag<WT>(&f)[NR], int k) {
+    const bool sp = k < ns;
+    const uint32_t uoff = (sp ? s_unit0 : d_unit0) + (uint32_t)k * UB;
+    // dense units load their "index" from the unit itself and replace it at use
+    const uint32_t ioff = sp ? s_idx0 + (uint32_t)k * kIdxBlock : uoff;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) {
+      if constexpr (sizeof(WT) == 1) {
+        f[r].a = buf_load16(wres, 16u * lane, roff[r] + uoff);
+      } else {
+        f[r].a0 = buf_load16(wres, 16u * lane, roff[r] + uoff);
+        f[r].a1 = buf_load16(wres, 16u * lane, roff[r] + uoff + 1024u);
+      }
+      f[r].idx = buf_load4(wres, 4u * lane, roff[r] + ioff);
+    }
   };
 
+  // Output scales and columns: loaded up front for small tiles (the epilogue
+  // then does not wait on memory); large tiles load them at the end, since
+  // 8 registers per row tile held through the K loop would not fit.
+  constexpr bool kEarlyOut = NR * MT < 32;
   TileOut to[NR];
+  auto load_out = [&]() {
 #pragma unroll
-  for (int r = 0; r < NR; ++r) to[r] = tile_out(d, rt0 + r < d.NT ? rt0 + r : 0, lane);
+    for (int r = 0; r < NR; ++r) to[r] = tile_out(d, rt0 + r < d.NT ? rt0 + r : 0, lane);
+  };
+  if constexpr (kEarlyOut) load_out();
 
   UnitFrag<WT> wr[P][NR];
-  // every wave streams (waves whose row tiles are all past the end stream tile
-  // 0), so all waves of the workgroup meet the same barriers
+  // every wave streams (waves whose row tiles are all past the end stream a
+  // valid tile), so all waves of the workgroup meet the same barriers
   const bool stream = total > 0;
   if (stream) {
 #pragma unroll
     for (int i = 0; i < P; ++i) load_step(wr[i], i < total ? i : total - 1);
   }
 
-  // piece e of a chunk: row = e / (16 CH), unit slot j = (e / 16) % CH, 8-column group c8 = e % 16.
-  // Loads are issued here and only consumed by write_chunk (after the chunk's
-  // compute).  Every thread issues the same loads whatever its piece: pieces
-  // outside the batch or the split read row 0, column 0 (X'p holds at least
-  // 128 columns) and their values are never used.  With a fixed load count
-  // the wait before write_chunk covers just these loads, so the weight ring
-  // stays in flight.  The sparse region of X'p starts at column 0, the dense
-  // one at K_sp (equal to K_s when X itself is X'p).
+  // Staging: thread t owns piece position tp = t % kPPR of the staged rows
+  // t / kPPR + i * kRowStep (i < kPieces): unit slot jslot, 16-byte piece cp.
+  const uint8_t* Xg = (const uint8_t*)a.X + m0 * a.ldx * XB;
+  const __amdgpu_buffer_rsrc_t xres = make_rsrc(Xg, (uint32_t)((int64_t)mloc * a.ldx * XB));
+  const int tp = (int)threadIdx.x % kPPR;
+  const int jslot = tp / kPPU, cp = tp % kPPU;
+  const int row0 = (int)threadIdx.x / kPPR;
+  const uint32_t xrow0 = (uint32_t)(row0 * a.ldx * XB), xrow_step = (uint32_t)(kRowStep * a.ldx * XB);
+  // LDS destination of piece 0 (the others follow every kRowStep rows); W8A8
+  // pieces are written as two 8-byte halves with the middle quarters of every
+  // 32-byte group swapped
+  const int dst0 = row0 * kPitch + kSlot * jslot + (A8 ? 32 * (cp >> 1) + 8 * (cp & 1) : 16 * cp);
+  const uint32_t s_col0 = (uint32_t)(128 * ms0 * XB) + 16u * cp;
+  const uint32_t d_col0 = (uint32_t)((d.K_sp + 128 * md0) * XB) + 16u * cp;
   u32x4 xv[kPieces];
   auto issue_chunk = [&](int c) {
+    const int k = c * CH + jslot;
+    const bool kv = k < total && (k < ns || cp < kPPU / 2);
+    const uint32_t colb = k < ns ? s_col0 + (uint32_t)(128 * XB * k) : d_col0 + (uint32_t)(64 * XB * (k - ns));
 #pragma unroll
     for (int i = 0; i < kPieces; ++i) {
-      const int e = threadIdx.x + i * NW * 64;
-      const int row = e / (16 * CH);
-      const int j = (e / 16) % CH, c8 = e % 16;
-      const int k = c * CH + j;
-      const bool ok = row < mloc && k < total && (k < ns || c8 < 8);
-      const int lc = ok ? unit_lcol(k) + 8 * c8 : 0;
-      const uint32_t rowoff = ok ? (uint32_t)(row * a.ldx) : 0u;
-      const int64_t col = !ok ? 0 : k < ns ? 128 * ms0 + lc : d.K_sp + 128 * md0 + (lc - 128 * ns);
-      xv[i] = *(const u32x4*)(X + rowoff + (uint32_t)col);
+      const bool ok = kv && row0 + i * kRowStep < mloc;
+      xv[i] = buf_load16(xres, ok ? xrow0 + i * xrow_step + colb : kOutOfRange, 0u);
     }
   };
-  auto write_chunk = [&](uint16_t* buf) {
+  // A piece of a row beyond the batch is not stored, but its load is still
+  // consumed (an empty use): a load left pending on one path would make the
+  // next chunk's loads wait for every older load before reusing its registers.
+  auto write_chunk = [&](uint8_t* buf) {
 #pragma unroll
     for (int i = 0; i < kPieces; ++i) {
-      const int e = threadIdx.x + i * NW * 64;
-      const int row = e / (16 * CH);
-      if (row < mloc) *(u32x4*)(buf + row * kPitch2 + 128 * ((e / 16) % CH) + 8 * (e % 16)) = xv[i];
+      if (row0 + i * kRowStep < mloc) {
+        uint8_t* q = buf + dst0 + i * kRowStep * kPitch;
+        if constexpr (A8) {
+          *(uint64_t*)q = (uint64_t)xv[i].x | ((uint64_t)xv[i].y << 32);
+          *(uint64_t*)(q + 16) = (uint64_t)xv[i].z | ((uint64_t)xv[i].w << 32);
+        } else {
+          *(u32x4*)q = xv[i];
+        }
+      } else {
+        asm volatile("" : : "v"(xv[i]));
+      }
     }
   };
 
+  uint8_t* xbuf0 = xs;
+  uint8_t* xbuf1 = xs + rows * kPitch;
   issue_chunk(0);
   write_chunk(xbuf0);
   __syncthreads();
@@ -801,56 +915,97 @@ __device__ __forceinline__ void stream_body(const LayerDesc& d, const LinearArgs
   // depends only on B column m, and those columns are never stored.
   int xoff[MT];
 #pragma unroll
-  for (int t = 0; t < MT; ++t) xoff[t] = (16 * t + m < mloc ? 16 * t + m : 0) * kPitch2 + 16 * g;
-  auto consume = [&](const UnitFrag<WT>(&f)[NR], int k, int j, const uint16_t* xb) {
+  for (int t = 0; t < MT; ++t) xoff[t] = (16 * t + m < mloc ? 16 * t + m : 0) * kPitch + 32 * (A8 ? (g >> 1) : g);
+  const int sp_off = A8 ? 64 * (g & 1) : 128;  // sparse-unit B offset: lane group (W8A8) or second step (bf16)
+  auto consume = [&](const UnitFrag<WT>(&f)[NR], int k, int j, const uint8_t* xb) {
     const bool sp = k < ns;
-    const int col1 = sp ? 128 * j + 64 : 128 * j;
-    if constexpr (kSplitAcc) {
-      mac_unit<WT>(acc[0], acc1, f[0], sp ? (int)f[0].idx : (int)kDenseIdx, lds_b(xb + xoff[0] + 128 * j),
-                   lds_b(xb + xoff[0] + col1));
+    if constexpr (A8) {
+      const int off = kSlot * j + (sp ? sp_off : 0);
+      if constexpr (kSplitAcc) {
+        const i32x8 B = lds_b8(xb + xoff[0] + off);
+        const int idx = sp ? (int)f[0].idx : (int)kDenseIdx;
+        if (j & 1) acc1 = smfmac_fp8(f[0].a, B, acc1, idx);
+        else acc[0] = smfmac_fp8(f[0].a, B, acc[0], idx);
+      } else {
+        int idx[NR];
+#pragma unroll
+        for (int r = 0; r < NR; ++r) idx[r] = sp ? (int)f[r].idx : (int)kDenseIdx;
+        if constexpr (MT <= 4) {  // every fragment of the unit up front
+          i32x8 B[MT];
+#pragma unroll
+          for (int t = 0; t < MT; ++t) B[t] = lds_b8(xb + xoff[t] + off);
+#pragma unroll
+          for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int r = 0; r < NR; ++r) acc[r * MT + t] = smfmac_fp8(f[r].a, B[t], acc[r * MT + t], idx[r]);
+        } else {  // one fragment ahead
+          i32x8 Bc = lds_b8(xb + xoff[0] + off);
+#pragma unroll
+          for (int t = 0; t < MT; ++t) {
+            i32x8 Bn;
+            if (t + 1 < MT) Bn = lds_b8(xb + xoff[t + 1] + off);
+#pragma unroll
+            for (int r = 0; r < NR; ++r) acc[r * MT + t] = smfmac_fp8(f[r].a, Bc, acc[r * MT + t], idx[r]);
+            if (t + 1 < MT) Bc = Bn;
+          }
+        }
+      }
     } else {
-      bf16x8 A0[NR], A1[NR];
-      int idx[NR];
-#pragma unroll
-      for (int r = 0; r < NR; ++r) {
-        unit_a<WT>(f[r], A0[r], A1[r]);
-        idx[r] = sp ? (int)f[r].idx : (int)kDenseIdx;
-      }
+      const int off0 = kSlot * j, off1 = off0 + (sp ? sp_off : 0);
+      bf16x16 B0[MT], B1[MT];
 #pragma unroll
       for (int t = 0; t < MT; ++t) {
-        const bf16x16 B0 = lds_b(xb + xoff[t] + 128 * j);
-#pragma unroll
-        for (int r = 0; r < NR; ++r) acc[r * MT + t] = smfmac_bf16<0>(A0[r], B0, acc[r * MT + t], idx[r]);
+        B0[t] = lds_b16(xb + xoff[t] + off0);
+        B1[t] = lds_b16(xb + xoff[t] + off1);
       }
+      if constexpr (kSplitAcc) {
+        mac_unit<WT>(acc[0], acc1, f[0], sp ? (int)f[0].idx : (int)kDenseIdx, B0[0], B1[0]);
+      } else {
+        bf16x8 A0[NR], A1[NR];
+        int idx[NR];
 #pragma unroll
-      for (int t = 0; t < MT; ++t) {
-        const bf16x16 B1 = lds_b(xb + xoff[t] + col1);
+        for (int r = 0; r < NR; ++r) {
+          unit_a<WT>(f[r], A0[r], A1[r]);
+          idx[r] = sp ? (int)f[r].idx : (int)kDenseIdx;
+        }
 #pragma unroll
-        for (int r = 0; r < NR; ++r) acc[r * MT + t] = smfmac_bf16<1>(A1[r], B1, acc[r * MT + t], idx[r]);
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+          for (int r = 0; r < NR; ++r) acc[r * MT + t] = smfmac_bf16<0>(A0[r], B0[t], acc[r * MT + t], idx[r]);
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+#pragma unroll
+          for (int r = 0; r < NR; ++r) acc[r * MT + t] = smfmac_bf16<1>(A1[r], B1[t], acc[r * MT + t], idx[r]);
       }
     }
   };
-  // Full chunks: every ring slot is consumed and refilled unconditionally and
-  // the loop body has no branch around ring registers (a merge of two paths
-  // would copy them, and a copy must wait for their loads to land).
+  // Full chunks: every ring slot is consumed and refilled, and the next
+  // chunk is loaded and staged, unconditionally (after the last chunk that
+  // stages zeros into the idle buffer), so every iteration issues the same
+  // loads and the loop body has no branch around ring registers (a merge of
+  // two paths would copy them, and a copy must wait for their loads to land).
+  // The scheduling barriers keep each refill right after the products that
+  // free its ring slot (left alone, the scheduler sinks every load of the
+  // chunk below its last product, so the next chunk waits on them at once).
   const int nfull = total / CH;
   for (int c = 0; c < nfull; ++c) {
-    const bool more = c + 1 < nchunks;
-    if (more) issue_chunk(c + 1);
-    const uint16_t* xb = (c & 1) ? xbuf1 : xbuf0;
+    issue_chunk(c + 1);
+    __builtin_amdgcn_sched_barrier(0);
+    const uint8_t* xb = (c & 1) ? xbuf1 : xbuf0;
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
       const int k = c * CH + j;
       consume(wr[j % P], k, j, xb);
       load_step(wr[j % P], k + P < total ? k + P : total - 1);
+      __builtin_amdgcn_sched_barrier(0);
     }
-    if (more) write_chunk((c & 1) ? xbuf0 : xbuf1);
+    write_chunk((c & 1) ? xbuf0 : xbuf1);
     __syncthreads();
   }
   // last, partial chunk (never followed by another): its first units are in the ring
   if (nfull < nchunks) {
     const int c = nfull;
-    const uint16_t* xb = (c & 1) ? xbuf1 : xbuf0;
+    const uint8_t* xb = (c & 1) ? xbuf1 : xbuf0;
 #pragma unroll
     for (int j = 0; j < CH; ++j) {
       const int k = c * CH + j;
@@ -861,24 +1016,34 @@ __device__ __forceinline__ void stream_body(const LayerDesc& d, const LinearArgs
     }
   }
   if constexpr (kSplitAcc) acc[0] += acc1;
-  finish_tile<NR, MT>(d, a, acc, to, rt0, m0, s, S, (int64_t)mg * p.rgroups + rg, &last_flag);
+  if constexpr (!kEarlyOut) load_out();
+  finish_tile<NR, MT, A8>(d, a, acc, to, rt0, m0, s, S, (int64_t)mg * p.rgroups + rg, &last_flag);
 }
 
 template <typename WT, int NW, int NR, int P, int CH, int MT>
 __global__ __launch_bounds__(NW * 64) void linear_stream_kernel(LayerDesc d, LinearArgs a, LinearPlan p) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t xs_dyn[];
+  extern __shared__ __attribute__((aligned(16))) uint8_t xsb_dyn[];
   __shared__ int last_flag;
-  stream_body<WT, NW, NR, P, CH, MT>(d, a, p, blockIdx.x, gridDim.x, xs_dyn, &last_flag);
+  stream_body<WT, false, NW, NR, P, CH, MT>(d, a, p, blockIdx.x, gridDim.x, xsb_dyn, &last_flag);
 }
 
 template <typename WT, int NW, int NR, int P, int CH, int MT>
 __global__ __launch_bounds__(NW * 64) void linear_stream2_kernel(LayerDesc d0, LinearArgs a0, LinearPlan p0,
                                                                  LayerDesc d1, LinearArgs a1, LinearPlan p1) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t xs_dyn[];
+  extern __shared__ __attribute__((aligned(16))) uint8_t xsb_dyn[];
   __shared__ int last_flag;
   const int g0 = p0.rgroups * p0.splits * p0.mgroups;
-  if ((int)blockIdx.x < g0) stream_body<WT, NW, NR, P, CH, MT>(d0, a0, p0, blockIdx.x, g0, xs_dyn, &last_flag);
-  else stream_body<WT, NW, NR, P, CH, MT>(d1, a1, p1, blockIdx.x - g0, gridDim.x - g0, xs_dyn, &last_flag);
+  if ((int)blockIdx.x < g0)
+    stream_body<WT, false, NW, NR, P, CH, MT>(d0, a0, p0, blockIdx.x, g0, xsb_dyn, &last_flag);
+  else
+    stream_body<WT, false, NW, NR, P, CH, MT>(d1, a1, p1, blockIdx.x - g0, gridDim.x - g0, xsb_dyn, &last_flag);
+}
+
+template <int NW, int NR, int P, int CH, int MT>
+__global__ __launch_bounds__(NW * 64) void linear_stream8_kernel(LayerDesc d, LinearArgs a, LinearPlan p) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t xsb_dyn[];
+  __shared__ int last_flag;
+  stream_body<uint8_t, true, NW, NR, P, CH, MT>(d, a, p, blockIdx.x, gridDim.x, xsb_dyn, &last_flag);
 }
 
 // X'p[m][j] = X[m][pip[j]] (0 where pip[j] < 0), as a contiguous [M][K_p]
@@ -891,186 +1056,6 @@ __global__ void gather_x_kernel(LayerDesc d, const uint16_t* __restrict__ X, int
   const int64_t mrow = gid / per_row, col = 8 * (gid % per_row);
   *(u32x4*)(Xp + mrow * d.K_p + col) =
       gather8_from(X + mrow * ldx, *(const u32x4*)(d.pip + col), *(const u32x4*)(d.pip + col + 4));
-}
-
-// ---------------------------------------------------------------------------
-// W8A8: e4m3 weights times per-token e4m3 activations on
-// v_smfmac_f32_16x16x128_fp8_fp8 (one instruction per unit; no widening of
-// the weights).  The activations arrive quantised in X'p order ([M][K_p]
-// codes, quantize_tokens_kernel) and pass through the same double-buffered
-// LDS chunks as in stream_body, one byte per column.
-//
-// Operand layout of the fp8 instruction (16 rows x 128 columns of a 2:4
-// step): lane l (row l % 16, lane group h = l / 16) gives 16 stored values,
-// bytes 2j, 2j+1 (j < 8) for group j of its 32-column slice, positions from
-// nibble j of the index word; B lane l (column l % 16) gives 32 activations,
-// and A byte pair j of lane group h pairs with B lane group
-// 2(h & 1) + (j >= 4), bytes 16(h >> 1) + 4(j & 3) + pos.  For the unit
-// layout (the A operands of the bf16 instruction pair, see
-// spense_internal.h), B lane group h then needs the 32 staged columns at
-// base = 64(h & 1) + 32(h >> 1) of a sparse unit (32(h >> 1) of a dense
-// unit, whose fixed index word 0xEEEE4444 picks positions 0,1 of groups 0-3
-// and 2,3 of groups 4-7) with the middle two 8-column quarters swapped.
-// ---------------------------------------------------------------------------
-typedef int i32x4 __attribute__((ext_vector_type(4)));
-typedef int i32x8 __attribute__((ext_vector_type(8)));
-
-__device__ __forceinline__ i32x8 lds_b8(const uint8_t* p) {
-  const i32x4 q0 = *(const i32x4*)p, q1 = *(const i32x4*)(p + 16);
-  return __builtin_shufflevector(q0, q1, 0, 1, 4, 5, 2, 3, 6, 7);
-}
-
-__device__ __forceinline__ f32x4 smfmac_fp8(const u32x4& a, const i32x8& b, const f32x4& c, int idx) {
-  return __builtin_amdgcn_smfmac_f32_16x16x128_fp8_fp8(__builtin_bit_cast(i32x4, a), b, c, idx, 0, 0);
-}
-
-template <int NW, int NR, int P, int CH, int MT>
-__device__ __forceinline__ void stream8_body(const LayerDesc& d, const LinearArgs& a, const LinearPlan& p, int block,
-                                             int grid, uint8_t* xs_dyn, int* last_flag_p) {
-  static_assert(CH % P == 0, "a chunk must hold whole rings");
-  int& last_flag = *last_flag_p;
-  constexpr int kPitch = CH * 128 + 16;                    // staged row bytes: CH unit slots of 128 columns + pad
-  constexpr int kPieces = (16 * MT * CH * 8) / (NW * 64);  // 16-byte pieces per thread per chunk (full m-group)
-  static_assert(kPieces * NW * 64 == 16 * MT * CH * 8, "pieces must divide evenly");
-  constexpr bool kSplitAcc = NR == 1 && MT == 1;  // alternate two accumulators when nothing else interleaves
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  int b = block;
-  if (p.xcd_remap) b = (b % 8) * (grid / 8) + b / 8;
-  const int S = p.splits;
-  const int mg = b % p.mgroups;
-  const int rg = (b / p.mgroups) % p.rgroups;
-  const int s = b / (p.mgroups * p.rgroups);
-  const int64_t rt0 = ((int64_t)rg * NW + wave) * NR;
-  const int64_t ms0 = d.n_sm * s / S, ms1 = d.n_sm * (s + 1) / S;
-  const int64_t md0 = d.n_dm * s / S, md1 = d.n_dm * (s + 1) / S;
-  const int ns = (int)(ms1 - ms0), nd = (int)(md1 - md0);
-  const int total = ns + 2 * nd;  // units
-  const int nchunks = (total + CH - 1) / CH;
-  const int64_t m0 = (int64_t)mg * 16 * MT;
-  const int mloc = (int)(a.M - m0 < 16 * MT ? a.M - m0 : 16 * MT);
-  const int rows = (int)(a.M < 16 * MT ? a.M : 16 * MT);
-  const int m = lane & 15, g = lane >> 4;
-  const int64_t sbase = ms0, dbase = d.n_sm + 2 * md0 - ns;
-  const uint8_t* tile[NR];
-#pragma unroll
-  for (int r = 0; r < NR; ++r) tile[r] = d.wpack + (rt0 + r < d.NT ? rt0 + r : 0) * d.tile_bytes;
-  uint8_t* xbuf0 = xs_dyn;
-  uint8_t* xbuf1 = xs_dyn + rows * kPitch;
-  const uint8_t* X = (const uint8_t*)a.X + m0 * a.ldx;
-
-  auto unit_ptr = [&](int r, int k) { return tile[r] + (k + (k < ns ? sbase : dbase)) * 1024; };
-  auto idx_ptr = [&](int r, int k) { return k < ns ? tile[r] + d.idx_off + (ms0 + k) * 256 : unit_ptr(r, k); };
-  auto load_step = [&](UnitFrag<uint8_t>(&f)[NR], int k) {
-#pragma unroll
-    for (int r = 0; r < NR; ++r) load_unit<uint8_t>(f[r], unit_ptr(r, k), idx_ptr(r, k) + 4 * lane, lane);
-  };
-
-  TileOut to[NR];
-#pragma unroll
-  for (int r = 0; r < NR; ++r) to[r] = tile_out(d, rt0 + r < d.NT ? rt0 + r : 0, lane);
-
-  UnitFrag<uint8_t> wr[P][NR];
-  const bool stream = total > 0;
-  if (stream) {
-#pragma unroll
-    for (int i = 0; i < P; ++i) load_step(wr[i], i < total ? i : total - 1);
-  }
-
-  // piece e of a chunk: row = e / (8 CH), unit slot j = (e / 8) % CH, 16-column
-  // group c16 = e % 8 (a dense unit has 4).  Same fixed-count load scheme as
-  // stream_body: pieces outside the batch or the split read column 0 of the
-  // m-group's first row and are dropped.
-  u32x4 xv[kPieces];
-  auto issue_chunk = [&](int c) {
-#pragma unroll
-    for (int i = 0; i < kPieces; ++i) {
-      const int e = threadIdx.x + i * NW * 64;
-      const int row = e / (8 * CH);
-      const int j = (e / 8) % CH, c16 = e % 8;
-      const int k = c * CH + j;
-      const bool ok = row < mloc && k < total && (k < ns || c16 < 4);
-      const uint32_t rowoff = ok ? (uint32_t)(row * a.ldx) : 0u;
-      const int64_t col = !ok ? 0 : k < ns ? 128 * (ms0 + k) + 16 * c16 : d.K_sp + 128 * md0 + 64 * (k - ns) + 16 * c16;
-      xv[i] = *(const u32x4*)(X + rowoff + (uint32_t)col);
-    }
-  };
-  auto write_chunk = [&](uint8_t* buf) {
-#pragma unroll
-    for (int i = 0; i < kPieces; ++i) {
-      const int e = threadIdx.x + i * NW * 64;
-      const int row = e / (8 * CH);
-      if (row < mloc) *(u32x4*)(buf + row * kPitch + 128 * ((e / 8) % CH) + 16 * (e % 8)) = xv[i];
-    }
-  };
-
-  issue_chunk(0);
-  write_chunk(xbuf0);
-  __syncthreads();
-
-  f32x4 acc[NR * MT], acc1 = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int t = 0; t < NR * MT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // activation rows beyond the batch read row 0 (their output columns are never stored)
-  int xoff[MT];
-#pragma unroll
-  for (int t = 0; t < MT; ++t) xoff[t] = (16 * t + m < mloc ? 16 * t + m : 0) * kPitch + 32 * (g >> 1);
-  const int sp_off = 64 * (g & 1);
-  auto consume = [&](const UnitFrag<uint8_t>(&f)[NR], int k, int j, const uint8_t* xb) {
-    const bool sp = k < ns;
-    const int off = 128 * j + (sp ? sp_off : 0);
-    if constexpr (kSplitAcc) {
-      const i32x8 B = lds_b8(xb + xoff[0] + off);
-      const int idx = sp ? (int)f[0].idx : (int)kDenseIdx;
-      if (j & 1) acc1 = smfmac_fp8(f[0].a, B, acc1, idx);
-      else acc[0] = smfmac_fp8(f[0].a, B, acc[0], idx);
-    } else {
-      int idx[NR];
-#pragma unroll
-      for (int r = 0; r < NR; ++r) idx[r] = sp ? (int)f[r].idx : (int)kDenseIdx;
-#pragma unroll
-      for (int t = 0; t < MT; ++t) {
-        const i32x8 B = lds_b8(xb + xoff[t] + off);
-#pragma unroll
-        for (int r = 0; r < NR; ++r) acc[r * MT + t] = smfmac_fp8(f[r].a, B, acc[r * MT + t], idx[r]);
-      }
-    }
-  };
-  const int nfull = total / CH;
-  for (int c = 0; c < nfull; ++c) {
-    const bool more = c + 1 < nchunks;
-    if (more) issue_chunk(c + 1);
-    const uint8_t* xb = (c & 1) ? xbuf1 : xbuf0;
-#pragma unroll
-    for (int j = 0; j < CH; ++j) {
-      const int k = c * CH + j;
-      consume(wr[j % P], k, j, xb);
-      load_step(wr[j % P], k + P < total ? k + P : total - 1);
-    }
-    if (more) write_chunk((c & 1) ? xbuf0 : xbuf1);
-    __syncthreads();
-  }
-  if (nfull < nchunks) {
-    const int c = nfull;
-    const uint8_t* xb = (c & 1) ? xbuf1 : xbuf0;
-#pragma unroll
-    for (int j = 0; j < CH; ++j) {
-      const int k = c * CH + j;
-      if (k < total) {
-        consume(wr[j % P], k, j, xb);
-        if (k + P < total) load_step(wr[j % P], k + P);
-      }
-    }
-  }
-  if constexpr (kSplitAcc) acc[0] += acc1;
-  finish_tile<NR, MT, true>(d, a, acc, to, rt0, m0, s, S, (int64_t)mg * p.rgroups + rg, &last_flag);
-}
-
-template <int NW, int NR, int P, int CH, int MT>
-__global__ __launch_bounds__(NW * 64) void linear_stream8_kernel(LayerDesc d, LinearArgs a, LinearPlan p) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t xs8_dyn[];
-  __shared__ int last_flag;
-  stream8_body<NW, NR, P, CH, MT>(d, a, p, blockIdx.x, gridDim.x, xs8_dyn, &last_flag);
 }
 
 // Per-token e4m3 quantisation, one workgroup of 256 threads per token: the
