@@ -492,6 +492,7 @@ static int plan_linear(const spense_layer* h, int64_t M, int32_t splits, int64_t
     // the gate/up layer at M = 8 and 16: 6-7% faster than four)
     p.chunked = (force_chunked || ch == 1 || decode_lds_bytes(d, M, S) > 64 * 1024) ? 1 : 0;
     p.rgroups = (int)((d.NT + p.waves - 1) / p.waves);
+    if (S > 1 && S * M * d.NT * 64 >= (int64_t(1) << 31)) return SPENSE_EUNSUPPORTED;  // 32-bit partial offsets
     p.splits = (int)S;
     p.lds_bytes = (int)(p.chunked ? stream_lds_bytes(M, kStreamChunk, xbytes) : decode_lds_bytes(d, M, S));
     return SPENSE_OK;
@@ -508,27 +509,30 @@ static int plan_linear(const spense_layer* h, int64_t M, int32_t splits, int64_t
 #undef SPENSE_PRESET
   };
   constexpr int kNumPresets = (int)(sizeof(kPresets) / sizeof(kPresets[0]));
-  // The largest blocking that still gives about 150 workgroups (measured on
-  // the 36B-class layers for M = 32..2048, both activation types: within a
-  // few percent of the best preset per shape in total).  Eight waves per
-  // workgroup with four m-tiles each when there are enough tiles (four row
-  // tiles per wave for bf16 activations, two for e4m3 codes, whose smaller
-  // staged rows let more workgroups share a CU), then eight waves with two
-  // row tiles and a deeper ring, then two m-tiles; at M <= 32 one m-group of
-  // two m-tiles with two row tiles per wave, or a single row tile.
+  // The largest blocking that still gives enough workgroups before splits
+  // (thresholds fitted to a sweep of every preset over the four 36B-class
+  // layers at M = 32..2048, both activation types: 6% above the best preset
+  // per shape in total).  Eight waves per workgroup with four m-tiles each
+  // (four row tiles per wave for bf16 activations, two for e4m3 codes, whose
+  // smaller staged rows let more workgroups share a CU), then eight waves
+  // with two row tiles and a deeper ring, then two m-tiles, then one row
+  // tile; at M <= 32 one m-group of two m-tiles with two row tiles per wave,
+  // or a single row tile.
   auto workgroups = [&](int i) {
     const Preset& c = kPresets[i];
     return (NT_fill + c.nw * c.nr - 1) / (c.nw * c.nr) * ((M + 16 * c.mt - 1) / (16 * c.mt));
   };
-  constexpr int64_t kEnough = 150;
   int pre;
   if (M <= 32) {
-    pre = workgroups(2) >= kEnough ? 2 : 7;
+    pre = workgroups(2) >= 150 ? 2 : 7;
   } else {
+    // (preset, workgroups it needs before splits)
+    const int big = xbytes == 1 ? 6 : 9;
+    const int64_t need[3][2] = {{big, 150}, {12, 120}, {2, 64}};
     pre = 0;
-    for (int c : {xbytes == 1 ? 6 : 9, 12, 2})
-      if (workgroups(c) >= kEnough) {
-        pre = c;
+    for (const auto& c : need)
+      if (workgroups((int)c[0]) >= c[1]) {
+        pre = (int)c[0];
         break;
       }
   }
@@ -560,6 +564,11 @@ static int plan_linear(const spense_layer* h, int64_t M, int32_t splits, int64_t
     // each split writes and reads back fp32 partials of the whole output
     // (8 M N bytes); keep that below half the packed weight bytes
     S = std::max<int64_t>(1, std::min<int64_t>(S, d.tile_bytes / (256 * M)));
+  }
+  // the partials are addressed with 32-bit offsets
+  if (S > 1 && S * M * d.NT * 64 >= (int64_t(1) << 31)) {
+    if (splits != 0) return SPENSE_EUNSUPPORTED;
+    S = std::max<int64_t>(1, ((int64_t(1) << 31) - 1) / (M * d.NT * 64));
   }
   p.splits = (int)S;
   const int64_t grid = (int64_t)p.rgroups * p.mgroups * S;

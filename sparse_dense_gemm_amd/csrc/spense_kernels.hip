@@ -101,21 +101,27 @@ __device__ __forceinline__ f32x4 smfmac_bf16(const bf16x8& a, const bf16x16& b, 
   return __builtin_amdgcn_smfmac_f32_16x16x64_bf16(a, b, c, idx, 0, ABID);
 }
 
-// Split-K handshake without cache maintenance.  Partials are written and read
-// with device-scope accesses (coherent at the device level, so no L2
-// write-back or invalidate is needed); each thread waits until its partial
-// stores have completed before the workgroup's arrival is counted, and the
-// workgroup that arrives last reads every partial.
-__device__ __forceinline__ void store_partial(float* p, const f32x4& v) {
-#pragma unroll
-  for (int r = 0; r < 4; ++r) __hip_atomic_store(p + r, v[r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Raw buffer resource over [base, base + bytes): a load at an offset beyond
+// `bytes` returns zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
-__device__ __forceinline__ f32x4 load_partial(const float* p) {
-  f32x4 v;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) v[r] = __hip_atomic_load(p + r, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return v;
+// Split-K handshake without cache maintenance.  Partials are written and read
+// with device-coherent accesses (the cache policy of relaxed agent-scope
+// atomics: written through to, and read from, the level shared by all XCDs,
+// so no L2 write-back or invalidate is needed), 16 bytes per lane; each thread
+// waits until its partial stores have completed before the workgroup's
+// arrival is counted, and the workgroup that arrives last reads every partial.
+// Layout [split][row tile][m][16 rows]: a wave's store for one tile and m-tile
+// is 1 KB contiguous.
+constexpr int kCoherent = 16;  // sc1 cache-policy bit of buffer loads/stores
+__device__ __forceinline__ void store_partial(__amdgpu_buffer_rsrc_t ws, uint32_t off, const f32x4& v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), ws, (int)off, 0, kCoherent);
+}
+
+__device__ __forceinline__ f32x4 load_partial(__amdgpu_buffer_rsrc_t ws, uint32_t off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ws, (int)off, 0, kCoherent));
 }
 
 // Returns true in every thread of the last-arriving workgroup; that workgroup
@@ -176,8 +182,12 @@ __device__ __forceinline__ void finish_tile(const LayerDesc& d, const LinearArgs
                                             int64_t cnt_index, int* last_flag) {
   const int lane = threadIdx.x & 63;
   const int nb = 4 * (lane >> 4);
-  const int64_t NP = d.NT * 16;
   constexpr int nr = NR, mtiles = MT;
+  // partial of (split, row tile, m) at byte ((split * NT + rt) * M + m) * 64 + 4 nb
+  const __amdgpu_buffer_rsrc_t wsr = make_rsrc(a.ws, S > 1 ? (uint32_t)((int64_t)S * d.NT * a.M * 64) : 0u);
+  auto poff = [&](int64_t split, int64_t rt, int64_t m) {
+    return (uint32_t)((((split * d.NT + rt) * a.M + m) * 16 + nb) * 4);
+  };
   if (S > 1) {
 #pragma unroll
     for (int r = 0; r < nr; ++r) {
@@ -186,7 +196,7 @@ __device__ __forceinline__ void finish_tile(const LayerDesc& d, const LinearArgs
 #pragma unroll
       for (int mt = 0; mt < mtiles; ++mt) {
         const int64_t m = m0 + 16 * mt + (lane & 15);
-        if (m < a.M) store_partial(a.ws + ((int64_t)s * a.M + m) * NP + rt * 16 + nb, acc[r * mtiles + mt]);
+        if (m < a.M) store_partial(wsr, poff(s, rt, m), acc[r * mtiles + mt]);
       }
     }
     if (!arrive_last(a.counters + cnt_index, S, last_flag)) return;
@@ -202,7 +212,7 @@ __device__ __forceinline__ void finish_tile(const LayerDesc& d, const LinearArgs
       f32x4 sum = acc[r * mtiles + mt];
       if (S > 1) {
         sum = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int s2 = 0; s2 < S; ++s2) sum += load_partial(a.ws + ((int64_t)s2 * a.M + m) * NP + rt * 16 + nb);
+        for (int s2 = 0; s2 < S; ++s2) sum += load_partial(wsr, poff(s2, rt, m));
       }
       if (a.glu) {
         // rows (q, q+1) of this lane are the gate and up rows of one
@@ -740,11 +750,6 @@ __global__ __launch_bounds__(NW * 64) void linear_decode2_kernel(LayerDesc d0, L
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 
-// Raw buffer resource over [base, base + bytes): a load at an offset beyond
-// `bytes` returns zero.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
-}
 constexpr uint32_t kOutOfRange = 0x80000000u;  // beyond every resource built here (all below 2 GB)
 
 __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
