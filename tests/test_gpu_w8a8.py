@@ -195,3 +195,31 @@ def test_w8a8_full_layer_sampled(lname):
             assert r <= 1.0
     finally:
         sdg.spense_free(h)
+
+
+def test_leading_dimensions_beyond_32bit_offsets_are_refused():
+    """The streaming kernels address staged activations with 32-bit offsets:
+    a leading dimension of 2^23 elements or more is refused on the host
+    (M = 1, so even a kernel launch would read only row 0, which exists)."""
+    N, K = 64, 256
+    W, s = synth.make_weight(N, K, DT_FP8, np.random.default_rng(560))
+    h = pack_dev(to_dev(W, DT_FP8), DT_FP8, to_dev(s, DT_F32), dense_fraction=0.25)
+    try:
+        Xd = to_dev(synth.make_x(1, K, DT_BF16, np.random.default_rng(561)), DT_BF16)
+        Y = torch.empty((1, N), dtype=torch.float32, device="cuda")
+        with pytest.raises(sdg.SpenseError) as e:
+            sdg.spense_linear_splits(h, Xd, Y, 0, ldx=1 << 23)
+        assert e.value.status == sdg.SPENSE_EUNSUPPORTED
+        Y1 = torch.empty_like(Y)
+        sdg.spense_linear_splits(h, Xd, Y1, 0, ldx=(1 << 23) - 1)  # just below the limit: accepted
+        sdg.spense_linear_splits(h, Xd, Y, 0)
+        torch.cuda.synchronize()
+        assert torch.equal(Y, Y1)
+        # the W8A8 path reads the caller's rows only in its quantisation pass
+        # (64-bit offsets) and stages its own workspace: any leading dimension works
+        sdg.spense_linear_w8a8(h, Xd, Y1, ldx=1 << 23)
+        sdg.spense_linear_w8a8(h, Xd, Y)
+        torch.cuda.synchronize()
+        assert torch.equal(Y, Y1)
+    finally:
+        sdg.spense_free(h)
