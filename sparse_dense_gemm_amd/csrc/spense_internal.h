@@ -118,7 +118,8 @@ struct LinearPlan {
   X(11, 4, 4, 4, 4, 2)         \
   X(12, 8, 2, 4, 4, 4)         \
   X(13, 8, 4, 4, 4, 4)         \
-  X(14, 4, 2, 4, 4, 8)
+  X(14, 4, 2, 4, 4, 8)         \
+  X(15, 8, 4, 2, 2, 8)
 
 constexpr int kStreamChunk = 8;  // units per activation chunk of linear_stream_kernel
 
