@@ -513,7 +513,8 @@ static int plan_linear(const spense_layer* h, int64_t M, int32_t splits, int64_t
   // (thresholds fitted to a sweep of every preset over the four 36B-class
   // layers at M = 32..2048, both activation types: 6% above the best preset
   // per shape in total).  Eight waves per workgroup with four m-tiles each
-  // (four row tiles per wave for bf16 activations; for e4m3 codes eight
+  // (four row tiles per wave and four-unit chunks for bf16 activations, whose
+  // activation loads then run a chunk further ahead; for e4m3 codes eight
   // m-tiles and four row tiles, else two row tiles, whose smaller staged rows
   // let more workgroups share a CU), then eight waves with two row tiles and
   // a deeper ring, then two m-tiles, then one row tile; at M <= 32 one m-group
@@ -530,7 +531,7 @@ static int plan_linear(const spense_layer* h, int64_t M, int32_t splits, int64_t
     // m-tiles per wave (four row tiles), which halves the weight bytes loaded
     // per product (gate/up 55296x5120 at M = 2048: 574 us vs 645 us)
     const int64_t need_a8[4][2] = {{15, 150}, {6, 150}, {12, 120}, {2, 64}};
-    const int64_t need_a16[4][2] = {{9, 150}, {9, 150}, {12, 120}, {2, 64}};
+    const int64_t need_a16[4][2] = {{16, 150}, {16, 150}, {12, 120}, {2, 64}};
     pre = 0;
     for (const auto& c : xbytes == 1 ? need_a8 : need_a16)
       if (workgroups((int)c[0]) >= c[1]) {

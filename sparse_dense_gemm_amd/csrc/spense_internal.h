@@ -119,7 +119,8 @@ struct LinearPlan {
   X(12, 8, 2, 4, 4, 4)         \
   X(13, 8, 4, 4, 4, 4)         \
   X(14, 4, 2, 4, 4, 8)         \
-  X(15, 8, 4, 2, 2, 8)
+  X(15, 8, 4, 2, 2, 8)         \
+  X(16, 8, 4, 2, 4, 4)
 
 constexpr int kStreamChunk = 8;  // units per activation chunk of linear_stream_kernel
 
