@@ -530,8 +530,8 @@ static int plan_linear(const spense_layer* h, int64_t M, int32_t splits, int64_t
     // (preset, workgroups it needs before splits); e4m3 codes first try eight
     // m-tiles per wave (four row tiles), which halves the weight bytes loaded
     // per product (gate/up 55296x5120 at M = 2048: 574 us vs 645 us)
-    const int64_t need_a8[4][2] = {{15, 150}, {6, 150}, {12, 120}, {2, 64}};
-    const int64_t need_a16[4][2] = {{16, 150}, {16, 150}, {12, 120}, {2, 64}};
+    const int64_t need_a8[4][2] = {{13, 150}, {6, 150}, {12, 120}, {2, 64}};
+    const int64_t need_a16[4][2] = {{14, 150}, {14, 150}, {12, 120}, {2, 64}};
     pre = 0;
     for (const auto& c : xbytes == 1 ? need_a8 : need_a16)
       if (workgroups((int)c[0]) >= c[1]) {
@@ -540,9 +540,10 @@ static int plan_linear(const spense_layer* h, int64_t M, int32_t splits, int64_t
       }
   }
   if (const char* t = std::getenv("SPENSE_TILE")) {
-    // a forced preset whose two staging buffers would not fit in one CU's LDS is ignored
+    // a forced preset whose two staging buffers would not fit in one CU's LDS,
+  // or that takes e4m3 codes only, is ignored
     const int v = std::atoi(t);
-    if (v >= 0 && v < kNumPresets &&
+    if (v >= 0 && v < kNumPresets && (xbytes == 1 || !preset_codes_only(v)) &&
         stream_lds_bytes(std::min<int64_t>(M, 16 * kPresets[v].mt), kPresets[v].ch, xbytes) <= kLdsPerCU)
       pre = v;
   }

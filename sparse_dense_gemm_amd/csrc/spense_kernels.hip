@@ -957,14 +957,9 @@ __device__ __forceinline__ void stream_body(const LayerDesc& d, const LinearArgs
       }
     } else {
       const int off0 = kSlot * j, off1 = off0 + (sp ? sp_off : 0);
-      bf16x16 B0[MT], B1[MT];
-#pragma unroll
-      for (int t = 0; t < MT; ++t) {
-        B0[t] = lds_b16(xb + xoff[t] + off0);
-        B1[t] = lds_b16(xb + xoff[t] + off1);
-      }
       if constexpr (kSplitAcc) {
-        mac_unit<WT>(acc[0], acc1, f[0], sp ? (int)f[0].idx : (int)kDenseIdx, B0[0], B1[0]);
+        mac_unit<WT>(acc[0], acc1, f[0], sp ? (int)f[0].idx : (int)kDenseIdx, lds_b16(xb + xoff[0] + off0),
+                     lds_b16(xb + xoff[0] + off1));
       } else {
         bf16x8 A0[NR], A1[NR];
         int idx[NR];
@@ -973,14 +968,40 @@ __device__ __forceinline__ void stream_body(const LayerDesc& d, const LinearArgs
           unit_a<WT>(f[r], A0[r], A1[r]);
           idx[r] = sp ? (int)f[r].idx : (int)kDenseIdx;
         }
+        if constexpr (MT <= 4) {  // every fragment of the unit up front
+          bf16x16 B0[MT], B1[MT];
 #pragma unroll
-        for (int t = 0; t < MT; ++t)
+          for (int t = 0; t < MT; ++t) {
+            B0[t] = lds_b16(xb + xoff[t] + off0);
+            B1[t] = lds_b16(xb + xoff[t] + off1);
+          }
 #pragma unroll
-          for (int r = 0; r < NR; ++r) acc[r * MT + t] = smfmac_bf16<0>(A0[r], B0[t], acc[r * MT + t], idx[r]);
+          for (int t = 0; t < MT; ++t)
 #pragma unroll
-        for (int t = 0; t < MT; ++t)
+            for (int r = 0; r < NR; ++r) acc[r * MT + t] = smfmac_bf16<0>(A0[r], B0[t], acc[r * MT + t], idx[r]);
 #pragma unroll
-          for (int r = 0; r < NR; ++r) acc[r * MT + t] = smfmac_bf16<1>(A1[r], B1[t], acc[r * MT + t], idx[r]);
+          for (int t = 0; t < MT; ++t)
+#pragma unroll
+            for (int r = 0; r < NR; ++r) acc[r * MT + t] = smfmac_bf16<1>(A1[r], B1[t], acc[r * MT + t], idx[r]);
+        } else {  // one m-tile's fragment pair ahead
+          bf16x16 B0c = lds_b16(xb + xoff[0] + off0), B1c = lds_b16(xb + xoff[0] + off1);
+#pragma unroll
+          for (int t = 0; t < MT; ++t) {
+            bf16x16 B0n, B1n;
+            if (t + 1 < MT) {
+              B0n = lds_b16(xb + xoff[t + 1] + off0);
+              B1n = lds_b16(xb + xoff[t + 1] + off1);
+            }
+#pragma unroll
+            for (int r = 0; r < NR; ++r) acc[r * MT + t] = smfmac_bf16<0>(A0[r], B0c, acc[r * MT + t], idx[r]);
+#pragma unroll
+            for (int r = 0; r < NR; ++r) acc[r * MT + t] = smfmac_bf16<1>(A1[r], B1c, acc[r * MT + t], idx[r]);
+            if (t + 1 < MT) {
+              B0c = B0n;
+              B1c = B1n;
+            }
+          }
+        }
       }
     }
   };
@@ -1264,7 +1285,9 @@ hipError_t launch_stream_preset(const Launch& L, hipStream_t s) {
   if (L.a[0]->gather) return hipErrorInvalidValue;
   switch (L.p[0]->preset) {
 #define SPENSE_PRESET(i, nw, nr, pp, ch, mt) \
-  case i: return launch_stream_k<WT, nw, nr, pp, ch, mt>(L, s);
+  case i:                                   \
+    if constexpr (preset_codes_only(i)) return hipErrorInvalidValue; \
+    else return launch_stream_k<WT, nw, nr, pp, ch, mt>(L, s);
     SPENSE_TILE_PRESETS(SPENSE_PRESET)
 #undef SPENSE_PRESET
     default: return hipErrorInvalidValue;

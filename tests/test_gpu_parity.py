@@ -276,7 +276,7 @@ def test_decode_variants(wdtype, dense, monkeypatch):
         sdg.spense_free(h)
 
 
-TILE_PRESETS = list(range(17))
+TILE_PRESETS = list(range(15))
 
 
 @pytest.mark.parametrize("wdtype", [DT_FP8, DT_BF16])

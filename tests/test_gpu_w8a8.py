@@ -24,7 +24,7 @@ from spense_gpu_util import log, oracle_pack_rows, pack_dev, to_dev, tol_ratio
 
 pytestmark = pytest.mark.gpu
 
-TILE_PRESETS = list(range(17))
+TILE_PRESETS = list(range(15))
 
 
 def _quantize_dev(X: np.ndarray):

@@ -3,8 +3,10 @@
 A matrix instruction whose destination registers overlap its A or B source
 registers gave wrong results on MI355X (seen with v_mfma_f32_16x16x32_bf16 and
 VGPR accumulators, where the destination is a separate operand).  The kernels
-now use only v_smfmac_f32_16x16x64_bf16, whose destination is tied to the
-accumulator; this test scans the emitted code for any overlap.
+now use only the structured-sparse instructions (v_smfmac_f32_16x16x64_bf16,
+and v_smfmac_f32_16x16x128_fp8_fp8 for W8A8), whose destination is tied to
+the accumulator; this test scans the emitted code for any overlap.  The code
+is built with the flags of the product build.
 """
 
 import os
@@ -32,9 +34,11 @@ def gfx950_asm():
     if not os.path.exists(HIPCC):
         pytest.skip("hipcc not available")
     with tempfile.TemporaryDirectory() as d:
-        cmd = [HIPCC, "-O3", "-std=c++17", "--offload-arch=gfx950", "--cuda-device-only", "-S",
-               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-               "-I", os.path.join(ROOT, "include"), SRC, "-o", os.path.join(d, "k.s")]
+        from sparse_dense_gemm_amd.build import EXTRA, FLAGS
+
+        flags = [f for f in FLAGS if f not in ("-fPIC", "-Wall", "-Wno-unused-function")]
+        cmd = [HIPCC, *flags, *EXTRA.get(os.path.basename(SRC), []), "--cuda-device-only", "-S",
+               SRC, "-o", os.path.join(d, "k.s")]
         r = subprocess.run(cmd, capture_output=True, text=True)
         assert r.returncode == 0, r.stderr[-2000:]
         with open(os.path.join(d, "k.s")) as f:
@@ -60,7 +64,39 @@ def test_no_packed_fp32_arithmetic(gfx950_asm):
 
 
 def test_both_regions_run_on_structured_sparse_instructions(gfx950_asm):
-    # the 2:4 region and the dense region (as pairs of fixed-index products,
-    # index word 0xEEEE4444) both use v_smfmac_f32_16x16x64_bf16
+    # the 2:4 region and the dense region (as fixed-index products, index word
+    # 0xEEEE4444) both use the structured-sparse instructions; no dense MFMA
     assert "v_smfmac_f32_16x16x64_bf16" in gfx950_asm
+    assert "v_smfmac_f32_16x16x128_fp8_fp8" in gfx950_asm
     assert re.search(r"0xeeee4444", gfx950_asm, re.I)
+    assert not re.search(r"\sv_mfma_", gfx950_asm)
+
+
+def test_main_loops_keep_loads_in_flight(gfx950_asm):
+    """The streaming kernels' main loops (those with structured-sparse
+    instructions) wait on vector memory only with several loads still in
+    flight: a wait for (almost) every outstanding load would drain the weight
+    ring once per chunk."""
+    labels = [(m.start(), m.group(1)) for m in re.finditer(r"^(_Z\w+):", gfx950_asm, re.M)]
+    checked = 0
+    for i, (pos, name) in enumerate(labels):
+        if "linear_stream" not in name:
+            continue
+        body = gfx950_asm[pos:labels[i + 1][0] if i + 1 < len(labels) else len(gfx950_asm)]
+        loops, cur = {}, None
+        for line in body.splitlines():
+            if line.startswith(".LBB"):
+                hm = re.search(r"Header=(\w+) Depth=1", line)
+                cur = line.split(":")[0][1:] if "Loop Header: Depth=1" in line else (hm.group(1) if hm else None)
+            if cur:
+                d = loops.setdefault(cur, {"smf": 0, "vm": []})
+                d["smf"] += "v_smfmac" in line
+                w = re.search(r"s_waitcnt vmcnt\((\d+)\)", line)
+                if w:
+                    d["vm"].append(int(w.group(1)))
+        main = max(loops.values(), key=lambda v: v["smf"], default=None)
+        if not main or not main["vm"]:
+            continue
+        checked += 1
+        assert min(main["vm"]) >= 4, (name[:90], sorted(set(main["vm"])))
+    assert checked > 20
