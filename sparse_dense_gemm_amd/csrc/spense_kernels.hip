@@ -485,16 +485,18 @@ struct UnitFrag<uint16_t> {
 
 // Loads one unit.  The index load is issued for dense units too (from the
 // unit itself, a cached address) and its value replaced by the dense index
-// word at use, so sparse and dense units issue the same loads.
+// word at use, so sparse and dense units issue the same loads.  Weights are
+// read once per call: the loads carry the non-temporal hint, which streams
+// faster than the default policy.
 template <typename WT>
 __device__ __forceinline__ void load_unit(UnitFrag<WT>& f, const uint8_t* unit, const uint8_t* idx_addr, int lane) {
   if constexpr (sizeof(WT) == 1) {
-    f.a = *(const u32x4*)(unit + 16 * lane);
+    f.a = __builtin_nontemporal_load((const u32x4*)(unit + 16 * lane));
   } else {
-    f.a0 = *(const u32x4*)(unit + 16 * lane);
-    f.a1 = *(const u32x4*)(unit + 1024 + 16 * lane);
+    f.a0 = __builtin_nontemporal_load((const u32x4*)(unit + 16 * lane));
+    f.a1 = __builtin_nontemporal_load((const u32x4*)(unit + 1024 + 16 * lane));
   }
-  f.idx = *(const uint32_t*)idx_addr;
+  f.idx = __builtin_nontemporal_load((const uint32_t*)idx_addr);
 }
 
 // Two SMFMACs: A0 with B0 (index half 0), A1 with B1 (index half 1).
@@ -752,11 +754,16 @@ typedef int i32x8 __attribute__((ext_vector_type(8)));
 
 constexpr uint32_t kOutOfRange = 0x80000000u;  // beyond every resource built here (all below 2 GB)
 
+// Cache policy of buffer loads: 0 default, kNonTemporal for data read once
+// (the non-temporal hint streams faster than the default policy).
+constexpr int kNonTemporal = 2;
+template <int POL = 0>
 __device__ __forceinline__ u32x4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, 0));
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)voff, (int)soff, POL));
 }
+template <int POL = 0>
 __device__ __forceinline__ uint32_t buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, 0);
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)voff, (int)soff, POL);
 }
 
 // 32 contiguous bytes of LDS as one B operand
@@ -772,7 +779,11 @@ __device__ __forceinline__ f32x4 smfmac_fp8(const u32x4& a, const i32x8& b, cons
   return __builtin_amdgcn_smfmac_f32_16x16x128_fp8_fp8(__builtin_bit_cast(i32x4, a), b, c, idx, 0, 0);
 }
 
-template <typename WT, bool A8, int NW, int NR, int P, int CH, int MT>
+// NTW: the weights are read once (one m-group): their loads carry the
+// non-temporal hint.  With several m-groups each wave's weights are read again
+// per m-group, mostly from L2, and keep the default policy (the hint makes
+// those re-reads miss: 3-16% slower at M = 2048).
+template <typename WT, bool A8, int NW, int NR, int P, int CH, int MT, bool NTW>
 __device__ __forceinline__ void stream_body(const LayerDesc& d, const LinearArgs& a, const LinearPlan& p, int block,
                                             int grid, uint8_t* xs, int* last_flag_p) {
   static_assert(CH % P == 0, "a chunk must hold whole rings");
@@ -819,6 +830,7 @@ __device__ __forceinline__ void stream_body(const LayerDesc& d, const LinearArgs
   const int64_t bt = rt0 < d.NT ? rt0 : d.NT - 1;
   const int64_t ntile = d.NT - bt < NR ? d.NT - bt : NR;
   const __amdgpu_buffer_rsrc_t wres = make_rsrc(d.wpack + bt * d.tile_bytes, (uint32_t)(ntile * d.tile_bytes));
+  constexpr int kWPol = NTW ? kNonTemporal : 0;
   uint32_t roff[NR];
 #pragma unroll
   for (int r = 0; r < NR; ++r) roff[r] = rt0 + r < d.NT ? (uint32_t)(r * d.tile_bytes) : 0u;
@@ -833,12 +845,12 @@ __device__ __forceinline__ void stream_body(const LayerDesc& d, const LinearArgs
 #pragma unroll
     for (int r = 0; r < NR; ++r) {
       if constexpr (sizeof(WT) == 1) {
-        f[r].a = buf_load16(wres, 16u * lane, roff[r] + uoff);
+        f[r].a = buf_load16<kWPol>(wres, 16u * lane, roff[r] + uoff);
       } else {
-        f[r].a0 = buf_load16(wres, 16u * lane, roff[r] + uoff);
-        f[r].a1 = buf_load16(wres, 16u * lane, roff[r] + uoff + 1024u);
+        f[r].a0 = buf_load16<kWPol>(wres, 16u * lane, roff[r] + uoff);
+        f[r].a1 = buf_load16<kWPol>(wres, 16u * lane, roff[r] + uoff + 1024u);
       }
-      f[r].idx = buf_load4(wres, 4u * lane, roff[r] + ioff);
+      f[r].idx = buf_load4<kWPol>(wres, 4u * lane, roff[r] + ioff);
     }
   };
 
@@ -1046,30 +1058,30 @@ __device__ __forceinline__ void stream_body(const LayerDesc& d, const LinearArgs
   finish_tile<NR, MT, A8>(d, a, acc, to, rt0, m0, s, S, (int64_t)mg * p.rgroups + rg, &last_flag);
 }
 
-template <typename WT, int NW, int NR, int P, int CH, int MT>
+template <typename WT, int NW, int NR, int P, int CH, int MT, bool NTW>
 __global__ __launch_bounds__(NW * 64) void linear_stream_kernel(LayerDesc d, LinearArgs a, LinearPlan p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t xsb_dyn[];
   __shared__ int last_flag;
-  stream_body<WT, false, NW, NR, P, CH, MT>(d, a, p, blockIdx.x, gridDim.x, xsb_dyn, &last_flag);
+  stream_body<WT, false, NW, NR, P, CH, MT, NTW>(d, a, p, blockIdx.x, gridDim.x, xsb_dyn, &last_flag);
 }
 
-template <typename WT, int NW, int NR, int P, int CH, int MT>
+template <typename WT, int NW, int NR, int P, int CH, int MT, bool NTW>
 __global__ __launch_bounds__(NW * 64) void linear_stream2_kernel(LayerDesc d0, LinearArgs a0, LinearPlan p0,
                                                                  LayerDesc d1, LinearArgs a1, LinearPlan p1) {
   extern __shared__ __attribute__((aligned(16))) uint8_t xsb_dyn[];
   __shared__ int last_flag;
   const int g0 = p0.rgroups * p0.splits * p0.mgroups;
   if ((int)blockIdx.x < g0)
-    stream_body<WT, false, NW, NR, P, CH, MT>(d0, a0, p0, blockIdx.x, g0, xsb_dyn, &last_flag);
+    stream_body<WT, false, NW, NR, P, CH, MT, NTW>(d0, a0, p0, blockIdx.x, g0, xsb_dyn, &last_flag);
   else
-    stream_body<WT, false, NW, NR, P, CH, MT>(d1, a1, p1, blockIdx.x - g0, gridDim.x - g0, xsb_dyn, &last_flag);
+    stream_body<WT, false, NW, NR, P, CH, MT, NTW>(d1, a1, p1, blockIdx.x - g0, gridDim.x - g0, xsb_dyn, &last_flag);
 }
 
-template <int NW, int NR, int P, int CH, int MT>
+template <int NW, int NR, int P, int CH, int MT, bool NTW>
 __global__ __launch_bounds__(NW * 64) void linear_stream8_kernel(LayerDesc d, LinearArgs a, LinearPlan p) {
   extern __shared__ __attribute__((aligned(16))) uint8_t xsb_dyn[];
   __shared__ int last_flag;
-  stream_body<uint8_t, true, NW, NR, P, CH, MT>(d, a, p, blockIdx.x, gridDim.x, xsb_dyn, &last_flag);
+  stream_body<uint8_t, true, NW, NR, P, CH, MT, NTW>(d, a, p, blockIdx.x, gridDim.x, xsb_dyn, &last_flag);
 }
 
 // X'p[m][j] = X[m][pip[j]] (0 where pip[j] < 0), as a contiguous [M][K_p]
@@ -1255,29 +1267,33 @@ hipError_t launch_decode_t(const Launch& L, hipStream_t s) {
   return launch_decode_k<WT, NW, P, false>(L, s);
 }
 
-template <typename WT, int NW, int NR, int P, int CH, int MT>
+template <typename WT, int NW, int NR, int P, int CH, int MT, bool NTW>
 hipError_t launch_stream_k(const Launch& L, hipStream_t s) {
   const LinearPlan& p = *L.p[0];
   if (p.waves != NW || p.nr != NR || p.depth != P || p.chunk != CH || p.mt != MT) return hipErrorInvalidValue;
   hipError_t e;
   if (L.two) {
-    auto k = linear_stream2_kernel<WT, NW, NR, P, CH, MT>;
+    auto k = linear_stream2_kernel<WT, NW, NR, P, CH, MT, NTW>;
     if ((e = allow_lds(k, L.lds())) != hipSuccess) return e;
     k<<<L.grid(), NW * 64, L.lds(), s>>>(*L.d[0], *L.a[0], *L.p[0], *L.d[1], *L.a[1], *L.p[1]);
   } else {
-    auto k = linear_stream_kernel<WT, NW, NR, P, CH, MT>;
+    auto k = linear_stream_kernel<WT, NW, NR, P, CH, MT, NTW>;
     if ((e = allow_lds(k, L.lds())) != hipSuccess) return e;
     k<<<L.grid(), NW * 64, L.lds(), s>>>(*L.d[0], *L.a[0], *L.p[0]);
   }
   return hipGetLastError();
 }
 
-// single row tile and m-tile per wave: X'p contiguous (gathered beforehand when needed)
+// single row tile and m-tile per wave (M <= 16, one m-group): X'p contiguous
+// (gathered beforehand when needed)
 template <typename WT, int NW, int P>
 hipError_t launch_stream_t(const Launch& L, hipStream_t s) {
   if (L.a[0]->gather) return hipErrorInvalidValue;
-  return launch_stream_k<WT, NW, 1, P, kStreamChunk, 1>(L, s);
+  return launch_stream_k<WT, NW, 1, P, kStreamChunk, 1, true>(L, s);
 }
+
+// one m-group in every launched layer: each weight byte is read once
+inline bool single_pass(const Launch& L) { return L.p[0]->mgroups == 1 && (!L.two || L.p[1]->mgroups == 1); }
 
 // blocked tiles (SPENSE_TILE_PRESETS): X'p contiguous, gathered beforehand when needed
 template <typename WT>
@@ -1287,7 +1303,10 @@ hipError_t launch_stream_preset(const Launch& L, hipStream_t s) {
 #define SPENSE_PRESET(i, nw, nr, pp, ch, mt) \
   case i:                                   \
     if constexpr (preset_codes_only(i)) return hipErrorInvalidValue; \
-    else return launch_stream_k<WT, nw, nr, pp, ch, mt>(L, s);
+    else if constexpr (preset_single_pass_variant(i)) { \
+      if (single_pass(L)) return launch_stream_k<WT, nw, nr, pp, ch, mt, true>(L, s); \
+      return launch_stream_k<WT, nw, nr, pp, ch, mt, false>(L, s); \
+    } else return launch_stream_k<WT, nw, nr, pp, ch, mt, false>(L, s);
     SPENSE_TILE_PRESETS(SPENSE_PRESET)
 #undef SPENSE_PRESET
     default: return hipErrorInvalidValue;
@@ -1322,10 +1341,10 @@ hipError_t launch_linear_units(const Launch& L, hipStream_t s) {
   }
 }
 
-template <int NW, int NR, int P, int CH, int MT>
+template <int NW, int NR, int P, int CH, int MT, bool NTW>
 hipError_t launch_stream8_k(const LayerDesc& d, const LinearArgs& a, const LinearPlan& p, hipStream_t s) {
   if (p.waves != NW || p.nr != NR || p.depth != P || p.chunk != CH || p.mt != MT) return hipErrorInvalidValue;
-  auto k = linear_stream8_kernel<NW, NR, P, CH, MT>;
+  auto k = linear_stream8_kernel<NW, NR, P, CH, MT, NTW>;
   const hipError_t e = allow_lds(k, p.lds_bytes);
   if (e != hipSuccess) return e;
   const unsigned grid = (unsigned)((int64_t)p.rgroups * p.splits * p.mgroups);
@@ -1338,18 +1357,22 @@ hipError_t launch_linear8(const LayerDesc& d, const LinearArgs& a, const LinearP
   if (d.wdtype != DT_FP8 || !p.chunked || a.gather || !a.xscale) return hipErrorInvalidValue;
   if (p.preset >= 0) {
     switch (p.preset) {
-#define SPENSE_PRESET(i, nw, nr, pp, ch, mt) \
-  case i: return launch_stream8_k<nw, nr, pp, ch, mt>(d, a, p, s);
+#define SPENSE_PRESET(i, nw, nr, pp, ch, mt)                                     \
+  case i:                                                                        \
+    if constexpr (preset_single_pass_variant(i)) {                               \
+      if (p.mgroups == 1) return launch_stream8_k<nw, nr, pp, ch, mt, true>(d, a, p, s); \
+    }                                                                            \
+    return launch_stream8_k<nw, nr, pp, ch, mt, false>(d, a, p, s);
       SPENSE_TILE_PRESETS(SPENSE_PRESET)
 #undef SPENSE_PRESET
       default: return hipErrorInvalidValue;
     }
   }
   switch (p.waves * 100 + p.depth) {
-    case 404: return launch_stream8_k<4, 1, 4, kStreamChunk, 1>(d, a, p, s);
-    case 408: return launch_stream8_k<4, 1, 8, kStreamChunk, 1>(d, a, p, s);
-    case 804: return launch_stream8_k<8, 1, 4, kStreamChunk, 1>(d, a, p, s);
-    case 808: return launch_stream8_k<8, 1, 8, kStreamChunk, 1>(d, a, p, s);
+    case 404: return launch_stream8_k<4, 1, 4, kStreamChunk, 1, true>(d, a, p, s);
+    case 408: return launch_stream8_k<4, 1, 8, kStreamChunk, 1, true>(d, a, p, s);
+    case 804: return launch_stream8_k<8, 1, 4, kStreamChunk, 1, true>(d, a, p, s);
+    case 808: return launch_stream8_k<8, 1, 8, kStreamChunk, 1, true>(d, a, p, s);
     default: return hipErrorInvalidValue;
   }
 }

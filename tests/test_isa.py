@@ -100,3 +100,42 @@ def test_main_loops_keep_loads_in_flight(gfx950_asm):
         checked += 1
         assert min(main["vm"]) >= 4, (name[:90], sorted(set(main["vm"])))
     assert checked > 20
+
+
+def _main_loop(body):
+    """Lines of the depth-1 loop with the most structured-sparse instructions."""
+    loops, cur = {}, None
+    for line in body.splitlines():
+        if line.startswith(".LBB"):
+            hm = re.search(r"Header=(\w+) Depth=1", line)
+            cur = line.split(":")[0][1:] if "Loop Header: Depth=1" in line else (hm.group(1) if hm else None)
+        if cur:
+            loops.setdefault(cur, []).append(line)
+    return max(loops.values(), key=lambda ls: sum("v_smfmac" in x for x in ls), default=[])
+
+
+def test_weights_read_once_stream_non_temporally(gfx950_asm):
+    """Kernels that read each weight byte once (the decode kernels and the
+    streaming kernels built for one m-group, template flag true) load the
+    weight units with the non-temporal hint; the streaming kernels built for
+    several m-groups (flag false), which re-read their weights from L2, do
+    not."""
+    labels = [(m.start(), m.group(1)) for m in re.finditer(r"^(_Z\w+):", gfx950_asm, re.M)]
+    seen = {"decode": 0, "nt": 0, "default": 0}
+    for i, (pos, name) in enumerate(labels):
+        body = gfx950_asm[pos:labels[i + 1][0] if i + 1 < len(labels) else len(gfx950_asm)]
+        loop = _main_loop(body)
+        if "linear_decode" in name:
+            loads = [x for x in loop if re.search(r"\sglobal_load_dwordx4\s", x)]
+            assert loads and all(x.rstrip().endswith(" nt") for x in loads), (name[:90], loads[:3])
+            seen["decode"] += 1
+        elif "linear_stream" in name:
+            loads = [x for x in loop if re.search(r"\sbuffer_load_dwordx4\s", x)]
+            nt = [x for x in loads if re.search(r"\snt\b", x)]
+            if "Lb1EEEv" in name:  # last template argument (the one-m-group flag) true
+                assert nt, name[:90]
+                seen["nt"] += 1
+            else:
+                assert loads and not nt, (name[:90], nt[:3])
+                seen["default"] += 1
+    assert seen["decode"] >= 8 and seen["nt"] >= 8 and seen["default"] >= 20, seen
