@@ -489,8 +489,10 @@ static int plan_linear(const spense_layer* h, int64_t M, int32_t splits, int64_t
         while (S < max_splits && decode_lds_bytes(d, M, S) > 64 * 1024) ++S;
     }
     // chunked staging keeps eight waves per workgroup as well (measured on
-    // the gate/up layer at M = 8 and 16: 6-7% faster than four)
+    // the gate/up layer at M = 8 and 16: 6-7% faster than four) with eight
+    // units in flight per wave (4% faster than four there)
     p.chunked = (force_chunked || ch == 1 || decode_lds_bytes(d, M, S) > 64 * 1024) ? 1 : 0;
+    if (p.chunked && !overridden) p.depth = 8;
     p.rgroups = (int)((d.NT + p.waves - 1) / p.waves);
     if (S > 1 && S * M * d.NT * 64 >= (int64_t(1) << 31)) return SPENSE_EUNSUPPORTED;  // 32-bit partial offsets
     p.splits = (int)S;
