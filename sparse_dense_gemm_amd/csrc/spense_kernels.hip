@@ -542,6 +542,29 @@ __device__ __forceinline__ u32x4 gather8_from(const uint16_t* xr, const u32x4& i
   return val;
 }
 
+// Steps [n s / S, n (s + 1) / S) of split s of S.  Launch set-up runs before
+// a wave's first weight load, so it avoids 64-bit division: n < 2^16 (K_p <
+// 2^23) and S <= 64 keep n (s + 1) below 2^31, and one split needs none.
+__device__ __forceinline__ void split_range(int64_t n, int s, int S, int& lo, int& hi) {
+  if (S == 1) {
+    lo = 0;
+    hi = (int)n;
+    return;
+  }
+  lo = (int)((uint32_t)((int)n * s) / (uint32_t)S);
+  hi = (int)((uint32_t)((int)n * (s + 1)) / (uint32_t)S);
+}
+
+// n / d for 0 <= n < 2^24 with a quotient below 16 (a staged activation row
+// index): the float estimate n * rcp (rcp ~ 1/d) is within one of the
+// quotient, and one correction step makes it exact.
+__device__ __forceinline__ int small_quotient(int n, int d, float rcp) {
+  int q = (int)((float)n * rcp);
+  const int r = n - q * d;
+  q += r < 0 ? -1 : (r >= d ? 1 : 0);
+  return q;
+}
+
 // Gathers 8 activations X'p[row][col..col+8) (col a multiple of 8).
 __device__ __forceinline__ u32x4 gather8(const LinearArgs& a, const LayerDesc& d, const uint16_t* xr, int64_t col) {
   if (!a.gather) return *(const u32x4*)(xr + col);
@@ -562,14 +585,15 @@ __device__ __forceinline__ void decode_body(const LayerDesc& d, const LinearArgs
   int& last_flag = *last_flag_p;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar address math
-  const int rg = block % p.rgroups;
-  const int S = p.splits;
-  const int s = (block / p.rgroups) % S;
+  const int S = p.splits;  // the grid is rgroups x S workgroups
+  const int rg = S == 1 ? block : (int)((uint32_t)block % (uint32_t)p.rgroups);
+  const int s = S == 1 ? 0 : (int)((uint32_t)block / (uint32_t)p.rgroups);
   const int64_t rt = (int64_t)rg * NW + wave;
   const bool active = rt < d.NT;
-  const int64_t ms0 = d.n_sm * s / S, ms1 = d.n_sm * (s + 1) / S;
-  const int64_t md0 = d.n_dm * s / S, md1 = d.n_dm * (s + 1) / S;
-  const int ns = (int)(ms1 - ms0), nd = (int)(md1 - md0);
+  int ms0, ms1, md0, md1;
+  split_range(d.n_sm, s, S, ms0, ms1);
+  split_range(d.n_dm, s, S, md0, md1);
+  const int ns = ms1 - ms0, nd = md1 - md0;
   const int total = ns + 2 * nd;  // units
   const int M = (int)a.M;
   const int m = lane & 15, g = lane >> 4;
@@ -585,6 +609,21 @@ __device__ __forceinline__ void decode_body(const LayerDesc& d, const LinearArgs
   auto unit_ptr = [&](int k) { return tile + (k + (k < ns ? sbase : dbase)) * kUnit<WT>; };
   auto idx_ptr = [&](int k) { return k < ns ? sidx + k * 256 : unit_ptr(k); };
 
+  // weight ring; waves without units (past the last row tile, or an empty
+  // split) load unit 0 of tile 0 so that every wave issues the same loads
+  const bool stream = active && total > 0;
+  UnitFrag<WT> wr[P];
+  auto issue_ring = [&]() {
+#pragma unroll
+    for (int i = 0; i < P; ++i) {
+      const int k = i < total ? i : total - 1;
+      load_unit<WT>(wr[i], stream ? unit_ptr(k) : d.wpack, (stream ? idx_ptr(k) : d.wpack) + 4 * lane, lane);
+    }
+  };
+  // Contiguous activations: the weight ring goes out first, so the staging
+  // set-up below runs while the first weight units are in flight.
+  if constexpr (!GATHER) issue_ring();
+
   const TileOut to = tile_out(d, active ? rt : 0, lane);
 
   // Stage X'p[0..M)[split columns] in LDS once: sparse macro-steps, then
@@ -592,14 +631,20 @@ __device__ __forceinline__ void decode_body(const LayerDesc& d, const LinearArgs
   // loads, then all activation loads, then the LDS writes, so a batch costs one
   // (contiguous) or two (gathered) memory round trips).  Every thread issues
   // every load of a batch: pieces past the end read piece 0 (a valid address)
-  // and are not stored, so the load count is fixed.  The first batch's
-  // activation loads go out before the weight ring, so writing them to LDS
-  // does not wait for the ring.
+  // and are not stored, so the load count is fixed.  Gathered: the first
+  // batch's column-index loads go out before the weight ring, so the
+  // activation loads that depend on them do not wait for the ring.  Offsets
+  // are 32-bit: rows < 16 and the leading dimension < 2^23 (the entry points
+  // refuse larger ones), columns < K_p < 2^23.
   const uint16_t* X = (const uint16_t*)a.X;
   const int per_row = (ns + nd) * 16;
   const int pieces = M * per_row;
+  const float rcp_row = 1.0f / (float)(per_row > 0 ? per_row : 1);
+  const int ldx = (int)a.ldx;
+  // X'p column of unit-step u: 128 u + (u < ns ? xcol_s : xcol_d)
+  const int xcol_s = 128 * ms0, xcol_d = (int)d.K_sp + 128 * (md0 - ns);
   constexpr int kStageBatch = GATHER ? 2 : 8;
-  int64_t rowoff[kStageBatch], col[kStageBatch];
+  int rowoff[kStageBatch], col[kStageBatch];
   int lds_off[kStageBatch];
   bool ok[kStageBatch];
   u32x4 val[kStageBatch], i0[kStageBatch], i1[kStageBatch];
@@ -609,11 +654,11 @@ __device__ __forceinline__ void decode_body(const LayerDesc& d, const LinearArgs
       const int e = e0 + j * NW * 64;
       ok[j] = e < pieces;
       const int ee = ok[j] ? e : 0;
-      const int mrow = ee / per_row;
+      const int mrow = small_quotient(ee, per_row, rcp_row);
       const int rem = ee - mrow * per_row;
       const int u = rem >> 4, c8 = rem & 15;
-      rowoff[j] = (int64_t)mrow * a.ldx;
-      col[j] = (u < ns ? 128 * (ms0 + u) : d.K_sp + 128 * (md0 + u - ns)) + 8 * c8;
+      rowoff[j] = mrow * ldx;
+      col[j] = 128 * u + (u < ns ? xcol_s : xcol_d) + 8 * c8;
       lds_off[j] = mrow * pitch + 128 * u + 8 * c8;
     }
   };
@@ -644,16 +689,7 @@ __device__ __forceinline__ void decode_body(const LayerDesc& d, const LinearArgs
     locate(threadIdx.x);
     load_first();
   }
-
-  // weight ring; waves without units (past the last row tile, or an empty
-  // split) load unit 0 of tile 0 so that every wave issues the same loads
-  const bool stream = active && total > 0;
-  UnitFrag<WT> wr[P];
-#pragma unroll
-  for (int i = 0; i < P; ++i) {
-    const int k = i < total ? i : total - 1;
-    load_unit<WT>(wr[i], stream ? unit_ptr(k) : d.wpack, (stream ? idx_ptr(k) : d.wpack) + 4 * lane, lane);
-  }
+  if constexpr (GATHER) issue_ring();
 
   if (staging) {
     load_second();
@@ -809,14 +845,23 @@ __device__ __forceinline__ void stream_body(const LayerDesc& d, const LinearArgs
   // about the same time, and all but the first read it from that XCD's L2.
   int b = block;
   if (p.xcd_remap) b = (b % 8) * (grid / 8) + b / 8;
+  // logical id = (s * rgroups + rg) * mgroups + mg; one m-group or one split
+  // (every decode launch) skips its division
   const int S = p.splits;
-  const int mg = b % p.mgroups;
-  const int rg = (b / p.mgroups) % p.rgroups;
-  const int s = b / (p.mgroups * p.rgroups);
+  int mg = 0, rg = b, s = 0;
+  if (p.mgroups > 1) {
+    mg = (int)((uint32_t)b % (uint32_t)p.mgroups);
+    rg = (int)((uint32_t)b / (uint32_t)p.mgroups);
+  }
+  if (S > 1) {
+    s = (int)((uint32_t)rg / (uint32_t)p.rgroups);
+    rg = (int)((uint32_t)rg % (uint32_t)p.rgroups);
+  }
   const int64_t rt0 = ((int64_t)rg * NW + wave) * NR;
-  const int64_t ms0 = d.n_sm * s / S, ms1 = d.n_sm * (s + 1) / S;
-  const int64_t md0 = d.n_dm * s / S, md1 = d.n_dm * (s + 1) / S;
-  const int ns = (int)(ms1 - ms0), nd = (int)(md1 - md0);
+  int ms0, ms1, md0, md1;
+  split_range(d.n_sm, s, S, ms0, ms1);
+  split_range(d.n_dm, s, S, md0, md1);
+  const int ns = ms1 - ms0, nd = md1 - md0;
   const int total = ns + 2 * nd;  // units
   const int nchunks = (total + CH - 1) / CH;
   const int64_t m0 = (int64_t)mg * 16 * MT;
