@@ -446,6 +446,9 @@ constexpr int64_t kCUs = 256;             // compute units of the target GPU
 // 32-bit offsets (128 staged rows of bf16)
 constexpr int64_t kMaxLd = int64_t(1) << 23;
 constexpr int64_t kLdsPerCU = 160 * 1024;  // LDS bytes per CU
+// dynamic LDS a kernel may take: the CU's LDS less room for the kernels' static
+// shared variables
+constexpr int64_t kMaxDynLds = kLdsPerCU - 1024;
 
 // NT_fill: row tiles launched in the same grid (the layer's own, or both row
 // classes of an output-split layer); the split count and the blocking are
@@ -482,16 +485,25 @@ static int plan_linear(const spense_layer* h, int64_t M, int32_t splits, int64_t
       p.depth = dp;
     }
     int64_t S = splits;
+    // Single-shot staging keeps the split's activations in LDS for the whole
+    // kernel.  Beyond 64 KB only one workgroup fits on a CU, which costs
+    // nothing while the grid has no more workgroups than CUs (gate/up 25600 x
+    // 5120: 200); there it beats chunked staging up to the CU's 160 KB (M = 8:
+    // 19.6 -> 19.1 us, M = 12: 20.1 -> 19.3 us).
+    auto lds_cap = [&](int64_t splits_) {
+      const int64_t wgs = (NT_fill + p.waves - 1) / p.waves * splits_;
+      return wgs <= kCUs ? kMaxDynLds : int64_t(64) * 1024;
+    };
     if (S == 0) {
       S = NT_fill >= 1024 ? 1 : std::max<int64_t>(1, (1920 + NT_fill - 1) / NT_fill);
       S = std::min<int64_t>(S, max_splits);
       if (ch == 0)  // single-shot staging requested: split until it fits
-        while (S < max_splits && decode_lds_bytes(d, M, S) > 64 * 1024) ++S;
+        while (S < max_splits && decode_lds_bytes(d, M, S) > lds_cap(S)) ++S;
     }
     // chunked staging keeps eight waves per workgroup as well (measured on
     // the gate/up layer at M = 8 and 16: 6-7% faster than four) with eight
     // units in flight per wave (4% faster than four there)
-    p.chunked = (force_chunked || ch == 1 || decode_lds_bytes(d, M, S) > 64 * 1024) ? 1 : 0;
+    p.chunked = (force_chunked || ch == 1 || decode_lds_bytes(d, M, S) > lds_cap(S)) ? 1 : 0;
     if (p.chunked && !overridden) p.depth = 8;
     p.rgroups = (int)((d.NT + p.waves - 1) / p.waves);
     if (S > 1 && S * M * d.NT * 64 >= (int64_t(1) << 31)) return SPENSE_EUNSUPPORTED;  // 32-bit partial offsets
@@ -546,7 +558,7 @@ static int plan_linear(const spense_layer* h, int64_t M, int32_t splits, int64_t
   // or that takes e4m3 codes only, is ignored
     const int v = std::atoi(t);
     if (v >= 0 && v < kNumPresets && (xbytes == 1 || !preset_codes_only(v)) &&
-        stream_lds_bytes(std::min<int64_t>(M, 16 * kPresets[v].mt), kPresets[v].ch, xbytes) <= kLdsPerCU)
+        stream_lds_bytes(std::min<int64_t>(M, 16 * kPresets[v].mt), kPresets[v].ch, xbytes) <= kMaxDynLds)
       pre = v;
   }
   const Preset& q = kPresets[pre];

@@ -1297,11 +1297,15 @@ hipError_t allow_lds(K kernel, int bytes) {
 
 template <typename WT, int NW, int P, bool GATHER>
 hipError_t launch_decode_k(const Launch& L, hipStream_t s) {
+  hipError_t e;
   if (L.two) {
-    linear_decode2_kernel<WT, NW, P, GATHER><<<L.grid(), NW * 64, L.lds(), s>>>(*L.d[0], *L.a[0], *L.p[0], *L.d[1],
-                                                                              *L.a[1], *L.p[1]);
+    auto k = linear_decode2_kernel<WT, NW, P, GATHER>;
+    if ((e = allow_lds(k, L.lds())) != hipSuccess) return e;
+    k<<<L.grid(), NW * 64, L.lds(), s>>>(*L.d[0], *L.a[0], *L.p[0], *L.d[1], *L.a[1], *L.p[1]);
   } else {
-    linear_decode_kernel<WT, NW, P, GATHER><<<L.grid(), NW * 64, L.lds(), s>>>(*L.d[0], *L.a[0], *L.p[0]);
+    auto k = linear_decode_kernel<WT, NW, P, GATHER>;
+    if ((e = allow_lds(k, L.lds())) != hipSuccess) return e;
+    k<<<L.grid(), NW * 64, L.lds(), s>>>(*L.d[0], *L.a[0], *L.p[0]);
   }
   return hipGetLastError();
 }

@@ -276,6 +276,42 @@ def test_decode_variants(wdtype, dense, monkeypatch):
         sdg.spense_free(h)
 
 
+@pytest.mark.parametrize("wdtype", [DT_FP8, DT_BF16])
+@pytest.mark.parametrize("dense", [("frac", 0.25), ("rand", 1280)])
+def test_single_shot_staging_beyond_64kb(wdtype, dense, monkeypatch):
+    """Batch sizes whose activations exceed 64 KB of LDS but fit a CU's 160 KB
+    (K = 5120 in one split, M = 7..15, a grid of fewer workgroups than CUs) run the
+    single-shot decode kernel: the result equals the chunked kernel's bit for
+    bit (same products, same order) and the oracle within tolerance."""
+    N, K = 160, 5120
+    W, s = _small(N, K, wdtype, 41)
+    X = synth.make_x(15, K, DT_BF16, np.random.default_rng(42))
+    sd = to_dev(s, DT_F32) if s is not None else None
+    if dense[0] == "frac":
+        h = pack_dev(to_dev(W, wdtype), wdtype, sd, dense_fraction=dense[1])
+        pi, K_s, _ = oracle.resolve_dense_set(K, dense_fraction=dense[1])
+        D = np.sort(pi[K_s:])
+    else:
+        D = synth.random_dense_set(K, dense[1], 43)
+        h = pack_dev(to_dev(W, wdtype), wdtype, sd, dense_cols=D)
+    try:
+        ref = oracle_pack_rows(W, wdtype, D)
+        Xd = to_dev(X, DT_BF16)
+        for M in (7, 8, 12, 15):
+            Yref, B = oracle.linear_ref(X[:M], DT_BF16, ref, s)
+            # one split: the whole K range (M x 5128 bf16 = 72-154 KB) staged at once
+            monkeypatch.delenv("SPENSE_DECODE", raising=False)
+            Y1 = linear_dev(h, Xd[:M], N, splits=1).cpu().numpy()
+            monkeypatch.setenv("SPENSE_DECODE", "8,4,1")  # chunked staging
+            Y2 = linear_dev(h, Xd[:M], N, splits=1).cpu().numpy()
+            assert np.array_equal(Y1, Y2), M
+            r = tol_ratio(Y1, Yref, B)
+            assert r <= 1.0, (M, r)
+        log(f"[single-shot > 64 KB] wdtype={wdtype} dense={dense}: equal to chunked, within tolerance")
+    finally:
+        sdg.spense_free(h)
+
+
 TILE_PRESETS = list(range(15))
 
 
