@@ -281,8 +281,10 @@ def test_decode_variants(wdtype, dense, monkeypatch):
 def test_single_shot_staging_beyond_64kb(wdtype, dense, monkeypatch):
     """Batch sizes whose activations exceed 64 KB of LDS but fit a CU's 160 KB
     (K = 5120 in one split, M = 7..15, a grid of fewer workgroups than CUs) run the
-    single-shot decode kernel: the result equals the chunked kernel's bit for
-    bit (same products, same order) and the oracle within tolerance."""
+    single-shot decode kernel when the activations are contiguous (tail dense
+    set; a chosen set is gathered and keeps chunked staging): the result equals
+    the chunked kernel's bit for bit (same products, same order) and the oracle
+    within tolerance."""
     N, K = 160, 5120
     W, s = _small(N, K, wdtype, 41)
     X = synth.make_x(15, K, DT_BF16, np.random.default_rng(42))
