@@ -1162,16 +1162,16 @@ __global__ __launch_bounds__(256) void quantize_tokens_kernel(const uint16_t* __
   const int tid = threadIdx.x;
   float amax = 0.f;
   if (((uintptr_t)x % 16) == 0 && K % 8 == 0) {
-    // four 16-byte loads in flight per thread
-    for (int64_t k0 = 8 * (int64_t)tid; k0 < K; k0 += 4 * 8 * 256) {
-      u32x4 v[4];
+    // eight 16-byte loads in flight per thread
+    for (int64_t k0 = 8 * (int64_t)tid; k0 < K; k0 += 8 * 8 * 256) {
+      u32x4 v[8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < 8; ++u) {
         const int64_t k = k0 + u * 8 * 256;
         v[u] = k < K ? *(const u32x4*)(x + k) : u32x4{0u, 0u, 0u, 0u};
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < 8; ++u) {
         const int64_t k = k0 + u * 8 * 256;
         if (STAGE && k < K) *(u32x4*)(xrow + k) = v[u];
 #pragma unroll
@@ -1198,25 +1198,40 @@ __global__ __launch_bounds__(256) void quantize_tokens_kernel(const uint16_t* __
   const uint16_t* src_row = STAGE ? xrow : x;
   uint8_t* q = Q + mrow * ldq;
   const bool vec_out = ((uintptr_t)q % 4) == 0;
-  for (int64_t j0 = 4 * (int64_t)tid; j0 < Kout; j0 += 4 * 256) {
-    int src[4];
-    if (pip && j0 + 4 <= Kout) {
-      const u32x4 p4 = *(const u32x4*)(pip + j0);
+  // Thread t writes 4 consecutive codes per step; the column indices of
+  // kBatch steps are loaded together, so a row costs one memory round trip
+  // per kBatch steps instead of one per step (K = 27648: 27 steps).
+  constexpr int kBatch = 8;
+  for (int64_t jb = 4 * (int64_t)tid; jb < Kout; jb += (int64_t)4 * 256 * kBatch) {
+    int src[kBatch][4];
 #pragma unroll
-      for (int t = 0; t < 4; ++t) src[t] = (int)p4[t];
-    } else {
+    for (int u = 0; u < kBatch; ++u) {
+      const int64_t j0 = jb + (int64_t)u * 4 * 256;
+      if (pip && j0 + 4 <= Kout) {
+        const u32x4 p4 = *(const u32x4*)(pip + j0);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) src[t] = j0 + t < Kout ? (pip ? pip[j0 + t] : (int)(j0 + t)) : -1;
+        for (int t = 0; t < 4; ++t) src[u][t] = (int)p4[t];
+      } else {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) src[u][t] = j0 + t < Kout ? (pip ? pip[j0 + t] : (int)(j0 + t)) : -1;
+      }
     }
-    float v[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) v[t] = src[t] >= 0 ? __uint_as_float((uint32_t)src_row[src[t]] << 16) / scale : 0.f;
-    int w = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
-    w = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], w, true);
-    if (vec_out && j0 + 4 <= Kout) {
-      *(uint32_t*)(q + j0) = (uint32_t)w;
-    } else {
-      for (int t = 0; t < 4 && j0 + t < Kout; ++t) q[j0 + t] = (uint8_t)((uint32_t)w >> (8 * t));
+    for (int u = 0; u < kBatch; ++u) {
+      const int64_t j0 = jb + (int64_t)u * 4 * 256;
+      if (j0 < Kout) {
+        float v[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+          v[t] = src[u][t] >= 0 ? __uint_as_float((uint32_t)src_row[src[u][t]] << 16) / scale : 0.f;
+        int w = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+        w = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], w, true);
+        if (vec_out && j0 + 4 <= Kout) {
+          *(uint32_t*)(q + j0) = (uint32_t)w;
+        } else {
+          for (int t = 0; t < 4 && j0 + t < Kout; ++t) q[j0 + t] = (uint8_t)((uint32_t)w >> (8 * t));
+        }
+      }
     }
   }
 }
