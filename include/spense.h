@@ -32,6 +32,11 @@
  *   - The library is not thread-safe per handle: at most one spense_linear may
  *     be in flight on a handle at a time (its split-K and gather workspaces
  *     are shared).
+ *   - spense_linear, spense_linear_w8a8 and spense_glu may be captured in a HIP
+ *     graph once an eager call on the same handle with at least the same batch
+ *     size has sized the handle's workspaces (a call that grows them
+ *     synchronises the stream and allocates).  The calls record kernel launches
+ *     only; the split-K hand-off counters are reset by the kernels.
  */
 #ifndef SPENSE_H
 #define SPENSE_H
