@@ -1,4 +1,4 @@
-"""spense_linear / spense_linear_w8a8 captured in a HIP graph (through torch's
+"""spense_linear / spense_linear_w8a8 / spense_glu captured in a HIP graph (through torch's
 graph capture on a side stream) and replayed: every replay equals the eager
 call bit for bit.  Each configuration is called once eagerly first, so its
 workspaces exist before capture (a call that grows them synchronises the
@@ -77,5 +77,43 @@ def test_graph_replays_equal_eager(form, M, splits, a8):
             torch.cuda.synchronize()
             assert torch.equal(other, Y_eager), (form, M, splits, a8, rep)
         log(f"[graph] {form} M={M} splits={splits} a8={a8}: 3 replays equal eager")
+    finally:
+        sdg.spense_free(h)
+
+
+@pytest.mark.parametrize("M", [4, 40])
+def test_graph_replays_of_the_glu_block_equal_eager(M):
+    H, I = 256, 512
+    Wgu, sgu = synth.make_weight(2 * I, H, DT_FP8, np.random.default_rng(61))
+    Wdn, sdn = synth.make_weight(H, I, DT_FP8, np.random.default_rng(62))
+    h = sdg.spense_pack_glu(to_dev(Wgu, DT_FP8), to_dev(Wdn, DT_FP8), DT_FP8, H=H, I=I, s_gu=to_dev(sgu, DT_F32),
+                            s_down=to_dev(sdn, DT_F32), dense_idx=synth.random_dense_set(I, 128, 63))
+    try:
+        X = to_dev(synth.make_x(M, H, DT_BF16, np.random.default_rng(64)), DT_BF16)
+        A, A_eager = (torch.empty((M, I), dtype=torch.bfloat16, device="cuda") for _ in range(2))
+        Y, Y_eager = (torch.empty((M, H), dtype=torch.float32, device="cuda") for _ in range(2))
+        sdg.spense_glu(h, X, A_eager, Y_eager)
+        torch.cuda.synchronize()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            sdg.spense_glu(h, X, A, Y)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            sdg.spense_glu(h, X, A, Y)
+        torch.cuda.synchronize()
+        A2, Y2 = torch.empty_like(A), torch.empty_like(Y)
+        for rep in range(3):
+            A.fill_(float("nan"))
+            Y.fill_(float("nan"))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(A, A_eager) and torch.equal(Y, Y_eager), (M, rep)
+            sdg.spense_glu(h, X, A2, Y2)  # eager work between replays
+            torch.cuda.synchronize()
+            assert torch.equal(Y2, Y_eager), (M, rep)
+        log(f"[graph] GLU block M={M}: 3 replays equal eager")
     finally:
         sdg.spense_free(h)
