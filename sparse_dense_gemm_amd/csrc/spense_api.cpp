@@ -535,14 +535,17 @@ static int plan_linear(const spense_layer* h, int64_t M, int32_t splits, int64_t
   // m-tiles and four row tiles, else two row tiles, whose smaller staged rows
   // let more workgroups share a CU), then eight waves with two row tiles and
   // a deeper ring, then two m-tiles, then one row tile; at M <= 32 one m-group
-  // of two m-tiles with two row tiles per wave, or a single row tile.
+  // of two m-tiles with two row tiles per wave, or a single row tile (eight
+  // waves per workgroup: at M = 32 the QKV 10240 x 5120, O 5120 x 8192 and
+  // down 5120 x 25600 layers took 20.7 / 17.0 / 38.1 us with four and 16.9 /
+  // 16.8 / 33.6 us with eight).
   auto workgroups = [&](int i) {
     const Preset& c = kPresets[i];
     return (NT_fill + c.nw * c.nr - 1) / (c.nw * c.nr) * ((M + 16 * c.mt - 1) / (16 * c.mt));
   };
   int pre;
   if (M <= 32) {
-    pre = workgroups(2) >= 150 ? 2 : 7;
+    pre = workgroups(2) >= 150 ? 2 : 0;
   } else {
     // (preset, workgroups it needs before splits); e4m3 codes first try eight
     // m-tiles per wave (four row tiles), which halves the weight bytes loaded

@@ -125,7 +125,7 @@ struct LinearPlan {
 constexpr bool preset_codes_only(int i) { return i == 13; }
 // presets the planner runs with one m-group (M <= 32): also built with
 // non-temporal weight loads, used when a launch has a single m-group
-constexpr bool preset_single_pass_variant(int i) { return i == 2 || i == 7; }
+constexpr bool preset_single_pass_variant(int i) { return i == 0 || i == 2; }
 
 constexpr int kStreamChunk = 8;  // units per activation chunk of linear_stream_kernel
 
