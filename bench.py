@@ -397,8 +397,6 @@ def main():
 
 def run_glu(args, torch, sdg, synth, wl):
     """The GLU block workload: spense_glu per batch size, all-dense block as the baseline."""
-    import oracle
-
     gu, dn = wl.layers
     H, I = dn.N, dn.K
     Ms = tuple(int(m) for m in args.ms.split(",")) if args.ms else wl.Ms
@@ -508,6 +506,8 @@ def run_glu(args, torch, sdg, synth, wl):
     ach = sum(alg(M) for M in Ms) / total / 1e3
     cpu = None
     if not args.no_cpu_baseline:
+        import oracle  # the CPU baseline leg only
+
         rows, M0 = 256, min(Ms)
         t0 = time.perf_counter()
         oracle.glu_block_ref(X[:M0], oracle.DT_BF16, Wgu[:rows], Wgu[I:I + rows], Wd[:, :rows], gu.wdtype,
