@@ -1150,29 +1150,33 @@ __global__ void gather_x_kernel(LayerDesc d, const uint16_t* __restrict__ X, int
 // pip[j] when a column map is given (the X'p order of a layer; -1: zero).
 // With STAGE the row is kept in LDS between the two passes (the re-ordering
 // then gathers from LDS); otherwise the second pass reads it again.
+// threads per token: two workgroups per CU fit a 27648-column row in LDS,
+// so wide workgroups keep more waves resident
+constexpr int kQuantThreads = 512;
+
 template <bool STAGE>
-__global__ __launch_bounds__(256) void quantize_tokens_kernel(const uint16_t* __restrict__ X, int64_t K, int64_t ldx,
+__global__ __launch_bounds__(kQuantThreads) void quantize_tokens_kernel(const uint16_t* __restrict__ X, int64_t K, int64_t ldx,
                                                               const int32_t* __restrict__ pip, int64_t Kout,
                                                               uint8_t* __restrict__ Q, int64_t ldq,
                                                               float* __restrict__ sx) {
   extern __shared__ __attribute__((aligned(16))) uint16_t xrow[];
-  __shared__ float wmax[4];
+  __shared__ float wmax[kQuantThreads / 64];
   const int64_t mrow = blockIdx.x;
   const uint16_t* x = X + mrow * ldx;
   const int tid = threadIdx.x;
   float amax = 0.f;
   if (((uintptr_t)x % 16) == 0 && K % 8 == 0) {
     // eight 16-byte loads in flight per thread
-    for (int64_t k0 = 8 * (int64_t)tid; k0 < K; k0 += 8 * 8 * 256) {
+    for (int64_t k0 = 8 * (int64_t)tid; k0 < K; k0 += 8 * 8 * kQuantThreads) {
       u32x4 v[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int64_t k = k0 + u * 8 * 256;
+        const int64_t k = k0 + u * 8 * kQuantThreads;
         v[u] = k < K ? *(const u32x4*)(x + k) : u32x4{0u, 0u, 0u, 0u};
       }
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        const int64_t k = k0 + u * 8 * 256;
+        const int64_t k = k0 + u * 8 * kQuantThreads;
         if (STAGE && k < K) *(u32x4*)(xrow + k) = v[u];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -1182,7 +1186,7 @@ __global__ __launch_bounds__(256) void quantize_tokens_kernel(const uint16_t* __
       }
     }
   } else {
-    for (int64_t k = tid; k < K; k += 256) {
+    for (int64_t k = tid; k < K; k += kQuantThreads) {
       const uint16_t v = x[k];
       if (STAGE) xrow[k] = v;
       amax = fmaxf(amax, __uint_as_float((uint32_t)(v & 0x7FFFu) << 16));
@@ -1192,7 +1196,9 @@ __global__ __launch_bounds__(256) void quantize_tokens_kernel(const uint16_t* __
   for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
   if ((tid & 63) == 0) wmax[tid >> 6] = amax;
   __syncthreads();
-  amax = fmaxf(fmaxf(wmax[0], wmax[1]), fmaxf(wmax[2], wmax[3]));
+  amax = wmax[0];
+#pragma unroll
+  for (int w = 1; w < kQuantThreads / 64; ++w) amax = fmaxf(amax, wmax[w]);
   const float scale = amax > 0.f ? amax / 448.0f : 1.0f;
   if (tid == 0) sx[mrow] = scale;
   const uint16_t* src_row = STAGE ? xrow : x;
@@ -1202,11 +1208,11 @@ __global__ __launch_bounds__(256) void quantize_tokens_kernel(const uint16_t* __
   // kBatch steps are loaded together, so a row costs one memory round trip
   // per kBatch steps instead of one per step (K = 27648: 27 steps).
   constexpr int kBatch = 8;
-  for (int64_t jb = 4 * (int64_t)tid; jb < Kout; jb += (int64_t)4 * 256 * kBatch) {
+  for (int64_t jb = 4 * (int64_t)tid; jb < Kout; jb += (int64_t)4 * kQuantThreads * kBatch) {
     int src[kBatch][4];
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      const int64_t j0 = jb + (int64_t)u * 4 * 256;
+      const int64_t j0 = jb + (int64_t)u * 4 * kQuantThreads;
       if (pip && j0 + 4 <= Kout) {
         const u32x4 p4 = *(const u32x4*)(pip + j0);
 #pragma unroll
@@ -1218,7 +1224,7 @@ __global__ __launch_bounds__(256) void quantize_tokens_kernel(const uint16_t* __
     }
 #pragma unroll
     for (int u = 0; u < kBatch; ++u) {
-      const int64_t j0 = jb + (int64_t)u * 4 * 256;
+      const int64_t j0 = jb + (int64_t)u * 4 * kQuantThreads;
       if (j0 < Kout) {
         float v[4];
 #pragma unroll
@@ -1448,10 +1454,10 @@ hipError_t launch_quantize_tokens(const void* X, int64_t M, int64_t K, int64_t l
   if (M <= 0) return hipSuccess;
   // rows up to 32768 columns are kept in LDS between the passes (64 KB)
   if (K <= 32768)
-    quantize_tokens_kernel<true><<<(unsigned)M, 256, (size_t)K * 2, s>>>((const uint16_t*)X, K, ldx, pip, Kout, Q,
+    quantize_tokens_kernel<true><<<(unsigned)M, kQuantThreads, (size_t)K * 2, s>>>((const uint16_t*)X, K, ldx, pip, Kout, Q,
                                                                         ldq, sx);
   else
-    quantize_tokens_kernel<false><<<(unsigned)M, 256, 0, s>>>((const uint16_t*)X, K, ldx, pip, Kout, Q, ldq, sx);
+    quantize_tokens_kernel<false><<<(unsigned)M, kQuantThreads, 0, s>>>((const uint16_t*)X, K, ldx, pip, Kout, Q, ldq, sx);
   return hipGetLastError();
 }
 
