@@ -211,8 +211,18 @@ __device__ __forceinline__ void finish_tile(const LayerDesc& d, const LinearArgs
       if (m >= a.M) continue;
       f32x4 sum = acc[r * mtiles + mt];
       if (S > 1) {
+        // the partials in split order, loaded eight at a time (one memory
+        // round trip per eight splits instead of one per split); splits past
+        // S read zero at an out-of-range offset and are not added
         sum = f32x4{0.f, 0.f, 0.f, 0.f};
-        for (int s2 = 0; s2 < S; ++s2) sum += load_partial(wsr, poff(s2, rt, m));
+        for (int s0 = 0; s0 < S; s0 += 8) {
+          f32x4 part[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) part[j] = load_partial(wsr, s0 + j < S ? poff(s0 + j, rt, m) : 0x80000000u);
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            if (s0 + j < S) sum += part[j];
+        }
       }
       if (a.glu) {
         // rows (q, q+1) of this lane are the gate and up rows of one
