@@ -166,27 +166,53 @@ def test_hand_worked(case):
         assert np.array_equal(np.signbit(p.vals), np.signbit(np.array(e["vals"], dtype=np.float32)))
         assert np.array_equal(p.dense, np.array(e["dense"], dtype=np.float32).reshape(p.dense.shape))
         X = np.array(case["X"], dtype=np.float32)
-        Y, _ = oracle.linear_ref(X, DT_F32, p)
+        Y, B = oracle.linear_ref(X, DT_F32, p)
+    elif case["dtype"] == "bf16":
+        def bits(rows):
+            return np.array([[int(v, 16) for v in row] for row in rows], dtype=np.uint16)
+        W = bits(case["W_bits"])
+        p = oracle.pack(W, DT_BF16, pi, K_s)
+        assert np.array_equal(p.vals, bits(e["vals_bits"]))
+        assert np.array_equal(p.dense, bits(e["dense_bits"]))
+        X = synth.bf16_encode(np.array(case["X"], dtype=np.float64))
+        Y, B = oracle.linear_ref(X, DT_BF16, p)
     else:
         W = np.array(case["W_codes"], dtype=np.uint8)
         p = oracle.pack(W, DT_FP8, pi, K_s)
         assert p.vals.tolist() == e["vals_codes"]
         assert p.dense.reshape(-1).tolist() == [c for row in e["dense_codes"] for c in row]
         X = synth.bf16_encode(np.array(case["X"], dtype=np.float64))
-        Y, _ = oracle.linear_ref(X, DT_BF16, p, scales=np.array(case["scales"], dtype=np.float32))
+        Y, B = oracle.linear_ref(X, DT_BF16, p, scales=np.array(case["scales"], dtype=np.float32))
     assert p.meta.tolist() == e["meta"]
     assert p.mask.tolist() == e["mask"]
     assert np.array_equal(Y, np.array(e["Y"], dtype=np.float64))
+    # the error scale of the pass rule, worked by hand over the pruned weights
+    assert np.array_equal(B, np.array(e["B"], dtype=np.float64))
 
 
 # --------------------------------------------------------------------------
 # a2: the 2:4 choice, exhaustively
 # --------------------------------------------------------------------------
+def abs_order_key(bits, dtype):
+    """Magnitude of each stored element, decoded by torch (not by the oracle):
+    |value| in float64, with NaN above every number (the reading for NaN)."""
+    b = np.ascontiguousarray(bits)
+    if dtype == DT_F32:
+        v = torch.from_numpy(b.astype(np.float32)).to(torch.float64)
+    elif dtype == DT_BF16:
+        v = torch.from_numpy(b.astype(np.uint16).view(np.int16)).view(torch.bfloat16).to(torch.float64)
+    else:
+        v = torch.from_numpy(b.astype(np.uint8)).view(torch.float8_e4m3fn).to(torch.float64)
+    a = v.abs().numpy()
+    return np.where(np.isnan(a), np.inf, a)
+
+
 def _check_groups(W, dtype):
-    """W[n, 4]: one group per row; compare oracle's choice with dominance."""
+    """W[n, 4]: one group per row; compare oracle's choice with dominance on
+    the decoded magnitudes."""
     pi = np.arange(4)
     p = oracle.pack(W, dtype, pi, 4)
-    keys = oracle.magnitude_key(W, dtype)
+    keys = abs_order_key(W, dtype)
     nib = p.meta[:, 0] & 0xF
     for n in range(W.shape[0]):
         i0, i1 = dominance_pair(keys[n].tolist())
@@ -212,7 +238,7 @@ def test_tie_break_all_e4m3_code_pairs():
     for patt in ((a, b, b, a), (a, a, b, b), (b, a, a, b)):
         W = np.stack(patt, axis=1)
         p = oracle.pack(W, DT_FP8, np.arange(4), 4)
-        keys = oracle.magnitude_key(W, DT_FP8)
+        keys = abs_order_key(W, DT_FP8)
         # vectorised dominance: count for each candidate pair whether it dominates
         nib = (p.meta[:, 0] & 0xF).astype(np.int64)
         sel = np.zeros(W.shape[0], dtype=np.int64) - 1
@@ -227,6 +253,39 @@ def test_tie_break_all_e4m3_code_pairs():
             sel[ok] = P[0] | (P[1] << 2)
         assert np.all(sel >= 0)
         assert np.array_equal(sel, nib)
+
+
+@pytest.mark.parametrize("dtype", [DT_BF16, DT_FP8])
+def test_key_order_is_magnitude_order_every_code(dtype):
+    """Over every bf16 bit pattern and every e4m3 code (NaN excluded), the
+    oracle's key orders elements exactly as their magnitudes decoded by torch:
+    sorted by key, |value| never decreases, and two codes share a key exactly
+    when they share a magnitude (so +x and -x tie, and +0 ties -0)."""
+    n = 65536 if dtype == DT_BF16 else 256
+    codes = np.arange(n, dtype=np.uint32).astype(np.uint16 if dtype == DT_BF16 else np.uint8)
+    t = torch.from_numpy(codes.view(np.int16) if dtype == DT_BF16 else codes)
+    vals = t.view(torch.bfloat16 if dtype == DT_BF16 else torch.float8_e4m3fn).to(torch.float64).numpy()
+    keep = ~np.isnan(vals)
+    codes, a = codes[keep], np.abs(vals[keep])
+    key = oracle.magnitude_key(codes, dtype)
+    order = np.argsort(key, kind="stable")
+    k, v = key[order], a[order]
+    assert np.all(v[1:] >= v[:-1])
+    assert np.array_equal(k[1:] == k[:-1], v[1:] == v[:-1])
+    # every magnitude is held by exactly two codes (+ and -), both with one key
+    assert np.all(np.unique(key, return_counts=True)[1] == 2)
+
+
+def test_key_order_is_magnitude_order_fp32_sample():
+    rng = np.random.default_rng(17)
+    v = np.concatenate([rng.normal(0, 1, 20000), rng.normal(0, 1e-40, 2000), [0.0, -0.0, 1e-45, -1e-45, 3e38]])
+    v = np.concatenate([v, -v]).astype(np.float32)
+    key = oracle.magnitude_key(v, DT_F32)
+    a = np.abs(v.astype(np.float64))
+    order = np.argsort(key, kind="stable")
+    k, b = key[order], a[order]
+    assert np.all(b[1:] >= b[:-1])
+    assert np.array_equal(k[1:] == k[:-1], b[1:] == b[:-1])
 
 
 # --------------------------------------------------------------------------
@@ -315,16 +374,84 @@ def test_brute_force_every_dense_set_8x16():
         for D in itertools.combinations(range(K), kd):
             pi, K_s, K_d = oracle.resolve_dense_set(K, dense_cols=list(D))
             p = oracle.pack(W, DT_F32, pi, K_s)
-            Y, _ = oracle.linear_ref(X, DT_F32, p)
+            Y, B = oracle.linear_ref(X, DT_F32, p)
             Wp = prune_python(Wl, keys, pi, K_s)
             for m in range(M):
                 for n in range(N):
-                    acc = 0.0
+                    acc = bnd = 0.0
                     for k in range(K):
                         acc += Xl[m][k] * Wp[n][k]
+                        bnd += abs(Xl[m][k] * Wp[n][k])
                     assert Y[m, n] == acc
+                    assert B[m, n] == bnd
             count += 1
     assert count == 1 + 1820 + 12870 + 1820 + 1
+
+
+def test_brute_force_e4m3_with_scales_and_bound():
+    """e4m3 codes of small integers and halves, bf16 integer activations,
+    per-channel scales: the layer output and its error scale by plain loops
+    over weights pruned with the dominance rule on torch-decoded magnitudes
+    (every product and sum is exact in float64, so equality is exact)."""
+    rng = np.random.default_rng(18)
+    N, K, M = 6, 24, 3
+    vals = torch.tensor([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, -0.5, -1.0, -2.0, -3.0, -4.0, -0.0],
+                        dtype=torch.float32).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    W = rng.choice(vals, size=(N, K))
+    X = synth.bf16_encode(rng.integers(-7, 8, size=(M, K)).astype(np.float64))
+    s = np.array([0.375, 1.0, 2.5, 0.0078125, 1.75, 3.0], dtype=np.float32)
+    D = [0, 5, 6, 13, 14, 23, 2, 9]
+    pi, K_s, _ = oracle.resolve_dense_set(K, dense_cols=D)
+    Y, B = oracle.linear_ref(X, DT_BF16, oracle.pack(W, DT_FP8, pi, K_s), s)
+    mag = abs_order_key(W, DT_FP8).tolist()
+    wv = torch.from_numpy(W).view(torch.float8_e4m3fn).to(torch.float64).numpy().tolist()
+    xv = torch.from_numpy(X.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy().tolist()
+    for n in range(N):
+        row = list(wv[n])
+        for g in range(K_s // 4):
+            cols = [int(pi[4 * g + t]) for t in range(4)]
+            P = dominance_pair([mag[n][c] for c in cols])
+            for t in range(4):
+                if t not in P:
+                    row[cols[t]] = 0.0
+        for m in range(M):
+            acc = bnd = 0.0
+            for k in range(K):
+                acc += xv[m][k] * row[k]
+                bnd += abs(xv[m][k] * row[k])
+            assert Y[m, n] == float(s[n]) * acc
+            assert B[m, n] == float(s[n]) * bnd
+
+
+def test_down_ref_brute_force_loops():
+    """The down projection on float64 activations: output and error scale by
+    plain loops over the pruned weights (dominance rule, scales applied after
+    the sums); integer-valued inputs keep every sum exact."""
+    rng = np.random.default_rng(19)
+    H, I, M = 5, 16, 2
+    vals = torch.tensor([0.0, 1.0, 2.0, 3.0, -1.0, -2.0, -3.0], dtype=torch.float32).to(
+        torch.float8_e4m3fn).view(torch.uint8).numpy()
+    Wd = rng.choice(vals, size=(H, I))
+    A = rng.integers(-6, 7, size=(M, I)).astype(np.float64)
+    sd = np.array([0.5, 1.25, 2.0, 0.125, 4.0], dtype=np.float32)
+    D = [3, 4, 10, 15]
+    pi, K_s, _ = oracle.resolve_dense_set(I, dense_cols=D)
+    Y, B = oracle.down_ref(A, oracle.pack(Wd, DT_FP8, pi, K_s), sd)
+    mag = abs_order_key(Wd, DT_FP8).tolist()
+    wv = torch.from_numpy(Wd).view(torch.float8_e4m3fn).to(torch.float64).numpy().tolist()
+    for n in range(H):
+        row = list(wv[n])
+        for g in range(K_s // 4):
+            cols = [int(pi[4 * g + t]) for t in range(4)]
+            P = dominance_pair([mag[n][c] for c in cols])
+            for t in range(4):
+                if t not in P:
+                    row[cols[t]] = 0.0
+        for m in range(M):
+            acc = sum(A[m, k] * row[k] for k in range(I))
+            bnd = sum(abs(A[m, k] * row[k]) for k in range(I))
+            assert Y[m, n] == float(sd[n]) * acc
+            assert B[m, n] == float(sd[n]) * bnd
 
 
 # --------------------------------------------------------------------------
@@ -439,7 +566,7 @@ def test_rows_brute_force_every_dense_row_set_6x8():
         for D in itertools.combinations(range(N), nd):
             rho, N_s, _ = oracle.resolve_dense_rows(N, K, dense_rows=list(D))
             p = oracle.pack_rows(W, DT_F32, rho, N_s)
-            Y, _ = oracle.linear_rows_ref(X, DT_F32, p)
+            Y, B = oracle.linear_rows_ref(X, DT_F32, p)
             for n in range(N):
                 row = [float(v) for v in W[n]]
                 if n not in D:
@@ -449,10 +576,12 @@ def test_rows_brute_force_every_dense_row_set_6x8():
                             if t not in P:
                                 row[4 * g + t] = 0.0
                 for m in range(M):
-                    acc = 0.0
+                    acc = bnd = 0.0
                     for k in range(K):
                         acc += Xl[m][k] * row[k]
+                        bnd += abs(Xl[m][k] * row[k])
                     assert Y[m, n] == acc
+                    assert B[m, n] == bnd
             count += 1
     assert count == 2 ** N
 
@@ -745,8 +874,11 @@ def test_w8a8_tiny_brute_force_loops():
         qm = [_e4m3_nearest_by_scan(np.float32(Xv[m, k]) / sxm) for k in range(K)]
         assert qm == [int(c) for c in q[m]]
         for n in range(N):
-            acc = 0.0
+            acc = bnd = 0.0
             for k in range(K):
-                acc += float(oracle.decode_values(np.uint8(qm[k]), DT_FP8)) * float(
+                prod = float(oracle.decode_values(np.uint8(qm[k]), DT_FP8)) * float(
                     oracle.decode_values(Wbits[n, k], DT_FP8))
+                acc += prod
+                bnd += abs(prod)
             assert Y[m, n] == acc * (float(sxm) * float(np.float32(s[n])))
+            assert B[m, n] == bnd * (float(sxm) * float(np.float32(s[n])))
