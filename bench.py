@@ -62,7 +62,8 @@ FP8_PEAK_TFLOPS = 5000.0  # dense e4m3 matrix peak (W8A8)
 MALL_BYTES = 256 << 20
 CSRC = os.path.join(ROOT, "sparse_dense_gemm_amd", "csrc")
 # the kernels and the launch planner that picks them decide the HBM traffic
-KERNEL_SRCS = [os.path.join(CSRC, f) for f in ("spense_kernels.hip", "spense_internal.h", "spense_api.cpp")]
+KERNEL_SRCS = [os.path.join(CSRC, f) for f in ("spense_kernels.hip", "spense_tile.hip", "spense_device.h",
+                                              "spense_internal.h", "spense_api.cpp")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "spense_linear_gateup_fp8_traffic.json")
 METRIC = "Spense linear us + achieved HBM GB/s at decode M=1..64; speedup vs dense GEMM"
 
@@ -521,6 +522,7 @@ def run_glu(args, torch, sdg, synth, wl):
                 break
         nbytes = wbytes * rows / I * passes
         cpu = {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": oracle_threads(), "kind": "oracle",
+               **host_cpu(),
                "sample": f"block restricted to the first {rows} intermediate indices (last quarter dense), "
                          f"M={M0}, {passes} passes ({dt:.1f} s)"}
     out = {
@@ -538,6 +540,24 @@ def run_glu(args, torch, sdg, synth, wl):
         "cpu_baseline": cpu, "input_gen_s": round(gen_s, 2), "spensegpt_plus_scoring": scoring,
     }
     print(json.dumps(out))
+
+
+def host_cpu() -> dict:
+    """The host CPU the baseline ran on: model name and logical CPUs visible to this process."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        nproc = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        nproc = os.cpu_count() or 1
+    return {"cpu_model": model, "nproc": nproc}
 
 
 def oracle_threads() -> int:
@@ -578,7 +598,7 @@ def cpu_baseline(layers, Ms, single, a8=False):
             passes += 1
         dt = time.perf_counter() - t0
         return {"value": round(passes * len(Ms) * L.wbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(cores),
-                "kind": "oracle",
+                "kind": "oracle", **host_cpu(),
                 "sample": f"full layer, oracle linear_ref for M in {list(Ms)}, {passes} passes ({dt:.1f} s); pack excluded"}
     rows, M = 256, min(Ms)
     nbytes, dt = 0.0, 0.0
@@ -595,7 +615,7 @@ def cpu_baseline(layers, Ms, single, a8=False):
         dt += time.perf_counter() - t0
         nbytes += L.wbytes * rows / L.spec.N
     what = "quantize_tokens_ref + linear_w8a8_ref" if a8 else "linear_ref"
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": int(cores), "kind": "oracle", **host_cpu(),
             "sample": f"oracle {what} on the first {rows} output rows of each layer, M={M} ({dt:.1f} s); "
                       "pack excluded"}
 

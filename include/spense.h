@@ -33,10 +33,13 @@
  *     be in flight on a handle at a time (its split-K and gather workspaces
  *     are shared).
  *   - spense_linear, spense_linear_w8a8 and spense_glu may be captured in a HIP
- *     graph once an eager call on the same handle with at least the same batch
- *     size has sized the handle's workspaces (a call that grows them
- *     synchronises the stream and allocates).  The calls record kernel launches
- *     only; the split-K hand-off counters are reset by the kernels.
+ *     graph once an eager call on the same handle at a batch size of at least
+ *     the captured one has run (automatic split counts): a call that has to
+ *     grow the handle's workspaces synchronises the stream and allocates, and
+ *     sizes them for every batch size up to its own, whatever split count the
+ *     planner picks there.  spense_linear_splits with a forced split count
+ *     sizes them for that call only.  The calls record kernel launches only;
+ *     the split-K hand-off counters are reset by the kernels.
  */
 #ifndef SPENSE_H
 #define SPENSE_H
@@ -218,7 +221,9 @@ int spense_score_glu(const void* W_gu, const void* W_down, int32_t wdtype, int64
  *   dense_idx  host pointer, [k] int32 output, ascending; ready for spense_pack_glu.
  * Index i is selected iff fewer than k indices j have score[j] > score[i] or
  * score[j] == score[i] with j < i (ties go to the lower index).  0 <= k <= n.
- * Allocates scratch (hipMalloc) and synchronises `stream`.
+ * Infinite scores take their place in that order; a NaN score has none, and
+ * the call then returns SPENSE_EINVAL (dense_idx untouched).  Allocates
+ * scratch (hipMalloc) and synchronises `stream`.
  */
 int spense_select_dense(const float* score, int64_t n, int64_t k, int32_t* dense_idx, void* stream);
 

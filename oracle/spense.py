@@ -435,8 +435,14 @@ def glu_scores_ref(X_cal_bits, A_cal_bits, xdtype: int, Wg_bits, Wu_bits, Wd_bit
 
 
 def select_dense_ref(score: np.ndarray, k: int) -> np.ndarray:
-    """The k highest scores, ties to the lower index; returned ascending."""
-    order = np.argsort(-np.asarray(score, dtype=np.float64), kind="stable")
+    """The k highest scores, ties to the lower index; returned ascending.
+
+    Infinite scores take their place in the order; a NaN score has none and is
+    rejected (ValueError)."""
+    score = np.asarray(score, dtype=np.float64)
+    if np.any(np.isnan(score)):
+        raise ValueError("NaN score")
+    order = np.argsort(-score, kind="stable")
     return np.sort(order[:k])
 
 

@@ -14,7 +14,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libspense.so")
-SOURCES = [os.path.join(HERE, "csrc", f) for f in ("spense_kernels.hip", "spense_score.hip", "spense_api.cpp")]
+SOURCES = [os.path.join(HERE, "csrc", f) for f in ("spense_kernels.hip", "spense_tile.hip", "spense_score.hip",
+                                                   "spense_api.cpp")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 # -packed-fp32-ops: keep the compiler from forming v_pk_{add,mul,fma}_f32.
@@ -23,7 +24,7 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-
 # The linear kernels rely on fully unrolled epilogue loops over register-
 # blocked accumulator tiles (up to 64 16x16 tiles per wave); above the default
 # size limit of a forced unroll the tile array would live in scratch memory.
-EXTRA = {"spense_kernels.hip": ["-mllvm", "-pragma-unroll-threshold=200000"]}
+EXTRA = {f: ["-mllvm", "-pragma-unroll-threshold=200000"] for f in ("spense_kernels.hip", "spense_tile.hip")}
 
 
 def _run(cmd):

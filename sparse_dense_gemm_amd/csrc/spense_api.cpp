@@ -450,6 +450,18 @@ constexpr int64_t kLdsPerCU = 160 * 1024;  // LDS bytes per CU
 // shared variables
 constexpr int64_t kMaxDynLds = kLdsPerCU - 1024;
 
+// SPENSE_LDS=<configuration> runs linear_tile_kernel for batches above 16
+// rows; without it the register-blocked streaming kernels run (measured
+// faster on every layer and batch size of the workloads), and a forced
+// streaming-kernel preset (SPENSE_TILE) takes precedence
+static int lds_forced() {
+  const char* e = std::getenv("SPENSE_LDS");
+  const char* t = std::getenv("SPENSE_TILE");
+  if (t && *t) return -1;
+  return e && *e ? std::atoi(e) : -1;
+}
+static bool lds_enabled() { return lds_forced() >= 0; }
+
 // NT_fill: row tiles launched in the same grid (the layer's own, or both row
 // classes of an output-split layer); the split count and the blocking are
 // chosen from it so that both classes get the same kernel shape.
@@ -464,6 +476,7 @@ static int plan_linear(const spense_layer* h, int64_t M, int32_t splits, int64_t
   if (splits < 0 || splits > max_splits) return SPENSE_EINVAL;
   p = LinearPlan{};
   p.preset = -1;
+  p.lds_preset = -1;
   p.nr = 1;
   p.mt = 1;
   p.mgroups = 1;
@@ -513,6 +526,44 @@ static int plan_linear(const spense_layer* h, int64_t M, int32_t splits, int64_t
     p.splits = (int)S;
     p.lds_bytes = (int)(p.chunked ? stream_lds_bytes(M, kStreamChunk, xbytes) : decode_lds_bytes(d, M, S));
     return SPENSE_OK;
+  }
+  // More than 16 rows, one layer per launch, on request: weight units
+  // staged through LDS and shared by waves that split the tokens
+  // (linear_tile_kernel).
+  if (NT_fill == d.NT && lds_enabled() && lds_forced() < lds_preset_count()) {
+    const int pre = lds_forced();
+    const LdsPreset c = lds_preset(pre);
+    // the kernel addresses the workgroup's row tiles with 32-bit offsets, and
+    // its stage ring must fit one CU's LDS
+    if ((int64_t)c.rt * d.tile_bytes < (int64_t(1) << 31) && lds_tile_bytes(pre, d.wdtype) <= kMaxDynLds) {
+      p.chunked = 1;
+      p.lds_preset = pre;
+      p.waves = c.nw;
+      p.mt = c.mt;
+      p.nr = c.rt;
+      p.chunk = c.ch;
+      p.depth = 0;
+      p.mgroups = (int)((M + 16 * c.mt * c.nw - 1) / (16 * c.mt * c.nw));
+      p.rgroups = (int)((d.NT + c.rt - 1) / c.rt);
+      const int64_t lds = lds_tile_bytes(pre, d.wdtype);
+      p.lds_bytes = (int)lds;
+      int64_t S = splits;
+      if (S == 0) {
+        const int64_t units = (int64_t)p.rgroups * p.mgroups;
+        const int64_t per_cu = std::max<int64_t>(1, std::min<int64_t>(kLdsPerCU / lds, 8 / (c.nw + c.np)));
+        const int64_t resident = kCUs * per_cu;
+        S = units >= resident / 2 ? 1 : std::max<int64_t>(1, std::min<int64_t>(resident / units, max_splits));
+        S = std::max<int64_t>(1, std::min<int64_t>(S, d.tile_bytes / (256 * M)));
+      }
+      if (S > 1 && S * M * d.NT * 64 >= (int64_t(1) << 31)) {
+        if (splits != 0) return SPENSE_EUNSUPPORTED;
+        S = std::max<int64_t>(1, ((int64_t(1) << 31) - 1) / (M * d.NT * 64));
+      }
+      p.splits = (int)S;
+      const int64_t grid = (int64_t)p.rgroups * p.mgroups * S;
+      p.xcd_remap = (p.mgroups > 1 && grid % 8 == 0) ? 1 : 0;
+      return SPENSE_OK;
+    }
   }
   // More than 16 rows: the chunked streaming kernel with register-blocked
   // tiles (row tiles x m-tiles per wave; every weight unit feeds each m-tile,
@@ -601,73 +652,111 @@ static int plan_linear(const spense_layer* h, int64_t M, int32_t splits, int64_t
   return SPENSE_OK;
 }
 
-// Grows the handle's workspaces for this call (synchronising the stream
-// first: earlier launches may still read the old ones) and fills a.ws /
-// a.counters.  With gather, also writes X'p into the gather workspace and
-// points a at it.
-static int prepare_call(spense_layer* h, int64_t M, const LinearPlan& p, LinearArgs& a, bool gather_now,
-                        hipStream_t s) {
+// Workspace a call needs on one layer: activations in X'p order (gathered
+// bf16 [M][K_p], or W8A8 codes [M][K_p] then the token scales [M]), split-K
+// partials and the split-K hand-off counters.
+struct WsNeed {
+  size_t xws = 0, ws = 0, cnt = 0;
+  void grow(const WsNeed& o) {
+    xws = std::max(xws, o.xws);
+    ws = std::max(ws, o.ws);
+    cnt = std::max(cnt, o.cnt);
+  }
+  bool fits(const spense_layer* h) const { return xws <= h->xws_bytes && ws <= h->ws_bytes && cnt <= h->n_counters; }
+};
+
+static size_t a8_codes_bytes(int64_t M, int64_t K_p) { return ((size_t)M * (size_t)K_p + 255) / 256 * 256; }
+
+static WsNeed call_need(const LayerDesc& d, int64_t M, const LinearPlan& p, bool gather_now, bool a8) {
+  WsNeed n;
+  if (a8) n.xws = a8_codes_bytes(M, d.K_p) + (size_t)M * 4;
+  else if (gather_now) n.xws = (size_t)M * (size_t)d.K_p * 2;
+  if (p.splits > 1) {
+    n.ws = (size_t)p.splits * (size_t)M * (size_t)(d.NT * kRowTile) * 4;
+    n.cnt = (size_t)p.rgroups * (size_t)p.mgroups;
+  }
+  return n;
+}
+
+// Batch sizes up to which the workspace of every smaller batch is planned
+// exactly when a call grows it; beyond, the planner's own caps bound it.
+constexpr int64_t kExactPlanM = 4096;
+
+// Bound on the split-K workspace of any batch size above kExactPlanM: the
+// planner keeps S * M below tile_bytes / 256 there, and only splits a launch
+// of fewer than kCUs / 2 workgroups (so fewer counters).
+static WsNeed large_batch_bound(const LayerDesc& d) {
+  WsNeed n;
+  n.ws = (size_t)std::min<int64_t>(d.NT * d.tile_bytes / 4, (int64_t(1) << 31) - 1);
+  n.cnt = (size_t)std::max<int64_t>(128, d.NT);
+  return n;
+}
+
+// Replaces h's workspaces with ones of at least `need` (synchronising the
+// stream first: earlier launches may still use the old ones).  New counters
+// are cleared by a fill kernel on the stream.
+static int grow_workspaces(spense_layer* h, const WsNeed& need, hipStream_t s) {
+  if (need.fits(h)) return SPENSE_OK;
+  hipError_t e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e);
+  auto regrow = [&](void** ptr, size_t& have, size_t want) -> int {
+    if (want <= have) return SPENSE_OK;
+    if (*ptr) (void)hipFree(*ptr);
+    *ptr = nullptr;
+    have = 0;
+    const hipError_t err = hipMalloc(ptr, want);
+    if (err != hipSuccess) return err == hipErrorOutOfMemory ? (g_last_hip = (int)err, SPENSE_ENOMEM) : hip_fail(err);
+    have = want;
+    return SPENSE_OK;
+  };
+  int rc = regrow(&h->xws, h->xws_bytes, need.xws);
+  if (rc == SPENSE_OK) rc = regrow((void**)&h->ws, h->ws_bytes, need.ws);
+  if (rc == SPENSE_OK && need.cnt > h->n_counters) {
+    size_t bytes = h->n_counters * 4;
+    rc = regrow((void**)&h->counters, bytes, need.cnt * 4);
+    h->n_counters = bytes / 4;
+    if (rc == SPENSE_OK) {
+      e = launch_zero_i32(h->counters, (int64_t)need.cnt, s);
+      if (e != hipSuccess) rc = hip_fail(e);
+    }
+  }
+  return rc;
+}
+
+// Workspaces of one call on one layer.
+struct WsPtrs {
+  void* xws = nullptr;
+  float* ws = nullptr;
+  int32_t* counters = nullptr;
+};
+
+static WsPtrs handle_ws(const spense_layer* h) { return WsPtrs{h->xws, h->ws, h->counters}; }
+
+// Points a at this call's workspaces; with gather_now, also writes X'p into
+// the gather workspace and points a at it.  The workspaces must fit already.
+static int bind_call(const spense_layer* h, int64_t M, const LinearPlan& p, LinearArgs& a, bool gather_now,
+                     const WsPtrs& w, hipStream_t s) {
   const LayerDesc& d = h->d;
   if (gather_now) {
-    const size_t need = (size_t)M * (size_t)d.K_p * 2;
-    if (need > h->xws_bytes) {
-      hipError_t e = hipStreamSynchronize(s);
-      if (e != hipSuccess) return hip_fail(e);
-      if (h->xws) (void)hipFree(h->xws);
-      h->xws = nullptr;
-      h->xws_bytes = 0;
-      e = hipMalloc(&h->xws, need);
-      if (e != hipSuccess) return e == hipErrorOutOfMemory ? SPENSE_ENOMEM : hip_fail(e);
-      h->xws_bytes = need;
-    }
-    hipError_t e = launch_gather_x(d, a.X, M, a.ldx, h->xws, s);
+    hipError_t e = launch_gather_x(d, a.X, M, a.ldx, w.xws, s);
     if (e != hipSuccess) return hip_fail(e);
-    a.X = h->xws;
+    a.X = w.xws;
     a.ldx = d.K_p;
     a.gather = 0;
   }
   if (p.splits > 1) {
-    const size_t need = (size_t)p.splits * (size_t)M * (size_t)(d.NT * kRowTile) * 4;
-    const size_t need_cnt = (size_t)p.rgroups * (size_t)p.mgroups;
-    if (need > h->ws_bytes || need_cnt > h->n_counters) {
-      hipError_t e = hipStreamSynchronize(s);
-      if (e != hipSuccess) return hip_fail(e);
-      if (need > h->ws_bytes) {
-        if (h->ws) (void)hipFree(h->ws);
-        h->ws = nullptr;
-        h->ws_bytes = 0;
-        e = hipMalloc((void**)&h->ws, need);
-        if (e != hipSuccess) return e == hipErrorOutOfMemory ? SPENSE_ENOMEM : hip_fail(e);
-        h->ws_bytes = need;
-      }
-      if (need_cnt > h->n_counters) {
-        if (h->counters) (void)hipFree(h->counters);
-        h->counters = nullptr;
-        h->n_counters = 0;
-        e = hipMalloc((void**)&h->counters, need_cnt * 4);
-        if (e != hipSuccess) return e == hipErrorOutOfMemory ? SPENSE_ENOMEM : hip_fail(e);
-        e = launch_zero_i32(h->counters, (int64_t)need_cnt, s);
-        if (e != hipSuccess) return hip_fail(e);
-        h->n_counters = need_cnt;
-      }
-    }
-    a.ws = h->ws;
-    a.counters = h->counters;
+    a.ws = w.ws;
+    a.counters = w.counters;
   }
   return SPENSE_OK;
 }
 
-// Plans and launches one layer, or the two row classes of an output-split
-// layer in one grid.  `base` carries X, M, Y and the output type.
-static int run_layers(spense_layer* const* parts, int n_parts, int64_t M, int32_t splits, const LinearArgs& base,
-                      hipStream_t s) {
-  const bool x_aligned = aligned16(base.X) && (base.ldx % 8) == 0;
+// Plans one call on `parts` (one layer, or the two row classes of an
+// output-split layer, which share one grid and so one kernel shape).
+static int plan_call(spense_layer* const* parts, int n_parts, int64_t M, int32_t splits, LinearPlan p[2]) {
   int64_t NT_fill = 0;
   for (int i = 0; i < n_parts; ++i) NT_fill += parts[i]->d.NT;
-  LinearPlan p[2]{};
-  LinearArgs aa[2]{base, base};
   for (int i = 0; i < n_parts; ++i) {
-    aa[i].gather = parts[i]->d.gather || !x_aligned;
     const int rc = plan_linear(parts[i], M, splits, NT_fill, p[i]);
     if (rc != SPENSE_OK) return rc;
   }
@@ -699,13 +788,60 @@ static int run_layers(spense_layer* const* parts, int n_parts, int64_t M, int32_
         if (rc != SPENSE_OK) return rc;
       }
   }
-  for (int i = 0; i < n_parts; ++i) aa[i].splits = p[i].splits;
-  // The row classes of an output-split layer see the same activations in the
-  // same column order (identity, padded to whole 128-column steps), so one
-  // gathered copy serves both.
+  return SPENSE_OK;
+}
+
+// Workspaces of every call with automatic splits at a batch size up to M
+// (any activation alignment: a chunked launch is assumed to gather), so that
+// after one call at M no call at a smaller batch size allocates, which keeps
+// such calls capturable in a HIP graph.
+static int max_need_parts(spense_layer* const* parts, int n_parts, int64_t M, WsNeed need[2]) {
+  LinearPlan p[2]{};
+  for (int64_t m = 1; m <= std::min(M, kExactPlanM); ++m) {
+    const int rc = plan_call(parts, n_parts, m, 0, p);
+    if (rc != SPENSE_OK) return rc;
+    for (int i = 0; i < n_parts; ++i) need[i].grow(call_need(parts[i]->d, m, p[i], p[i].chunked && i == 0, false));
+  }
+  if (M > kExactPlanM) {
+    for (int i = 0; i < n_parts; ++i) {
+      need[i].grow(large_batch_bound(parts[i]->d));
+      if (i == 0) need[i].xws = std::max(need[i].xws, (size_t)M * (size_t)parts[i]->d.K_p * 2);
+    }
+  }
+  return SPENSE_OK;
+}
+
+// Plans and launches one layer, or the two row classes of an output-split
+// layer in one grid.  `base` carries X, M, Y and the output type.
+static int run_layers(spense_layer* const* parts, int n_parts, int64_t M, int32_t splits, const LinearArgs& base,
+                      hipStream_t s) {
+  const bool x_aligned = aligned16(base.X) && (base.ldx % 8) == 0;
+  LinearPlan p[2]{};
+  LinearArgs aa[2]{base, base};
+  int rc = plan_call(parts, n_parts, M, splits, p);
+  if (rc != SPENSE_OK) return rc;
+  bool gather_now[2] = {false, false};
+  WsNeed need[2];
+  bool grow = false;
   for (int i = 0; i < n_parts; ++i) {
-    const bool gather_now = p[i].chunked && aa[i].gather && i == 0;
-    const int rc = prepare_call(parts[i], M, p[i], aa[i], gather_now, s);
+    aa[i].gather = parts[i]->d.gather || !x_aligned;
+    aa[i].splits = p[i].splits;
+    // The row classes of an output-split layer see the same activations in
+    // the same column order (identity, padded to whole 128-column steps), so
+    // one gathered copy serves both.
+    gather_now[i] = p[i].chunked && aa[i].gather && i == 0;
+    need[i] = call_need(parts[i]->d, M, p[i], gather_now[i], false);
+    grow = grow || !need[i].fits(parts[i]);
+  }
+  WsPtrs w[2];
+  if (grow) {
+    if (splits == 0 && (rc = max_need_parts(parts, n_parts, M, need)) != SPENSE_OK) return rc;
+    for (int i = 0; i < n_parts; ++i)
+      if ((rc = grow_workspaces(parts[i], need[i], s)) != SPENSE_OK) return rc;
+  }
+  for (int i = 0; i < n_parts; ++i) w[i] = handle_ws(parts[i]);
+  for (int i = 0; i < n_parts; ++i) {
+    rc = bind_call(parts[i], M, p[i], aa[i], gather_now[i], w[i], s);
     if (rc != SPENSE_OK) return rc;
     if (i == 1 && p[1].chunked && aa[1].gather) {
       aa[1].X = aa[0].X;
@@ -785,21 +921,21 @@ int spense_linear_w8a8(spense_handle h, const void* X, int64_t M, int64_t ldx, v
   LinearPlan p{};
   int rc = plan_linear(h, M, splits, d.NT, p, true, 1);
   if (rc != SPENSE_OK) return rc;
-  // workspace: the codes [M][K_p] in X'p order, then the token scales [M]
-  const size_t codes = ((size_t)M * (size_t)d.K_p + 255) / 256 * 256;
-  const size_t need = codes + (size_t)M * 4;
-  if (need > h->xws_bytes) {
-    hipError_t e = hipStreamSynchronize(s);
-    if (e != hipSuccess) return hip_fail(e);
-    if (h->xws) (void)hipFree(h->xws);
-    h->xws = nullptr;
-    h->xws_bytes = 0;
-    e = hipMalloc(&h->xws, need);
-    if (e != hipSuccess) return e == hipErrorOutOfMemory ? SPENSE_ENOMEM : hip_fail(e);
-    h->xws_bytes = need;
+  WsNeed need = call_need(d, M, p, false, true);
+  if (!need.fits(h)) {
+    if (splits == 0) {  // every smaller batch size too (graph capture after one eager call)
+      LinearPlan q{};
+      for (int64_t m = 1; m <= std::min(M, kExactPlanM); ++m) {
+        if ((rc = plan_linear(h, m, 0, d.NT, q, true, 1)) != SPENSE_OK) return rc;
+        need.grow(call_need(d, m, q, false, true));
+      }
+      if (M > kExactPlanM) need.grow(large_batch_bound(d));
+    }
+    if ((rc = grow_workspaces(h, need, s)) != SPENSE_OK) return rc;
   }
+  // workspace: the codes [M][K_p] in X'p order, then the token scales [M]
   uint8_t* q = (uint8_t*)h->xws;
-  float* sx = (float*)(q + codes);
+  float* sx = (float*)(q + a8_codes_bytes(M, d.K_p));
   // quantise and re-order the columns into X'p in one pass
   hipError_t e = launch_quantize_tokens(X, M, d.K, ldx, d.pip, d.K_p, q, d.K_p, sx, s);
   if (e != hipSuccess) return hip_fail(e);
@@ -814,7 +950,7 @@ int spense_linear_w8a8(spense_handle h, const void* X, int64_t M, int64_t ldx, v
   a.splits = p.splits;
   a.a8 = 1;
   a.xscale = sx;
-  rc = prepare_call(h, M, p, a, false, s);
+  rc = bind_call(h, M, p, a, false, handle_ws(h), s);
   if (rc != SPENSE_OK) return rc;
   e = launch_linear(d, a, p, s);
   return e == hipSuccess ? SPENSE_OK : hip_fail(e);
@@ -910,13 +1046,13 @@ int spense_select_dense(const float* score, int64_t n, int64_t k, int32_t* dense
   (void)hipFree(sel);
   if (e == hipSuccess) e = e2;
   if (e != hipSuccess) return hip_fail(e);
-  int64_t m = 0;
   for (int64_t i = 0; i < n; ++i)
-    if (h_sel[(size_t)i]) {
-      if (m == k) return hip_fail(hipErrorUnknown);  // cannot happen: exactly k ranks are below k
-      dense_idx[m++] = (int32_t)i;
-    }
-  return m == k ? SPENSE_OK : hip_fail(hipErrorUnknown);
+    if (h_sel[(size_t)i] == 2) return SPENSE_EINVAL;  // a NaN score
+  // the ranks of n numbers are a permutation of 0..n-1, so exactly k are below k
+  int64_t m = 0;
+  for (int64_t i = 0; i < n && m < k; ++i)
+    if (h_sel[(size_t)i]) dense_idx[m++] = (int32_t)i;
+  return SPENSE_OK;
 }
 
 int spense_info(spense_handle h, spense_layer_info* info) {

@@ -99,7 +99,22 @@ struct LinearPlan {
   int nr;        // row tiles per wave (linear_stream_kernel)
   int preset;    // index into SPENSE_TILE_PRESETS, or -1 (one row tile and m-tile per wave)
   int xcd_remap; // 1: logical workgroup id = XCD-major remap of blockIdx (grid a multiple of 8)
+  int lds_preset = -1; // >= 0: linear_tile_kernel configuration (spense_tile.hip); waves, mt, nr (row
+                  // tiles per workgroup) and chunk (unit-steps per LDS stage) then describe it
 };
+
+// Configurations of linear_tile_kernel (weight units staged through LDS,
+// consumer waves splitting the tokens): consumer waves, m-tiles per consumer,
+// row tiles per workgroup, unit-steps per stage, stages in the LDS ring,
+// producer waves.
+struct LdsPreset {
+  int nw, mt, rt, ch, ns, np;
+};
+int lds_preset_count();
+LdsPreset lds_preset(int i);
+// LDS of configuration i (its stages of units and index blocks)
+int64_t lds_tile_bytes(int i, int32_t wdtype);
+hipError_t launch_linear_tile(const LayerDesc& d, const LinearArgs& a, const LinearPlan& p, hipStream_t s);
 
 // Blocked configurations of linear_stream_kernel for batches above 16 rows:
 // X(index, waves per workgroup, row tiles per wave, ring depth, chunk units, m-tiles).
@@ -136,6 +151,7 @@ hipError_t launch_linear(const LayerDesc& d, const LinearArgs& a, const LinearPl
 hipError_t launch_linear2(const LayerDesc& d0, const LinearArgs& a0, const LinearPlan& p0, const LayerDesc& d1,
                           const LinearArgs& a1, const LinearPlan& p1, hipStream_t s);
 hipError_t launch_zero_i32(int32_t* p, int64_t n, hipStream_t s);
+
 // SpenseGPT+ scoring (spense_score.hip): diag(X^T X) of a bf16 [T, C] matrix via
 // fixed-order chunk partials [C][ceil(T / rows_per_chunk)]; GLU index scores;
 // exact top-k selection (ties to the lower index) as a 0/1 mask

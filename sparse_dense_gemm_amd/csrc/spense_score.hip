@@ -148,10 +148,13 @@ __global__ __launch_bounds__(kRankTile) void rank_partial_kernel(const float* __
   if (i < n && cnt) atomicAdd(rank + i, cnt);
 }
 
-// sel[i] = 1 iff rank[i] < k: the k highest scores with ties to the lower index
-__global__ void rank_final_kernel(const int* __restrict__ rank, int n, int64_t k, uint8_t* __restrict__ sel) {
+// sel[i] = 1 iff rank[i] < k: the k highest scores with ties to the lower
+// index; 2 marks a NaN score (NaN has no place in the order, so the host
+// rejects the call)
+__global__ void rank_final_kernel(const float* __restrict__ score, const int* __restrict__ rank, int n, int64_t k,
+                                  uint8_t* __restrict__ sel) {
   const int i = (int)(blockIdx.x * blockDim.x + threadIdx.x);
-  if (i < n) sel[i] = rank[i] < k ? 1 : 0;
+  if (i < n) sel[i] = score[i] != score[i] ? 2 : (rank[i] < k ? 1 : 0);
 }
 
 __global__ void fill_zero_kernel(int* __restrict__ p, int n) {
@@ -199,7 +202,7 @@ hipError_t launch_rank_select(const float* score, int64_t n, int64_t k, int* ran
   const int nn = (int)n;
   fill_zero_kernel<<<blocks(n, 256), 256, 0, s>>>(rank, nn);
   rank_partial_kernel<<<dim3(blocks(n, kRankTile), blocks(n, kRankRange)), kRankTile, 0, s>>>(score, nn, rank);
-  rank_final_kernel<<<blocks(n, 256), 256, 0, s>>>(rank, nn, k, sel);
+  rank_final_kernel<<<blocks(n, 256), 256, 0, s>>>(score, rank, nn, k, sel);
   return hipGetLastError();
 }
 

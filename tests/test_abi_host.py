@@ -39,7 +39,7 @@ def test_abi_version_and_strerror():
     assert sdg.spense_abi_version() == 5
     lib = sdg._lib()
     for code in (0, -1, -2, -3, -4):
-        assert lib.spense_strerror(code)
+        assert lib.spense_strerror(code) and lib.spense_strerror(code) != b"unknown status"
     assert lib.spense_strerror(12345) == b"unknown status"
 
 

@@ -27,7 +27,7 @@ def test_published_mi355x_peaks():
 
 def test_kernel_hash_covers_the_kernel_sources():
     names = sorted(os.path.basename(p) for p in bench.KERNEL_SRCS)
-    assert names == ["spense_api.cpp", "spense_internal.h", "spense_kernels.hip"]
+    assert names == ["spense_api.cpp", "spense_device.h", "spense_internal.h", "spense_kernels.hip", "spense_tile.hip"]
     h = bench.kernel_hash()
     assert len(h) == 16 and int(h, 16) >= 0
     assert bench.kernel_hash() == h

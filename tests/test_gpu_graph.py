@@ -117,3 +117,46 @@ def test_graph_replays_of_the_glu_block_equal_eager(M):
         log(f"[graph] GLU block M={M}: 3 replays equal eager")
     finally:
         sdg.spense_free(h)
+
+
+@pytest.mark.parametrize("form,a8", [("chosen", False), ("rows", False), ("tail", True)])
+def test_capture_at_a_smaller_batch_after_one_larger_call(form, a8):
+    """One eager call at M = 128 sizes the workspaces for every smaller batch
+    size, so a capture at M = 1 (a split-K decode launch, which the M = 128
+    call does not use) allocates nothing; its replays equal eager calls."""
+    h = _layer(form)
+    try:
+        Xbig = to_dev(synth.make_x(128, K, DT_BF16, np.random.default_rng(55)), DT_BF16)
+        Ybig = torch.empty((128, N), dtype=torch.float32, device="cuda")
+
+        def call(X, out, stream=None):
+            if a8:
+                sdg.spense_linear_w8a8(h, X, out, stream=stream)
+            else:
+                sdg.spense_linear(h, X, out, stream=stream)
+
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            call(Xbig, Ybig)  # the only call before the capture
+        torch.cuda.synchronize()
+        X1 = Xbig[:1]
+        Y1 = torch.empty((1, N), dtype=torch.float32, device="cuda")
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            call(X1, Y1)
+        torch.cuda.synchronize()
+        Y_eager = torch.empty_like(Y1)
+        call(X1, Y_eager)
+        torch.cuda.synchronize()
+        for rep in range(3):
+            Y1.fill_(float("nan"))
+            torch.cuda.synchronize()
+            g.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(Y1, Y_eager), (form, a8, rep)
+            call(Xbig, Ybig)  # eager work at the larger batch between replays
+            torch.cuda.synchronize()
+        log(f"[graph] {form} a8={a8}: capture at M=1 after one call at M=128, 3 replays equal eager")
+    finally:
+        sdg.spense_free(h)

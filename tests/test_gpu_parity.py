@@ -1,14 +1,11 @@
-"""Parity of the HIP library (called through its C interface) with the oracle.
+"""Parity of the HIP library (called through its C interface) with the oracle
+on small and edge shapes, every kernel variant and launch configuration.
 
 * spense_pack: canonical export equals the oracle's packed form bit for bit.
 * spense_linear: every element within 1e-3 * sum_k |x_k w_k| of the oracle's
   float64 result, compared on the fp32 output before any cast.
-Full workloads run at their real shapes; the oracle checks all rows for the
-single-layer workloads and a spread sample of row tiles (and of activation
-rows at M >= 256) for the large layer sets.
+The benchmark's workloads at their full sizes are in test_gpu_full_size.py.
 """
-
-import functools
 
 import numpy as np
 import pytest
@@ -23,71 +20,6 @@ from spense_gpu_util import (assert_pack_equal, export, linear_dev, log, oracle_
                              tol_ratio)
 
 pytestmark = pytest.mark.gpu
-
-WL = synth.WORKLOADS
-
-
-def _cases():
-    cases = []
-    for key, w in WL.items():
-        for spec in w.layers:
-            cases.append((spec.layer_index, spec.wdtype, key, spec.name))
-    # group equal layers (same seeds, same W) next to each other so inputs are reused
-    cases.sort(key=lambda c: (c[2].startswith("layer32b"), c[0], c[1], c[2]))
-    return [(c[2], c[3]) for c in cases]
-
-
-@functools.lru_cache(maxsize=1)
-def _weights(N, K, wdtype, layer_index, single):
-    spec = synth.LayerSpec("w", N, K, 0, wdtype, DT_F32 if wdtype == DT_F32 else DT_BF16, "tail", layer_index)
-    W, s, _, _ = synth.layer_inputs(spec, 1, single_stream=single)
-    return W, s
-
-
-def _sample_rows(N, big):
-    if not big:
-        return None
-    NT = (N + 15) // 16
-    tiles = np.unique(np.concatenate([np.linspace(0, NT - 1, 24).astype(np.int64), [0, NT - 1]]))
-    rows = np.concatenate([np.arange(16 * t, min(N, 16 * t + 16)) for t in tiles])
-    return rows
-
-
-@pytest.mark.parametrize("key,lname", _cases())
-def test_workload_parity(key, lname):
-    w = WL[key]
-    spec = next(s for s in w.layers if s.name == lname)
-    Mmax = max(w.Ms)
-    log(f"[parity] {key}/{lname} N={spec.N} K={spec.K} K_d={spec.K_d} wdtype={spec.wdtype} Ms={w.Ms}")
-    W, s = _weights(spec.N, spec.K, spec.wdtype, spec.layer_index, w.single_stream)
-    _, _, X, D = synth.layer_inputs(synth.LayerSpec(spec.name, 1, spec.K, spec.K_d, spec.wdtype, spec.xdtype,
-                                                    spec.dense, spec.layer_index), Mmax, single_stream=False)
-    if w.single_stream:
-        _, _, X, D = synth.layer_inputs(spec, Mmax, single_stream=True)
-    big = spec.N * spec.K > 40_000_000
-    rows = _sample_rows(spec.N, big)
-    Wd = to_dev(W, spec.wdtype)
-    sd = to_dev(s, DT_F32) if s is not None else None
-    h = pack_dev(Wd, spec.wdtype, sd, dense_cols=D)
-    try:
-        ref = oracle_pack_rows(W, spec.wdtype, D, rows)
-        got = export(h, spec.wdtype, rows)
-        assert_pack_equal(got, ref)
-        log(f"  pack bit-exact ({'all' if rows is None else len(rows)} rows)")
-        Xd = to_dev(X, spec.xdtype)
-        s_rows = None if s is None else (s if rows is None else s[rows])
-        for M in w.Ms:
-            Y = linear_dev(h, Xd[:M], spec.N).cpu().numpy()
-            mrows = np.arange(M) if M <= 128 else np.unique(np.concatenate(
-                [np.random.default_rng(M).choice(M, 62, replace=False), [0, M - 1]]))
-            Yref, B = oracle.linear_ref(X[mrows], spec.xdtype, ref, s_rows)
-            Yg = Y[mrows] if rows is None else Y[mrows][:, rows]
-            r = tol_ratio(Yg, Yref, B)
-            log(f"  M={M}: max err / (1e-3 * sum|xw|) = {r:.3e}")
-            assert r <= 1.0
-    finally:
-        sdg.spense_free(h)
-
 
 # ---------------------------------------------------------------------------
 # edge cases on small shapes
@@ -347,5 +279,71 @@ def test_tile_presets(wdtype, dense, monkeypatch):
                     r = tol_ratio(Y, Yref, B)
                     assert r <= 1.0, (v, M, sp, r)
         log(f"[tile presets] wdtype={wdtype} dense={dense}: all presets within tolerance")
+    finally:
+        sdg.spense_free(h)
+
+
+LDS_PRESETS = list(range(7))
+
+
+@pytest.mark.parametrize("wdtype", [DT_FP8, DT_BF16])
+@pytest.mark.parametrize("dense", [("frac", 0.25), ("rand", 192)])
+def test_lds_tile_presets(wdtype, dense, monkeypatch):
+    """Every configuration of the kernel that stages weight units through LDS
+    for waves splitting the tokens (waves per workgroup, m-tiles per wave, row
+    tiles per workgroup, unit-steps per stage), on ragged row counts, batches
+    ending mid m-tile, one or several m-groups, several split counts and a
+    chosen dense set, agrees with the oracle."""
+    N, K = 232, 1536  # 14.5 row tiles: the last row group is partial for every configuration
+    W, s = _small(N, K, wdtype, 34)
+    X = synth.make_x(300, K, DT_BF16, np.random.default_rng(35))
+    sd = to_dev(s, DT_F32) if s is not None else None
+    if dense[0] == "frac":
+        h = pack_dev(to_dev(W, wdtype), wdtype, sd, dense_fraction=dense[1])
+        pi, K_s, _ = oracle.resolve_dense_set(K, dense_fraction=dense[1])
+        D = np.sort(pi[K_s:])
+    else:
+        D = synth.random_dense_set(K, dense[1], 36)
+        h = pack_dev(to_dev(W, wdtype), wdtype, sd, dense_cols=D)
+    try:
+        ref = oracle_pack_rows(W, wdtype, D)
+        Xd = to_dev(X, DT_BF16)
+        worst = 0.0
+        for v in LDS_PRESETS:
+            monkeypatch.setenv("SPENSE_LDS", str(v))
+            for M in (17, 40, 64, 130, 300):
+                Yref, B = oracle.linear_ref(X[:M], DT_BF16, ref, s)
+                for sp in (0, 1, 3):
+                    Y = linear_dev(h, Xd[:M], N, splits=sp).cpu().numpy()
+                    r = tol_ratio(Y, Yref, B)
+                    assert r <= 1.0, (v, M, sp, r)
+                    worst = max(worst, r)
+        log(f"[lds presets] wdtype={wdtype} dense={dense}: all configurations within tolerance (worst {worst:.2e})")
+    finally:
+        sdg.spense_free(h)
+
+
+def test_lds_tile_equals_streaming_bitwise_on_one_split():
+    """With one split both M > 16 kernels add the same products per output in
+    the same unit order (sparse units, then dense units, two instructions per
+    unit, fp32 accumulators), so on the same packed layer they agree bit for bit."""
+    N, K, M = 160, 1024, 64
+    W, s = _small(N, K, DT_FP8, 37)
+    sd = to_dev(s, DT_F32)
+    h = pack_dev(to_dev(W, DT_FP8), DT_FP8, sd, dense_fraction=0.25)
+    try:
+        Xd = to_dev(synth.make_x(M, K, DT_BF16, np.random.default_rng(38)), DT_BF16)
+        import os
+        os.environ["SPENSE_LDS"] = "1"
+        try:
+            y_lds = linear_dev(h, Xd, N, splits=1)
+        finally:
+            del os.environ["SPENSE_LDS"]
+        os.environ["SPENSE_TILE"] = "3"  # eight waves, one row tile and four m-tiles each
+        try:
+            y_str = linear_dev(h, Xd, N, splits=1)
+        finally:
+            del os.environ["SPENSE_TILE"]
+        assert torch.equal(y_lds, y_str)
     finally:
         sdg.spense_free(h)

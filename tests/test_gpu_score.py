@@ -71,6 +71,21 @@ def test_selection_ties_go_to_lower_index():
             assert np.array_equal(sdg.spense_select_dense(d, k), oracle.select_dense_ref(sc.astype(np.float64), k))
 
 
+def test_selection_with_infinities_and_nan():
+    """Infinite scores take their place in the order; a NaN score is rejected
+    with SPENSE_EINVAL, like the oracle rejects it."""
+    sc = np.array([1.0, np.inf, -np.inf, 2.0, np.inf, 0.0, -np.inf, 3.0], dtype=np.float32)
+    d = torch.from_numpy(sc).cuda()
+    for k in range(len(sc) + 1):
+        assert np.array_equal(sdg.spense_select_dense(d, k), oracle.select_dense_ref(sc.astype(np.float64), k)), k
+    sc[5] = np.nan
+    with pytest.raises(ValueError):
+        oracle.select_dense_ref(sc.astype(np.float64), 3)
+    with pytest.raises(sdg.SpenseError) as e:
+        sdg.spense_select_dense(torch.from_numpy(sc).cuda(), 3)
+    assert e.value.status == sdg.SPENSE_EINVAL
+
+
 def test_scores_are_repeatable():
     H, I, T, wdt = 128, 256, 130, DT_FP8
     args = _block(H, I, T, wdt, 93)

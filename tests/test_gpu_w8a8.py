@@ -138,6 +138,30 @@ def test_w8a8_tile_presets(dense, monkeypatch):
         sdg.spense_free(h)
 
 
+@pytest.mark.parametrize("dense", [("frac", 0.25), ("rand", 192)])
+def test_w8a8_lds_tile_presets(dense, monkeypatch):
+    """Every configuration of the LDS-staged kernel on e4m3 activation codes:
+    ragged row counts, batches ending mid m-tile, several m-groups and split counts."""
+    N, K = 232, 1536
+    W, s, D, h = _pack_case(N, K, dense, 532)
+    try:
+        ref = oracle_pack_rows(W, DT_FP8, D)
+        X = synth.make_x(300, K, DT_BF16, np.random.default_rng(533))
+        Xd = to_dev(X, DT_BF16)
+        for M in (17, 40, 64, 130, 300):
+            q, sx = oracle.quantize_tokens_ref(X[:M], DT_BF16)
+            Yref, B = oracle.linear_w8a8_ref(q, sx, ref, s)
+            for v in range(7):
+                monkeypatch.setenv("SPENSE_LDS", str(v))
+                for sp in (0, 1, 3):
+                    Y = _w8a8_dev(h, Xd[:M], N, splits=sp).cpu().numpy()
+                    r = tol_ratio(Y, Yref, B)
+                    assert r <= 1.0, (v, M, sp, r)
+        log(f"[w8a8 lds presets] dense={dense}: all configurations within tolerance")
+    finally:
+        sdg.spense_free(h)
+
+
 def test_w8a8_bf16_output_repeatable_and_rne():
     N, K, M = 160, 1024, 48
     W, s, D, h = _pack_case(N, K, ("rand", 256), 540)

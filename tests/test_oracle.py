@@ -752,6 +752,11 @@ def test_select_dense_rank_definition():
         want = sorted(i for i in range(n) if rank[i] < k)
         assert oracle.select_dense_ref(sc, k).tolist() == want
     assert oracle.select_dense_ref(np.array([1.0, 3.0, 3.0, 2.0, 3.0]), 2).tolist() == [1, 2]
+    # infinities take their place in the order; NaN has none and is rejected
+    assert oracle.select_dense_ref(np.array([1.0, np.inf, -np.inf, np.inf, 0.0]), 3).tolist() == [0, 1, 3]
+    assert oracle.select_dense_ref(np.array([-np.inf, -np.inf, 0.0]), 2).tolist() == [0, 2]
+    with pytest.raises(ValueError):
+        oracle.select_dense_ref(np.array([1.0, np.nan, 0.0]), 1)
 
 
 # --------------------------------------------------------------------------
