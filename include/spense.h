@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define SPENSE_ABI_VERSION 5
+#define SPENSE_ABI_VERSION 6
 
 /* Element types.  The numbering is fixed. */
 typedef enum spense_dtype {
@@ -64,7 +64,8 @@ typedef enum spense_status {
   SPENSE_EINVAL = -1,       /* bad argument (null pointer, size, dense set, ...) */
   SPENSE_EUNSUPPORTED = -2, /* valid but unsupported combination of types */
   SPENSE_ENOMEM = -3,       /* device or host allocation failed */
-  SPENSE_EHIP = -4          /* a HIP runtime call failed */
+  SPENSE_EHIP = -4,         /* a HIP runtime call failed */
+  SPENSE_ESCRATCH = -5      /* spense_linear_noalloc: the call needs more than its fixed scratch */
 } spense_status;
 
 typedef struct spense_layer* spense_handle;
@@ -261,6 +262,30 @@ int spense_linear(spense_handle h, const void* X, int32_t xdtype, int64_t M, int
  */
 int spense_linear_splits(spense_handle h, const void* X, int32_t xdtype, int64_t M, int64_t ldx, void* Y,
                          int32_t ydtype, int64_t ldy, int32_t splits, void* stream);
+
+/*
+ * spense_linear_noalloc - spense_linear that allocates nothing.
+ *
+ * For callers that cannot allocate device memory during the call: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same arguments, result and kernels as spense_linear (automatic split
+ * count), bitwise equal to it; only the call's workspaces differ: the split-K
+ * counters and partials and the gathered activations live in a fixed device
+ * array of 32 MiB that the library holds on every GPU it runs on until the
+ * process ends (64 KiB of it for counters), instead of the handle's own
+ * workspaces.  Its first call on a device looks the array up and clears its
+ * counters (a fill kernel on `stream`); every completed call leaves them
+ * cleared.  No hipMalloc, hipFree or other allocating routine is called.
+ *
+ * A call whose workspaces exceed the array returns SPENSE_ESCRATCH before any
+ * launch (for example a chosen dense set gathered for a large batch: M * K_p
+ * * 2 bytes, K_p = K rounded up per region to 128 columns).  Every call on
+ * one GPU shares that GPU's array, so two such calls that overlap in time on
+ * one GPU (different streams, or different host threads) race and must be
+ * ordered by the caller; calls on one stream are ordered by the stream.
+ */
+int spense_linear_noalloc(spense_handle h, const void* X, int32_t xdtype, int64_t M, int64_t ldx, void* Y,
+                          int32_t ydtype, int64_t ldy, void* stream);
 
 /*
  * spense_quantize_tokens - per-token e4m3 quantisation of bf16 activations.

@@ -25,6 +25,7 @@ SPENSE_EINVAL = -1
 SPENSE_EUNSUPPORTED = -2
 SPENSE_ENOMEM = -3
 SPENSE_EHIP = -4
+SPENSE_ESCRATCH = -5
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libspense.so")
 
@@ -75,6 +76,8 @@ def _lib():
     lib.spense_linear.argtypes = [vp, vp, i32, i64, i64, vp, i32, i64, vp]
     lib.spense_linear.restype = ctypes.c_int
     lib.spense_linear_splits.argtypes = [vp, vp, i32, i64, i64, vp, i32, i64, i32, vp]
+    lib.spense_linear_noalloc.argtypes = [vp, vp, i32, i64, i64, vp, i32, i64, vp]
+    lib.spense_linear_noalloc.restype = ctypes.c_int
     lib.spense_quantize_tokens.restype = ctypes.c_int
     lib.spense_quantize_tokens.argtypes = [vp, i64, i64, i64, vp, i64, vp, vp]
     lib.spense_linear_w8a8.restype = ctypes.c_int
@@ -260,6 +263,19 @@ def spense_linear_splits(h: int, X, Y, splits: int, *, xdtype: Optional[int] = N
         ldy = Y.stride(0)
     st = _lib().spense_linear_splits(h, _ptr(X), xdtype, M, ldx, _ptr(Y), ydtype, ldy, splits, _stream(stream))
     _check(st, "spense_linear")
+
+
+def spense_linear_noalloc(h: int, X, Y, *, xdtype: Optional[int] = None, ydtype: Optional[int] = None,
+                          M: Optional[int] = None, ldx: Optional[int] = None, ldy: Optional[int] = None,
+                          stream=None) -> None:
+    """spense_linear with its workspaces in the library's fixed device scratch (allocates nothing)."""
+    xdtype = dtype_of(X) if xdtype is None else xdtype
+    ydtype = dtype_of(Y) if ydtype is None else ydtype
+    M = X.shape[0] if M is None else M
+    ldx = X.stride(0) if ldx is None else ldx
+    ldy = Y.stride(0) if ldy is None else ldy
+    st = _lib().spense_linear_noalloc(h, _ptr(X), xdtype, M, ldx, _ptr(Y), ydtype, ldy, _stream(stream))
+    _check(st, "spense_linear_noalloc")
 
 
 def spense_quantize_tokens(X, Xq, sx, *, M: Optional[int] = None, K: Optional[int] = None,

@@ -134,6 +134,7 @@ const char* spense_strerror(int status) {
     case SPENSE_EUNSUPPORTED: return "unsupported type combination";
     case SPENSE_ENOMEM: return "out of memory";
     case SPENSE_EHIP: return "HIP runtime error";
+    case SPENSE_ESCRATCH: return "the call needs more workspace than the fixed scratch of spense_linear_noalloc holds";
     default: return "unknown status";
   }
 }
@@ -723,7 +724,7 @@ static int grow_workspaces(spense_layer* h, const WsNeed& need, hipStream_t s) {
   return rc;
 }
 
-// Workspaces of one call on one layer.
+// Workspaces of one call on one layer (the handle's, or carved from the fixed scratch).
 struct WsPtrs {
   void* xws = nullptr;
   float* ws = nullptr;
@@ -811,10 +812,16 @@ static int max_need_parts(spense_layer* const* parts, int n_parts, int64_t M, Ws
   return SPENSE_OK;
 }
 
+static size_t align256(size_t n) { return (n + 255) / 256 * 256; }
+
 // Plans and launches one layer, or the two row classes of an output-split
-// layer in one grid.  `base` carries X, M, Y and the output type.
+// layer in one grid.  `base` carries X, M, Y and the output type.  With
+// `scratch` the call's workspaces are carved from that fixed device area
+// (counters first, then partials, then the gathered activations) instead of
+// the handles' own, and a call that needs more than it holds is refused
+// (SPENSE_ESCRATCH) before any launch.
 static int run_layers(spense_layer* const* parts, int n_parts, int64_t M, int32_t splits, const LinearArgs& base,
-                      hipStream_t s) {
+                      hipStream_t s, uint8_t* scratch = nullptr) {
   const bool x_aligned = aligned16(base.X) && (base.ldx % 8) == 0;
   LinearPlan p[2]{};
   LinearArgs aa[2]{base, base};
@@ -834,12 +841,27 @@ static int run_layers(spense_layer* const* parts, int n_parts, int64_t M, int32_
     grow = grow || !need[i].fits(parts[i]);
   }
   WsPtrs w[2];
-  if (grow) {
-    if (splits == 0 && (rc = max_need_parts(parts, n_parts, M, need)) != SPENSE_OK) return rc;
-    for (int i = 0; i < n_parts; ++i)
-      if ((rc = grow_workspaces(parts[i], need[i], s)) != SPENSE_OK) return rc;
+  if (scratch) {
+    size_t cnt = 0, bytes = 0;
+    for (int i = 0; i < n_parts; ++i) {
+      w[i].counters = (int32_t*)scratch + cnt;
+      cnt += need[i].cnt;
+      w[i].ws = (float*)(scratch + kScratchCounterBytes + bytes);
+      bytes += align256(need[i].ws);
+    }
+    for (int i = 0; i < n_parts; ++i) {
+      w[i].xws = scratch + kScratchCounterBytes + bytes;
+      bytes += align256(need[i].xws);
+    }
+    if (cnt * 4 > kScratchCounterBytes || bytes > kScratchBytes - kScratchCounterBytes) return SPENSE_ESCRATCH;
+  } else {
+    if (grow) {
+      if (splits == 0 && (rc = max_need_parts(parts, n_parts, M, need)) != SPENSE_OK) return rc;
+      for (int i = 0; i < n_parts; ++i)
+        if ((rc = grow_workspaces(parts[i], need[i], s)) != SPENSE_OK) return rc;
+    }
+    for (int i = 0; i < n_parts; ++i) w[i] = handle_ws(parts[i]);
   }
-  for (int i = 0; i < n_parts; ++i) w[i] = handle_ws(parts[i]);
   for (int i = 0; i < n_parts; ++i) {
     rc = bind_call(parts[i], M, p[i], aa[i], gather_now[i], w[i], s);
     if (rc != SPENSE_OK) return rc;
@@ -866,8 +888,10 @@ static int layer_parts(spense_layer* h, spense_layer* parts[2]) {
   return n;
 }
 
-int spense_linear_splits(spense_handle h, const void* X, int32_t xdtype, int64_t M, int64_t ldx, void* Y,
-                         int32_t ydtype, int64_t ldy, int32_t splits, void* stream) {
+// spense_linear_splits and spense_linear_noalloc: validation, then the launch
+// with the handle's workspaces or the fixed scratch.
+static int linear_call(spense_handle h, const void* X, int32_t xdtype, int64_t M, int64_t ldx, void* Y,
+                       int32_t ydtype, int64_t ldy, int32_t splits, void* stream, bool noalloc) {
   if (!h || !X || !Y) return SPENSE_EINVAL;
   if (h->split == 2) return SPENSE_EINVAL;  // a GLU block runs through spense_glu
   const LayerDesc& d = h->d;
@@ -897,7 +921,22 @@ int spense_linear_splits(spense_handle h, const void* X, int32_t xdtype, int64_t
   }
   spense_layer* parts[2] = {nullptr, nullptr};
   const int n_parts = layer_parts(h, parts);
-  return run_layers(parts, n_parts, M, splits, a, s);
+  uint8_t* scratch = nullptr;
+  if (noalloc) {
+    const hipError_t e = scratch_area(s, &scratch);
+    if (e != hipSuccess) return hip_fail(e);
+  }
+  return run_layers(parts, n_parts, M, splits, a, s, scratch);
+}
+
+int spense_linear_splits(spense_handle h, const void* X, int32_t xdtype, int64_t M, int64_t ldx, void* Y,
+                         int32_t ydtype, int64_t ldy, int32_t splits, void* stream) {
+  return linear_call(h, X, xdtype, M, ldx, Y, ydtype, ldy, splits, stream, false);
+}
+
+int spense_linear_noalloc(spense_handle h, const void* X, int32_t xdtype, int64_t M, int64_t ldx, void* Y,
+                          int32_t ydtype, int64_t ldy, void* stream) {
+  return linear_call(h, X, xdtype, M, ldx, Y, ydtype, ldy, 0, stream, true);
 }
 
 int spense_quantize_tokens(const void* X, int64_t M, int64_t K, int64_t ldx, uint8_t* Xq, int64_t ldq, float* sx,

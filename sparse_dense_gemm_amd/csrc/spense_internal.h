@@ -152,6 +152,14 @@ hipError_t launch_linear2(const LayerDesc& d0, const LinearArgs& a0, const Linea
                           const LinearArgs& a1, const LinearPlan& p1, hipStream_t s);
 hipError_t launch_zero_i32(int32_t* p, int64_t n, hipStream_t s);
 
+// Fixed device scratch of the no-allocation entry point (spense_kernels.hip):
+// kScratchBytes per GPU, the first kScratchCounterBytes holding split-K
+// counters that every completed launch leaves at zero.  scratch_area returns
+// the current device's copy (its address looked up once per device, its
+// counters cleared then by a fill kernel on `s`).
+constexpr size_t kScratchBytes = size_t(32) << 20;
+constexpr size_t kScratchCounterBytes = size_t(64) << 10;
+hipError_t scratch_area(hipStream_t s, uint8_t** base);
 // SpenseGPT+ scoring (spense_score.hip): diag(X^T X) of a bf16 [T, C] matrix via
 // fixed-order chunk partials [C][ceil(T / rows_per_chunk)]; GLU index scores;
 // exact top-k selection (ties to the lower index) as a 0/1 mask

@@ -8,6 +8,7 @@
 #include "spense_device.h"
 
 #include <algorithm>
+#include <mutex>
 
 namespace spense {
 namespace {
@@ -1199,6 +1200,41 @@ hipError_t launch_zero_i32(int32_t* p, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   zero_i32_kernel<<<blocks_for(n, 256), 256, 0, s>>>(p, n);
   return hipGetLastError();
+}
+
+// Scratch of the no-allocation entry point: split-K counters, split-K
+// partials and gathered activations of one call, in a fixed array that every
+// GPU holds for the life of the process.  In host code `scratch` names a
+// host-side stand-in, not device memory: the device address comes from
+// hipGetSymbolAddress, once per device with that device current, and only
+// that address is handed to kernels.
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint8_t* g_scratch_ptr[kMaxDevices] = {};
+}  // namespace
+
+hipError_t scratch_area(hipStream_t s, uint8_t** base) {
+  *base = nullptr;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    // the counters start at zero (every launch that uses one re-arms it)
+    e = launch_zero_i32((int32_t*)p, (int64_t)(kScratchCounterBytes / 4), s);
+    if (e != hipSuccess) return e;
+    g_scratch_ptr[dev] = (uint8_t*)p;
+  }
+  *base = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 }  // namespace spense

@@ -36,9 +36,9 @@ def test_library_exports_every_declared_function():
 
 
 def test_abi_version_and_strerror():
-    assert sdg.spense_abi_version() == 5
+    assert sdg.spense_abi_version() == 6
     lib = sdg._lib()
-    for code in (0, -1, -2, -3, -4):
+    for code in (0, -1, -2, -3, -4, -5):
         assert lib.spense_strerror(code) and lib.spense_strerror(code) != b"unknown status"
     assert lib.spense_strerror(12345) == b"unknown status"
 
@@ -104,6 +104,8 @@ def test_pack_rows_rejects_bad_arguments(kw, want):
 def test_linear_rejects_bad_arguments():
     lib = sdg._lib()
     assert lib.spense_linear(None, FAKE_PTR, sdg.DT_BF16, 1, 128, FAKE_PTR, sdg.DT_F32, 64, None) == sdg.SPENSE_EINVAL
+    assert lib.spense_linear_noalloc(None, FAKE_PTR, sdg.DT_BF16, 1, 128, FAKE_PTR, sdg.DT_F32, 64,
+                                     None) == sdg.SPENSE_EINVAL
     assert lib.spense_free(None) == sdg.SPENSE_EINVAL
     assert lib.spense_info(None, None) == sdg.SPENSE_EINVAL
     assert lib.spense_export(None, None, None, None, None, None, None) == sdg.SPENSE_EINVAL
