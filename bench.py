@@ -102,6 +102,15 @@ def spin_up(torch, step, seconds=SPIN_UP_S):
             return (time.perf_counter() - t0) * 1e3
 
 
+def lead_in(launch):
+    """One untimed launch just before the first timing event of a sequence:
+    with the device idle, that event would fire at once and the first timed
+    kernel would start only when the host has issued it (about one host call,
+    7-10 us, spread over the K steps); behind a running kernel the next launch
+    is already queued when the event fires."""
+    launch()
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -113,6 +122,8 @@ def parse():
     ap.add_argument("--ms", type=str, default="", help="override batch sizes, e.g. 1,4,16")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed region, run a plain 512 MiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--no-dense", action="store_true",
+                    help="skip the all-dense baseline (profiling runs: every linear launch is then a Spense one)")
     return ap.parse_args()
 
 
@@ -139,7 +150,7 @@ def load_traffic():
 class Layer:
     """One layer's inputs on the device and its packed handles (Spense and all-dense)."""
 
-    def __init__(self, sdg, torch, dev, spec, Mmax, rotate):
+    def __init__(self, sdg, torch, dev, spec, Mmax, rotate, with_dense=True):
         import synth
 
         self.spec = spec
@@ -171,11 +182,13 @@ class Layer:
         info = sdg.spense_info(h0)
         self.wbytes = info["weight_bytes"]
         self.handles = [h0] + [pack() for _ in range(copies(info) - 1)]
-        hd0 = sdg.spense_pack(Wd, wdt, scales=self.sd, dense_fraction=1.0)
-        dinfo = sdg.spense_info(hd0)
-        self.dbytes = dinfo["weight_bytes"]
-        self.dhandles = [hd0] + [sdg.spense_pack(Wd, wdt, scales=self.sd, dense_fraction=1.0)
-                                 for _ in range(copies(dinfo) - 1)]
+        self.dhandles, self.dbytes = [], None
+        if with_dense:
+            hd0 = sdg.spense_pack(Wd, wdt, scales=self.sd, dense_fraction=1.0)
+            dinfo = sdg.spense_info(hd0)
+            self.dbytes = dinfo["weight_bytes"]
+            self.dhandles = [hd0] + [sdg.spense_pack(Wd, wdt, scales=self.sd, dense_fraction=1.0)
+                                     for _ in range(copies(dinfo) - 1)]
         del Wd
 
     def flops(self, M):
@@ -219,7 +232,8 @@ def main():
     hv = variants.index(HEADLINE_VARIANT.get(args.workload, variants[0]))
 
     t0 = time.time()
-    sets = [[Layer(sdg, torch, dev, spec, Mmax, rotate=single) for spec in wl.layers] for wl in wls]
+    sets = [[Layer(sdg, torch, dev, spec, Mmax, rotate=single, with_dense=not args.no_dense) for spec in wl.layers]
+            for wl in wls]
     gen_s = time.time() - t0
 
     a8 = args.workload in A8_SETS
@@ -246,7 +260,8 @@ def main():
         for M in Ms:
             for layers in sets:
                 run_set(layers, M, i, False)
-            run_set(sets[hv], M, i, True)
+            if not args.no_dense:
+                run_set(sets[hv], M, i, True)
 
     spin_ms = spin_up(torch, warm_step)
     for i in range(args.warmup):
@@ -257,6 +272,7 @@ def main():
     ev = {}
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
+    lead_in(lambda: run_set(sets[0], Ms[0], 0, False))
     for vi, layers in enumerate(sets):
         for M in Ms:
             e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -272,7 +288,9 @@ def main():
     # ---- dense baseline (the same layers packed with dense fraction 1.0), same protocol ----
     dev_ = {}
     torch.cuda.synchronize()
-    for M in Ms:
+    if not args.no_dense:
+        lead_in(lambda: run_set(sets[hv], Ms[0], 0, True))
+    for M in Ms if not args.no_dense else ():
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for i in range(args.steps):
@@ -286,6 +304,7 @@ def main():
     per_layer = {}
     if not single:
         layers = sets[hv]
+        lead_in(lambda: call(layers[0].handles[0], layers[0].Xd[:Ms[0]], layers[0].Y[:Ms[0]]))
         for M in Ms:
             evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(layers) + 1)] for _ in range(args.steps)]
             for i in range(args.steps):
@@ -308,17 +327,18 @@ def main():
 
     head = sets[hv]
     wbytes = sum(L.wbytes for L in head)
-    dbytes = sum(L.dbytes for L in head)
+    dbytes = None if args.no_dense else sum(L.dbytes for L in head)
     per_m = {}
     for M in Ms:
         t = spense_us[(hv, M)]
+        du = dense_us.get(M)
         per_m[str(M)] = {
             "spense_us": round(t, 3),
-            "dense_us": round(dense_us[M], 3),
-            "speedup_vs_dense": round(dense_us[M] / t, 4),
+            "dense_us": None if du is None else round(du, 3),
+            "speedup_vs_dense": None if du is None else round(du / t, 4),
             "weight_GBs": round(wbytes / t / 1e3, 1),
             "weight_frac_of_peak": round(wbytes / t / 1e3 / HBM_PEAK_GBS, 4),
-            "dense_weight_GBs": round(dbytes / dense_us[M] / 1e3, 1),
+            "dense_weight_GBs": None if du is None else round(dbytes / du / 1e3, 1),
             "alg_TFLOPs": round(sum(L.flops(M) for L in head) / t / 1e6, 1),
         }
     total_us = sum(spense_us[(hv, M)] for M in Ms)
@@ -343,7 +363,8 @@ def main():
             variants_out[v] = {"dense_fraction": wls[vi].extra.get("fraction"),
                                "weight_bytes": sum(L.wbytes for L in sets[vi]),
                                **{f"M{M}_us": round(spense_us[(vi, M)], 3) for M in Ms},
-                               **{f"M{M}_speedup_vs_dense": round(dense_us[M] / spense_us[(vi, M)], 4) for M in Ms}}
+                               **{f"M{M}_speedup_vs_dense": (None if M not in dense_us else
+                                                             round(dense_us[M] / spense_us[(vi, M)], 4)) for M in Ms}}
 
     pack_ms = round(sum(L.pack_ms for L in head), 3)
     cpu = None if args.no_cpu_baseline else cpu_baseline(head, Ms, single, a8)
@@ -381,7 +402,7 @@ def main():
         "data": "synthetic",
         "config": cfg,
         "per_m": per_m,
-        "speedup_vs_dense": round(sum(dense_us.values()) / total_us, 4),
+        "speedup_vs_dense": None if args.no_dense else round(sum(dense_us.values()) / total_us, 4),
         "spense_weight_bytes": wbytes,
         "dense_weight_bytes": dbytes,
         "pack_ms_wall": pack_ms,
@@ -444,6 +465,7 @@ def run_glu(args, torch, sdg, synth, wl):
     torch.cuda.synchronize()
     ev = {}
     t_wall = time.perf_counter()
+    lead_in(lambda: step(hs, Ms[0], 0))
     for M in Ms:
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
@@ -455,6 +477,7 @@ def run_glu(args, torch, sdg, synth, wl):
     wall_s = time.perf_counter() - t_wall
     us = {M: a.elapsed_time(b) * 1e3 / args.steps for M, (a, b) in ev.items()}
     dev_ = {}
+    lead_in(lambda: step(hd, Ms[0], 0))
     for M in Ms:
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)

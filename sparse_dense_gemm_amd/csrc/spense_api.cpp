@@ -429,10 +429,15 @@ static bool decode_override(int& waves, int& depth, int& chunked) {
   return true;
 }
 
-// dynamic LDS of the single-shot decode kernel: the whole split's activations
+// dynamic LDS of the single-shot decode kernel: the whole split's activations,
+// M staged rows of the larger of the two row pitches (gathered: the split's
+// columns plus 16 bytes; contiguous: whole 1 KB copies plus 16 bytes), since a
+// call may run either form
 static int64_t decode_lds_bytes(const LayerDesc& d, int64_t M, int64_t S) {
   const int64_t steps = (d.n_sm + S - 1) / S + (d.n_dm + S - 1) / S;
-  return M * (steps * kMacro + 8) * 2;
+  const int64_t gathered = steps * kMacro * 2 + 16;
+  const int64_t contiguous = (steps + 3) / 4 * 1024 + 16;
+  return M * std::max(gathered, contiguous);
 }
 
 // dynamic LDS of the chunked kernels: two chunk buffers of `rows` staged rows,

@@ -286,6 +286,21 @@ __device__ __forceinline__ void load_unit(UnitFrag<WT>& f, const uint8_t* unit, 
   f.idx = __builtin_nontemporal_load((const uint32_t*)idx_addr);
 }
 
+// vector-memory loads load_unit issues
+template <typename WT>
+constexpr int kUnitLoads = sizeof(WT) == 1 ? 2 : 3;
+
+// s_waitcnt vmcnt(n), other counters left alone (gfx9 encoding: vmcnt bits
+// 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
+#define SPENSE_WAIT_VM(n) \
+  __builtin_amdgcn_s_waitcnt((int)(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8)))
+
+// A workgroup barrier without a memory fence: the fence of __syncthreads
+// would make every wave wait for all of its loads into LDS, the ones still in
+// flight included.  The memory clobber keeps the compiler from moving memory
+// accesses across it.
+__device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
+
 // Two SMFMACs: A0 with B0 (index half 0), A1 with B1 (index half 1).
 // The unit's two A operands as bf16 (e4m3 widened exactly).
 template <typename WT>

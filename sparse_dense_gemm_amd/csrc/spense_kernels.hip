@@ -303,7 +303,11 @@ __device__ __forceinline__ void decode_body(const LayerDesc& d, const LinearArgs
   // contiguous, so the unit index within the tile is k plus a per-range offset
   const int64_t sbase = ms0, dbase = d.n_sm + 2 * md0 - ns;
   const uint8_t* sidx = tile + d.idx_off + ms0 * 256;
-  const int pitch = (ns + nd) * 128 + 8;
+  // staged row pitch (elements): gathered rows are padded by 16 bytes;
+  // contiguous rows, copied in 1 KB pieces, to whole pieces plus 16 bytes
+  // (either way consecutive rows start on different LDS banks)
+  const int nch = (ns + nd + 3) / 4;  // 1 KB pieces of a contiguous staged row
+  const int pitch = GATHER ? (ns + nd) * 128 + 8 : 512 * nch + 8;
 
   // weights of unit k (lane offset 16 lane) and its index word (lane offset
   // 4 lane; a dense unit reads a word of itself, replaced at use)
@@ -321,30 +325,46 @@ __device__ __forceinline__ void decode_body(const LayerDesc& d, const LinearArgs
       load_unit<WT>(wr[i], stream ? unit_ptr(k) : d.wpack, (stream ? idx_ptr(k) : d.wpack) + 4 * lane, lane);
     }
   };
-  // Contiguous activations: the weight ring goes out first, so the staging
-  // set-up below runs while the first weight units are in flight.
-  if constexpr (!GATHER) issue_ring();
-
-  const TileOut to = tile_out(d, active ? rt : 0, lane);
-
-  // Stage X'p[0..M)[split columns] in LDS once: sparse macro-steps, then
-  // dense ones, in batches of kStageBatch 16-byte pieces per thread (all index
-  // loads, then all activation loads, then the LDS writes, so a batch costs one
-  // (contiguous) or two (gathered) memory round trips).  Every thread issues
-  // every load of a batch: pieces past the end read piece 0 (a valid address)
-  // and are not stored, so the load count is fixed.  Gathered: the first
-  // batch's column-index loads go out before the weight ring, so the
-  // activation loads that depend on them do not wait for the ring.  Offsets
-  // are 32-bit: rows < 16 and the leading dimension < 2^23 (the entry points
-  // refuse larger ones), columns < K_p < 2^23.
+  // Offsets are 32-bit: rows < 16 and the leading dimension < 2^23 (the entry
+  // points refuse larger ones), columns < K_p < 2^23.
   const uint16_t* X = (const uint16_t*)a.X;
-  const int per_row = (ns + nd) * 16;
-  const int pieces = M * per_row;
-  const float rcp_row = 1.0f / (float)(per_row > 0 ? per_row : 1);
   const int ldx = (int)a.ldx;
   // X'p column of unit-step u: 128 u + (u < ns ? xcol_s : xcol_d)
   const int xcol_s = 128 * ms0, xcol_d = (int)d.K_sp + 128 * (md0 - ns);
-  constexpr int kStageBatch = GATHER ? 2 : 8;
+  if constexpr (!GATHER) {
+    // Contiguous activations go straight from memory into LDS (no register
+    // round trip), issued before the weight ring: they land while the first
+    // units are in flight, and the wait for them below leaves the ring's
+    // loads outstanding.  Copy q: staged row q / nch, its bytes 1024 (q % nch)
+    // onwards, 16 bytes per lane; bytes past the split's columns read out of
+    // range, i.e. zero.
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(X, (uint32_t)(M * ldx * 2));
+    const int copies = M * nch;
+    for (int q = wave; q < copies; q += NW) {
+      const int mrow = q / nch, t = q - mrow * nch;
+      const int e = 512 * t + 8 * lane;  // element of the staged row
+      const int u = e >> 7;              // its unit-step
+      const uint32_t voff = u < ns + nd ? (uint32_t)((mrow * ldx + 128 * u + (u < ns ? xcol_s : xcol_d) + (e & 127)) * 2)
+                                        : kOutOfRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (void*)(xs_dyn + mrow * pitch + 512 * t), 16, voff, 0, 0, 0);
+    }
+    issue_ring();
+  }
+
+  const TileOut to = tile_out(d, active ? rt : 0, lane);
+
+  // Gathered activations are staged through registers: sparse macro-steps,
+  // then dense ones, in batches of kStageBatch 16-byte pieces per thread (all
+  // index loads, then all activation loads, then the LDS writes, so a batch
+  // costs two memory round trips).  Every thread issues every load of a batch:
+  // pieces past the end read piece 0 (a valid address) and are not stored, so
+  // the load count is fixed.  The first batch's column-index loads go out
+  // before the weight ring, so the activation loads that depend on them do
+  // not wait for the ring.
+  const int per_row = (ns + nd) * 16;
+  const int pieces = GATHER ? M * per_row : 0;
+  const float rcp_row = 1.0f / (float)(per_row > 0 ? per_row : 1);
+  constexpr int kStageBatch = 2;
   int rowoff[kStageBatch], col[kStageBatch];
   int lds_off[kStageBatch];
   bool ok[kStageBatch];
@@ -363,46 +383,47 @@ __device__ __forceinline__ void decode_body(const LayerDesc& d, const LinearArgs
       lds_off[j] = mrow * pitch + 128 * u + 8 * c8;
     }
   };
-  auto load_first = [&]() {  // contiguous: the activations; gathered: the column indices
+  auto load_first = [&]() {  // the column indices
 #pragma unroll
     for (int j = 0; j < kStageBatch; ++j) {
-      if constexpr (!GATHER) {
-        val[j] = *(const u32x4*)(X + rowoff[j] + col[j]);
-      } else {
-        i0[j] = *(const u32x4*)(d.pip + col[j]);
-        i1[j] = *(const u32x4*)(d.pip + col[j] + 4);
-      }
+      i0[j] = *(const u32x4*)(d.pip + col[j]);
+      i1[j] = *(const u32x4*)(d.pip + col[j] + 4);
     }
   };
-  auto load_second = [&]() {  // gathered: the activations at those columns
-    if constexpr (GATHER) {
+  auto load_second = [&]() {  // the activations at those columns
 #pragma unroll
-      for (int j = 0; j < kStageBatch; ++j) val[j] = gather8_from(X + rowoff[j], i0[j], i1[j]);
-    }
+    for (int j = 0; j < kStageBatch; ++j) val[j] = gather8_from(X + rowoff[j], i0[j], i1[j]);
   };
   auto store = [&]() {
 #pragma unroll
     for (int j = 0; j < kStageBatch; ++j)
       if (ok[j]) *(u32x4*)(xs_dyn + lds_off[j]) = val[j];
   };
-  const bool staging = pieces > 0;
-  if (staging) {
-    locate(threadIdx.x);
-    load_first();
-  }
-  if constexpr (GATHER) issue_ring();
-
-  if (staging) {
-    load_second();
-    store();
-    for (int e0 = threadIdx.x + kStageBatch * NW * 64; e0 < pieces; e0 += kStageBatch * NW * 64) {
-      locate(e0);
+  if constexpr (GATHER) {
+    const bool staging = pieces > 0;
+    if (staging) {
+      locate(threadIdx.x);
       load_first();
+    }
+    issue_ring();
+    if (staging) {
       load_second();
       store();
+      for (int e0 = threadIdx.x + kStageBatch * NW * 64; e0 < pieces; e0 += kStageBatch * NW * 64) {
+        locate(e0);
+        load_first();
+        load_second();
+        store();
+      }
     }
+    __syncthreads();
+  } else {
+    // this wave's copies have landed once at most the ring's loads are
+    // outstanding (they were issued after the copies, and the counter retires
+    // in order); the barrier then covers the other waves' copies
+    SPENSE_WAIT_VM(P * kUnitLoads<WT>);
+    barrier_no_fence();
   }
-  __syncthreads();
 
   f32x4 acc0 = f32x4{0.f, 0.f, 0.f, 0.f}, acc1 = f32x4{0.f, 0.f, 0.f, 0.f};
   if (stream) {

@@ -46,17 +46,6 @@ namespace {
   X(5, 4, 2, 8, 2, 4, 2)      \
   X(6, 2, 2, 8, 2, 3, 1)
 
-// s_waitcnt vmcnt(n), other counters left alone (gfx9 encoding: vmcnt bits
-// 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8)
-#define SPENSE_WAIT_VM(n) \
-  __builtin_amdgcn_s_waitcnt((int)(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8)))
-
-// A workgroup barrier without a memory fence: the fence of __syncthreads
-// would make every wave wait for all of its loads into LDS, the ones in flight
-// for later stages included.  The memory clobber keeps the compiler from
-// moving memory accesses across it.
-__device__ __forceinline__ void barrier_no_fence() { asm volatile("s_barrier" ::: "memory"); }
-
 template <typename WT, bool A8, int NW, int MT, int RT, int CH, int NS, int NP, bool NTW>
 __global__ __launch_bounds__((NW + NP) * 64) void linear_tile_kernel(LayerDesc d, LinearArgs a, LinearPlan p) {
   static_assert(!A8 || sizeof(WT) == 1, "W8A8 takes e4m3 weights");

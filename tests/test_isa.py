@@ -160,3 +160,36 @@ def test_weights_read_once_stream_non_temporally(gfx950_asm):
                 assert loads and not nt, (name[:90], nt[:3])
                 seen["default"] += 1
     assert seen["decode"] >= 8 and seen["nt"] >= 20 and seen["default"] >= 40, seen
+
+
+def test_decode_contiguous_staging_waits_only_for_its_copies(gfx950_asm):
+    """The decode kernels on contiguous activations copy them into LDS with
+    direct-to-LDS loads issued before the weight ring, then wait with the
+    ring still in flight: the vector-memory wait before the first barrier
+    must leave outstanding no more loads than were issued after the last
+    copy (the counter retires in order, so every copy has then landed), and
+    at least one (the ring is not drained)."""
+    labels = [(m.start(), m.group(1)) for m in re.finditer(r"^(_Z\w+):", gfx950_asm, re.M)]
+    checked = 0
+    for i, (pos, name) in enumerate(labels):
+        if "linear_decode" not in name or "Lb0EEEv" not in name:
+            continue
+        body = gfx950_asm[pos:labels[i + 1][0] if i + 1 < len(labels) else len(gfx950_asm)]
+        copies = after = 0
+        wait = None
+        for line in body.splitlines():
+            t = line.strip()
+            if t.startswith("s_barrier"):
+                break
+            if re.search(r"^buffer_load_dword\S*\s.*\slds\b", t):
+                assert after == 0, (name[:90], "a copy after a weight load")
+                copies += 1
+            elif re.match(r"(global|buffer)_load", t):
+                after += 1
+            w = re.search(r"s_waitcnt vmcnt\((\d+)\)", t)
+            if w:
+                wait = int(w.group(1))
+        assert copies >= 1 and wait is not None, name[:90]
+        assert 1 <= wait <= after, (name[:90], wait, after)
+        checked += 1
+    assert checked >= 8
