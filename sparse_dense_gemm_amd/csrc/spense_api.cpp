@@ -509,9 +509,10 @@ static int plan_linear(const spense_layer* h, int64_t M, int32_t splits, int64_t
     // nothing while the grid has no more workgroups than CUs (gate/up 25600 x
     // 5120: 200); there contiguous activations beat chunked staging up to the
     // CU's 160 KB (M = 8: 19.6 -> 19.1 us, M = 12: 20.1 -> 19.3 us).  Gathered
-    // activations stay at 64 KB: their staging takes two dependent loads per
-    // piece, and beyond that the gather pre-pass plus chunked staging wins
-    // (down 5120 x 25600, 6 splits: M = 16 26.4 us chunked vs 33.3 single-shot).
+    // activations stay at 64 KB: their staging issues one 2-byte load per
+    // activation, and beyond that the gather pre-pass plus chunked staging is
+    // as fast or faster (down 5120 x 25600, 6 splits, M = 8: 24.0 us chunked
+    // vs 24.7 single-shot; M = 16: 26.4 vs 33.3 with the earlier staging).
     auto lds_cap = [&](int64_t splits_) {
       const int64_t wgs = (NT_fill + p.waves - 1) / p.waves * splits_;
       return wgs <= kCUs && !d.gather ? kMaxDynLds : int64_t(64) * 1024;

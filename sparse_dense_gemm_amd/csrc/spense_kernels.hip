@@ -256,16 +256,6 @@ __device__ __forceinline__ u32x4 gather8_from(const uint16_t* xr, const u32x4& i
   return val;
 }
 
-// n / d for 0 <= n < 2^24 with a quotient below 16 (a staged activation row
-// index): the float estimate n * rcp (rcp ~ 1/d) is within one of the
-// quotient, and one correction step makes it exact.
-__device__ __forceinline__ int small_quotient(int n, int d, float rcp) {
-  int q = (int)((float)n * rcp);
-  const int r = n - q * d;
-  q += r < 0 ? -1 : (r >= d ? 1 : 0);
-  return q;
-}
-
 // Gathers 8 activations X'p[row][col..col+8) (col a multiple of 8).
 __device__ __forceinline__ u32x4 gather8(const LinearArgs& a, const LayerDesc& d, const uint16_t* xr, int64_t col) {
   if (!a.gather) return *(const u32x4*)(xr + col);
@@ -353,68 +343,69 @@ __device__ __forceinline__ void decode_body(const LayerDesc& d, const LinearArgs
 
   const TileOut to = tile_out(d, active ? rt : 0, lane);
 
-  // Gathered activations are staged through registers: sparse macro-steps,
-  // then dense ones, in batches of kStageBatch 16-byte pieces per thread (all
-  // index loads, then all activation loads, then the LDS writes, so a batch
-  // costs two memory round trips).  Every thread issues every load of a batch:
-  // pieces past the end read piece 0 (a valid address) and are not stored, so
-  // the load count is fixed.  The first batch's column-index loads go out
-  // before the weight ring, so the activation loads that depend on them do
-  // not wait for the ring.
-  const int per_row = (ns + nd) * 16;
-  const int pieces = GATHER ? M * per_row : 0;
-  const float rcp_row = 1.0f / (float)(per_row > 0 ? per_row : 1);
-  constexpr int kStageBatch = 2;
-  int rowoff[kStageBatch], col[kStageBatch];
-  int lds_off[kStageBatch];
-  bool ok[kStageBatch];
-  u32x4 val[kStageBatch], i0[kStageBatch], i1[kStageBatch];
-  auto locate = [&](int e0) {
+  // Gathered activations are staged through registers, one 16-byte piece (8
+  // consecutive X'p columns) at a time per thread.  The column map is the
+  // same for every row, so a thread loads the piece's 8 map entries once and
+  // then issues the gathers of every row of that piece together (kGRows rows
+  // at a time: one memory round trip for the map, one per kGRows rows for the
+  // activations).  A 2-byte buffer load per activation, from a resource over
+  // that row; padding columns (map entry < 0) read out of range, i.e. zero.
+  // The first map loads go out before the weight ring, so the gathers that
+  // depend on them do not wait for the ring.
+  const int per_row = (ns + nd) * 16;  // pieces per staged row
+  constexpr int kGRows = 8;
+  u32x4 map0, map1;  // the piece's 8 map entries
+  // (a piece past the row reads the map's first entries and stores nothing)
+  auto load_map = [&](int q) {
+    const int u = q >> 4, c8 = q & 15;
+    const int col = q < per_row ? 128 * u + (u < ns ? xcol_s : xcol_d) + 8 * c8 : 0;
+    map0 = *(const u32x4*)(d.pip + col);
+    map1 = *(const u32x4*)(d.pip + col + 4);
+  };
+  auto gather_piece = [&](int q) {
+    const bool okq = q < per_row;
+    const int u = okq ? q >> 4 : 0, c8 = q & 15;
+    const int src[8] = {(int)map0.x, (int)map0.y, (int)map0.z, (int)map0.w,
+                        (int)map1.x, (int)map1.y, (int)map1.z, (int)map1.w};
+    int sv[8];  // byte offsets in the row of the piece's source columns
 #pragma unroll
-    for (int j = 0; j < kStageBatch; ++j) {
-      const int e = e0 + j * NW * 64;
-      ok[j] = e < pieces;
-      const int ee = ok[j] ? e : 0;
-      const int mrow = small_quotient(ee, per_row, rcp_row);
-      const int rem = ee - mrow * per_row;
-      const int u = rem >> 4, c8 = rem & 15;
-      rowoff[j] = mrow * ldx;
-      col[j] = 128 * u + (u < ns ? xcol_s : xcol_d) + 8 * c8;
-      lds_off[j] = mrow * pitch + 128 * u + 8 * c8;
+    for (int t = 0; t < 8; ++t) sv[t] = src[t] >= 0 ? 2 * src[t] : (int)kOutOfRange;
+    uint16_t* dst = xs_dyn + 128 * u + 8 * c8;
+    for (int m0 = 0; m0 < M; m0 += kGRows) {
+      uint32_t h[kGRows][8];
+#pragma unroll
+      for (int r = 0; r < kGRows; ++r) {
+        if (m0 + r < M) {
+          const __amdgpu_buffer_rsrc_t xr = make_rsrc(X + (int64_t)(m0 + r) * ldx, (uint32_t)(2 * ldx));
+#pragma unroll
+          for (int t = 0; t < 8; ++t) h[r][t] = __builtin_amdgcn_raw_buffer_load_b16(xr, sv[t], 0, 0);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < kGRows; ++r) {
+        if (okq && m0 + r < M) {
+          u32x4 v;
+          v.x = h[r][0] | (h[r][1] << 16);
+          v.y = h[r][2] | (h[r][3] << 16);
+          v.z = h[r][4] | (h[r][5] << 16);
+          v.w = h[r][6] | (h[r][7] << 16);
+          *(u32x4*)(dst + (m0 + r) * pitch) = v;
+        }
+      }
     }
-  };
-  auto load_first = [&]() {  // the column indices
-#pragma unroll
-    for (int j = 0; j < kStageBatch; ++j) {
-      i0[j] = *(const u32x4*)(d.pip + col[j]);
-      i1[j] = *(const u32x4*)(d.pip + col[j] + 4);
-    }
-  };
-  auto load_second = [&]() {  // the activations at those columns
-#pragma unroll
-    for (int j = 0; j < kStageBatch; ++j) val[j] = gather8_from(X + rowoff[j], i0[j], i1[j]);
-  };
-  auto store = [&]() {
-#pragma unroll
-    for (int j = 0; j < kStageBatch; ++j)
-      if (ok[j]) *(u32x4*)(xs_dyn + lds_off[j]) = val[j];
   };
   if constexpr (GATHER) {
-    const bool staging = pieces > 0;
-    if (staging) {
-      locate(threadIdx.x);
-      load_first();
-    }
+    // every thread loads a map and gathers (unconditionally: a load on one
+    // path only would be copied at the merge, and the copy would wait for it)
+    load_map(threadIdx.x);
     issue_ring();
-    if (staging) {
-      load_second();
-      store();
-      for (int e0 = threadIdx.x + kStageBatch * NW * 64; e0 < pieces; e0 += kStageBatch * NW * 64) {
-        locate(e0);
-        load_first();
-        load_second();
-        store();
-      }
+    // keep the map's first use below the ring (a wait for the map must not
+    // hold back the ring's loads)
+    __builtin_amdgcn_sched_barrier(0);
+    gather_piece(threadIdx.x);
+    for (int q = threadIdx.x + NW * 64; q < per_row; q += NW * 64) {  // splits wider than 32 unit-steps
+      load_map(q);
+      gather_piece(q);
     }
     __syncthreads();
   } else {
