@@ -429,15 +429,17 @@ static bool decode_override(int& waves, int& depth, int& chunked) {
   return true;
 }
 
-// dynamic LDS of the single-shot decode kernel: the whole split's activations,
-// M staged rows of the larger of the two row pitches (gathered: the split's
-// columns plus 16 bytes; contiguous: whole 1 KB copies plus 16 bytes), since a
-// call may run either form
-static int64_t decode_lds_bytes(const LayerDesc& d, int64_t M, int64_t S) {
+// dynamic LDS of the single-shot decode kernel: the whole split's activations
+// in M staged rows, plus 16 bytes for the split-K arrival flag when the launch
+// has several splits.  Padded rows (swz false) take the larger of the two
+// pitches, since a call may run either form (gathered: the split's columns +
+// 16 bytes; contiguous: whole 1 KB blocks of 4 unit-steps + 16 bytes);
+// swizzled rows are whole 1 KB blocks.
+static int64_t decode_lds_bytes(const LayerDesc& d, int64_t M, int64_t S, bool swz = false) {
   const int64_t steps = (d.n_sm + S - 1) / S + (d.n_dm + S - 1) / S;
-  const int64_t gathered = steps * kMacro * 2 + 16;
-  const int64_t contiguous = (steps + 3) / 4 * 1024 + 16;
-  return M * std::max(gathered, contiguous);
+  const int64_t blocks = (steps + 3) / 4 * 1024;
+  const int64_t row = swz ? blocks : std::max(steps * kMacro * 2 + 16, blocks + 16);
+  return M * row + (S > 1 ? 16 : 0);
 }
 
 // dynamic LDS of the chunked kernels: two chunk buffers of `rows` staged rows,
@@ -453,7 +455,7 @@ constexpr int64_t kCUs = 256;             // compute units of the target GPU
 constexpr int64_t kMaxLd = int64_t(1) << 23;
 constexpr int64_t kLdsPerCU = 160 * 1024;  // LDS bytes per CU
 // dynamic LDS a kernel may take: the CU's LDS less room for the kernels' static
-// shared variables
+// shared variables (the decode kernels have none and may take all of it)
 constexpr int64_t kMaxDynLds = kLdsPerCU - 1024;
 
 // SPENSE_LDS=<configuration> runs linear_tile_kernel for batches above 16
@@ -515,7 +517,7 @@ static int plan_linear(const spense_layer* h, int64_t M, int32_t splits, int64_t
     // vs 24.7 single-shot; M = 16: 26.4 vs 33.3 with the earlier staging).
     auto lds_cap = [&](int64_t splits_) {
       const int64_t wgs = (NT_fill + p.waves - 1) / p.waves * splits_;
-      return wgs <= kCUs && !d.gather ? kMaxDynLds : int64_t(64) * 1024;
+      return wgs <= kCUs && !d.gather ? kLdsPerCU : int64_t(64) * 1024;
     };
     if (S == 0) {
       S = NT_fill >= 1024 ? 1 : std::max<int64_t>(1, (1920 + NT_fill - 1) / NT_fill);
@@ -526,12 +528,16 @@ static int plan_linear(const spense_layer* h, int64_t M, int32_t splits, int64_t
     // chunked staging keeps eight waves per workgroup as well (measured on
     // the gate/up layer at M = 8 and 16: 6-7% faster than four) with eight
     // units in flight per wave (4% faster than four there)
-    p.chunked = (force_chunked || ch == 1 || decode_lds_bytes(d, M, S) > lds_cap(S)) ? 1 : 0;
+    // unpadded swizzled rows where padded ones do not fit (gate/up M = 13-16:
+    // 16 x 5120 activations are exactly the CU's 160 KB)
+    p.swz = (decode_lds_bytes(d, M, S) > lds_cap(S) && decode_lds_bytes(d, M, S, true) <= lds_cap(S)) ? 1 : 0;
+    p.chunked = (force_chunked || ch == 1 || decode_lds_bytes(d, M, S, p.swz) > lds_cap(S)) ? 1 : 0;
+    if (p.chunked) p.swz = 0;
     if (p.chunked && !overridden) p.depth = 8;
     p.rgroups = (int)((d.NT + p.waves - 1) / p.waves);
     if (S > 1 && S * M * d.NT * 64 >= (int64_t(1) << 31)) return SPENSE_EUNSUPPORTED;  // 32-bit partial offsets
     p.splits = (int)S;
-    p.lds_bytes = (int)(p.chunked ? stream_lds_bytes(M, kStreamChunk, xbytes) : decode_lds_bytes(d, M, S));
+    p.lds_bytes = (int)(p.chunked ? stream_lds_bytes(M, kStreamChunk, xbytes) : decode_lds_bytes(d, M, S, p.swz));
     return SPENSE_OK;
   }
   // More than 16 rows, one layer per launch, on request: weight units
@@ -795,6 +801,12 @@ static int plan_call(spense_layer* const* parts, int n_parts, int64_t M, int32_t
         if (rc != SPENSE_OK) return rc;
       }
   }
+  // ... and the same staged-row layout (swizzled rows fit wherever padded ones do)
+  if (n_parts == 2 && !p[0].chunked && !p[1].chunked && p[0].swz != p[1].swz)
+    for (int i = 0; i < 2; ++i) {
+      p[i].swz = 1;
+      p[i].lds_bytes = (int)decode_lds_bytes(parts[i]->d, M, p[i].splits, true);
+    }
   return SPENSE_OK;
 }
 

@@ -101,6 +101,7 @@ struct LinearPlan {
   int xcd_remap; // 1: logical workgroup id = XCD-major remap of blockIdx (grid a multiple of 8)
   int lds_preset = -1; // >= 0: linear_tile_kernel configuration (spense_tile.hip); waves, mt, nr (row
                   // tiles per workgroup) and chunk (unit-steps per LDS stage) then describe it
+  int swz = 0;    // linear_decode_kernel: unpadded, swizzled staged rows (taken where padded rows do not fit)
 };
 
 // Configurations of linear_tile_kernel (weight units staged through LDS,

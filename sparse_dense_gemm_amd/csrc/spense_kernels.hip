@@ -270,10 +270,12 @@ __device__ __forceinline__ u32x4 gather8(const LinearArgs& a, const LayerDesc& d
 // two SMFMACs (only addresses and the index word differ), so the loop body is
 // straight-line code and the in-order load counter stays P-1 units ahead.
 // ---------------------------------------------------------------------------
-template <typename WT, int NW, int P, bool GATHER>
+template <typename WT, int NW, int P, bool GATHER, bool SWZ>
 __device__ __forceinline__ void decode_body(const LayerDesc& d, const LinearArgs& a, const LinearPlan& p, int block,
-                                            uint16_t* xs_dyn, int* last_flag_p) {
-  int& last_flag = *last_flag_p;
+                                            uint16_t* xs_dyn) {
+  // the split-K arrival flag sits in the last 16 bytes of the dynamic LDS
+  // (reserved by the planner only when the launch has several splits)
+  int* last_flag = (int*)((uint8_t*)xs_dyn + p.lds_bytes - 16);
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform: scalar address math
   const int S = p.splits;  // the grid is rgroups x S workgroups
@@ -293,11 +295,16 @@ __device__ __forceinline__ void decode_body(const LayerDesc& d, const LinearArgs
   // contiguous, so the unit index within the tile is k plus a per-range offset
   const int64_t sbase = ms0, dbase = d.n_sm + 2 * md0 - ns;
   const uint8_t* sidx = tile + d.idx_off + ms0 * 256;
-  // staged row pitch (elements): gathered rows are padded by 16 bytes;
-  // contiguous rows, copied in 1 KB pieces, to whole pieces plus 16 bytes
-  // (either way consecutive rows start on different LDS banks)
-  const int nch = (ns + nd + 3) / 4;  // 1 KB pieces of a contiguous staged row
-  const int pitch = GATHER ? (ns + nd) * 128 + 8 : 512 * nch + 8;
+  // Staged rows, so that the 16 rows a B read touches at once sit on
+  // different LDS banks: padded by 16 bytes (gathered rows: the split's
+  // columns + 16 bytes; contiguous rows, copied in 1 KB blocks of 4
+  // unit-steps: whole blocks + 16 bytes), or with SWZ unpadded whole 1 KB
+  // blocks in which row r keeps the 16-byte piece c of each unit-step (16
+  // pieces) at position c ^ (r & 15).  The swizzle lets 16 rows of 5120
+  // activations (exactly 160 KB) fit one CU; it costs address arithmetic
+  // per B read, so it is used only where the padded rows do not fit.
+  const int nch = (ns + nd + 3) / 4;  // 1 KB blocks of a contiguous staged row
+  const int pitch = SWZ ? 512 * nch : GATHER ? (ns + nd) * 128 + 8 : 512 * nch + 8;  // elements
 
   // weights of unit k (lane offset 16 lane) and its index word (lane offset
   // 4 lane; a dense unit reads a word of itself, replaced at use)
@@ -328,11 +335,13 @@ __device__ __forceinline__ void decode_body(const LayerDesc& d, const LinearArgs
     // loads outstanding.  Copy q: staged row q / nch, its bytes 1024 (q % nch)
     // onwards, 16 bytes per lane; bytes past the split's columns read out of
     // range, i.e. zero.
+    // (lane l writes position l of its 1 KB block, so with SWZ it loads the
+    // piece the swizzle puts there)
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(X, (uint32_t)(M * ldx * 2));
     const int copies = M * nch;
     for (int q = wave; q < copies; q += NW) {
       const int mrow = q / nch, t = q - mrow * nch;
-      const int e = 512 * t + 8 * lane;  // element of the staged row
+      const int e = 512 * t + 8 * (SWZ ? lane ^ (mrow & 15) : lane);  // element of the staged row
       const int u = e >> 7;              // its unit-step
       const uint32_t voff = u < ns + nd ? (uint32_t)((mrow * ldx + 128 * u + (u < ns ? xcol_s : xcol_d) + (e & 127)) * 2)
                                         : kOutOfRange;
@@ -370,7 +379,6 @@ __device__ __forceinline__ void decode_body(const LayerDesc& d, const LinearArgs
     int sv[8];  // byte offsets in the row of the piece's source columns
 #pragma unroll
     for (int t = 0; t < 8; ++t) sv[t] = src[t] >= 0 ? 2 * src[t] : (int)kOutOfRange;
-    uint16_t* dst = xs_dyn + 128 * u + 8 * c8;
     for (int m0 = 0; m0 < M; m0 += kGRows) {
       uint32_t h[kGRows][8];
 #pragma unroll
@@ -389,7 +397,7 @@ __device__ __forceinline__ void decode_body(const LayerDesc& d, const LinearArgs
           v.y = h[r][2] | (h[r][3] << 16);
           v.z = h[r][4] | (h[r][5] << 16);
           v.w = h[r][6] | (h[r][7] << 16);
-          *(u32x4*)(dst + (m0 + r) * pitch) = v;
+          *(u32x4*)(xs_dyn + (m0 + r) * pitch + 128 * u + 8 * (SWZ ? c8 ^ ((m0 + r) & 15) : c8)) = v;
         }
       }
     }
@@ -419,13 +427,28 @@ __device__ __forceinline__ void decode_body(const LayerDesc& d, const LinearArgs
   f32x4 acc0 = f32x4{0.f, 0.f, 0.f, 0.f}, acc1 = f32x4{0.f, 0.f, 0.f, 0.f};
   if (stream) {
     // Lanes of activation rows m >= M read row 0: output column m depends only
-    // on B column m, and columns m >= M are never stored.
-    const uint16_t* xb = xs_dyn + (m < M ? m : 0) * pitch + 16 * g;
+    // on B column m, and columns m >= M are never stored.  With SWZ lane l
+    // reads the pieces 8h + 2g and 8h + 2g + 1 of a unit-step (h: which
+    // 64-column half) at their swizzled positions.
+    const int mm = m < M ? m : 0;
+    const uint16_t* xb = xs_dyn + mm * pitch + 16 * g;
+    const uint8_t* xrow = (const uint8_t*)xs_dyn + mm * pitch * 2;
+    const int o00 = 16 * ((2 * g) ^ mm), o01 = 16 * ((2 * g + 1) ^ mm);
+    const int o10 = 16 * ((8 + 2 * g) ^ mm), o11 = 16 * ((9 + 2 * g) ^ mm);
+    auto xread = [&](int col) {  // B operand at staged column col (a multiple of 64)
+      if constexpr (SWZ) {
+        const uint8_t* q = xrow + 256 * (col >> 7);
+        const bool hi = (col >> 6) & 1;
+        return as_bf16x16(*(const u32x4*)(q + (hi ? o10 : o00)), *(const u32x4*)(q + (hi ? o11 : o01)));
+      } else {
+        return lds_b(xb + col);
+      }
+    };
     auto consume = [&](int i, int k) {
       const bool sp = k < ns;
       const int col0 = sp ? 128 * k : 128 * ns + 64 * (k - ns);
       const int col1 = sp ? col0 + 64 : col0;
-      mac_unit<WT>(acc0, acc1, wr[i], sp ? (int)wr[i].idx : (int)kDenseIdx, lds_b(xb + col0), lds_b(xb + col1));
+      mac_unit<WT>(acc0, acc1, wr[i], sp ? (int)wr[i].idx : (int)kDenseIdx, xread(col0), xread(col1));
     };
     // whole rings: every slot is consumed and refilled unconditionally, so
     // each slot waits for exactly its own loads
@@ -444,26 +467,25 @@ __device__ __forceinline__ void decode_body(const LayerDesc& d, const LinearArgs
       if (k0 + i < total) consume(i, k0 + i);
   }
   const f32x4 acc = acc0 + acc1;
-  finish_tile<1, 1>(d, a, &acc, &to, rt, 0, s, S, rg, &last_flag);
+  finish_tile<1, 1>(d, a, &acc, &to, rt, 0, s, S, rg, last_flag);
 }
 
-template <typename WT, int NW, int P, bool GATHER>
+// No static LDS: the staged activations may take all 160 KB of the CU.
+template <typename WT, int NW, int P, bool GATHER, bool SWZ>
 __global__ __launch_bounds__(NW * 64) void linear_decode_kernel(LayerDesc d, LinearArgs a, LinearPlan p) {
   extern __shared__ __attribute__((aligned(16))) uint16_t xs_dyn[];
-  __shared__ int last_flag;
-  decode_body<WT, NW, P, GATHER>(d, a, p, blockIdx.x, xs_dyn, &last_flag);
+  decode_body<WT, NW, P, GATHER, SWZ>(d, a, p, blockIdx.x, xs_dyn);
 }
 
 // Two layers in one grid (the two row classes of an output-split layer): the
 // first workgroups run layer 0, the rest layer 1, with the same kernel shape.
-template <typename WT, int NW, int P, bool GATHER>
+template <typename WT, int NW, int P, bool GATHER, bool SWZ>
 __global__ __launch_bounds__(NW * 64) void linear_decode2_kernel(LayerDesc d0, LinearArgs a0, LinearPlan p0,
                                                                  LayerDesc d1, LinearArgs a1, LinearPlan p1) {
   extern __shared__ __attribute__((aligned(16))) uint16_t xs_dyn[];
-  __shared__ int last_flag;
   const int g0 = p0.rgroups * p0.splits * p0.mgroups;
-  if ((int)blockIdx.x < g0) decode_body<WT, NW, P, GATHER>(d0, a0, p0, blockIdx.x, xs_dyn, &last_flag);
-  else decode_body<WT, NW, P, GATHER>(d1, a1, p1, blockIdx.x - g0, xs_dyn, &last_flag);
+  if ((int)blockIdx.x < g0) decode_body<WT, NW, P, GATHER, SWZ>(d0, a0, p0, blockIdx.x, xs_dyn);
+  else decode_body<WT, NW, P, GATHER, SWZ>(d1, a1, p1, blockIdx.x - g0, xs_dyn);
 }
 
 // ---------------------------------------------------------------------------
@@ -999,15 +1021,15 @@ hipError_t allow_lds(K kernel, int bytes) {
   return hipFuncSetAttribute((const void*)kernel, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
 }
 
-template <typename WT, int NW, int P, bool GATHER>
+template <typename WT, int NW, int P, bool GATHER, bool SWZ>
 hipError_t launch_decode_k(const Launch& L, hipStream_t s) {
   hipError_t e;
   if (L.two) {
-    auto k = linear_decode2_kernel<WT, NW, P, GATHER>;
+    auto k = linear_decode2_kernel<WT, NW, P, GATHER, SWZ>;
     if ((e = allow_lds(k, L.lds())) != hipSuccess) return e;
     k<<<L.grid(), NW * 64, L.lds(), s>>>(*L.d[0], *L.a[0], *L.p[0], *L.d[1], *L.a[1], *L.p[1]);
   } else {
-    auto k = linear_decode_kernel<WT, NW, P, GATHER>;
+    auto k = linear_decode_kernel<WT, NW, P, GATHER, SWZ>;
     if ((e = allow_lds(k, L.lds())) != hipSuccess) return e;
     k<<<L.grid(), NW * 64, L.lds(), s>>>(*L.d[0], *L.a[0], *L.p[0]);
   }
@@ -1016,8 +1038,10 @@ hipError_t launch_decode_k(const Launch& L, hipStream_t s) {
 
 template <typename WT, int NW, int P>
 hipError_t launch_decode_t(const Launch& L, hipStream_t s) {
-  if (L.a[0]->gather) return launch_decode_k<WT, NW, P, true>(L, s);
-  return launch_decode_k<WT, NW, P, false>(L, s);
+  const bool swz = L.p[0]->swz || (L.two && L.p[1]->swz);
+  if (L.two && L.p[0]->swz != L.p[1]->swz) return hipErrorInvalidValue;
+  if (L.a[0]->gather) return swz ? launch_decode_k<WT, NW, P, true, true>(L, s) : launch_decode_k<WT, NW, P, true, false>(L, s);
+  return swz ? launch_decode_k<WT, NW, P, false, true>(L, s) : launch_decode_k<WT, NW, P, false, false>(L, s);
 }
 
 template <typename WT, int NW, int NR, int P, int CH, int MT, bool NTW>

@@ -212,14 +212,17 @@ def test_decode_variants(wdtype, dense, monkeypatch):
 @pytest.mark.parametrize("dense", [("frac", 0.25), ("rand", 1280)])
 def test_single_shot_staging_beyond_64kb(wdtype, dense, monkeypatch):
     """Batch sizes whose activations exceed 64 KB of LDS but fit a CU's 160 KB
-    (K = 5120 in one split, M = 7..15, a grid of fewer workgroups than CUs) run the
+    (K = 5120 in one split, M = 7..16, a grid of fewer workgroups than CUs) run the
     single-shot decode kernel when the activations are contiguous (tail dense
     set; a chosen set is gathered and keeps chunked staging): the result equals
     the chunked kernel's bit for bit (same products, same order) and the oracle
-    within tolerance."""
+    within tolerance.  At M = 16 the padded rows do not fit and the unpadded,
+    swizzled rows run; with the tail set, activations at a leading dimension
+    that is not a multiple of 8 take the register (gathering) staging into the
+    same swizzled rows, and equal the aligned result bit for bit."""
     N, K = 160, 5120
     W, s = _small(N, K, wdtype, 41)
-    X = synth.make_x(15, K, DT_BF16, np.random.default_rng(42))
+    X = synth.make_x(16, K, DT_BF16, np.random.default_rng(42))
     sd = to_dev(s, DT_F32) if s is not None else None
     if dense[0] == "frac":
         h = pack_dev(to_dev(W, wdtype), wdtype, sd, dense_fraction=dense[1])
@@ -231,11 +234,16 @@ def test_single_shot_staging_beyond_64kb(wdtype, dense, monkeypatch):
     try:
         ref = oracle_pack_rows(W, wdtype, D)
         Xd = to_dev(X, DT_BF16)
-        for M in (7, 8, 12, 15):
+        Xu = torch.zeros((16, K + 1), dtype=torch.bfloat16, device="cuda")[:, :K]  # leading dimension K + 1
+        Xu.copy_(Xd)
+        for M in (7, 8, 12, 15, 16):
             Yref, B = oracle.linear_ref(X[:M], DT_BF16, ref, s)
-            # one split: the whole K range (M x 5128 bf16 = 72-154 KB) staged at once
+            # one split: the whole K range (M x 5128 bf16 = 72-154 KB; 160 KB unpadded at M = 16) staged at once
             monkeypatch.delenv("SPENSE_DECODE", raising=False)
             Y1 = linear_dev(h, Xd[:M], N, splits=1).cpu().numpy()
+            if dense[0] == "frac" and M >= 12:
+                Yu = linear_dev(h, Xu[:M], N, splits=1).cpu().numpy()
+                assert np.array_equal(Y1, Yu), ("unaligned", M)
             monkeypatch.setenv("SPENSE_DECODE", "8,4,1")  # chunked staging
             Y2 = linear_dev(h, Xd[:M], N, splits=1).cpu().numpy()
             assert np.array_equal(Y1, Y2), M
