@@ -846,6 +846,63 @@ __global__ void gather_x_kernel(LayerDesc d, const uint16_t* __restrict__ X, int
       gather8_from(X + mrow * ldx, *(const u32x4*)(d.pip + col), *(const u32x4*)(d.pip + col + 4));
 }
 
+// The same X'p for large batches: a workgroup stages `tok` whole rows of X in
+// LDS with 16-byte loads, then each thread loads the map entries of its
+// 8-column pieces (kGBatch pieces at a time) once and gathers them from LDS for
+// every staged row.  The 2-byte gathers run on LDS instead of the memory
+// path, and the map is read once per workgroup instead of once per row.
+constexpr int kGatherThreads = 512;
+constexpr int kGBatch = 4;
+__global__ __launch_bounds__(kGatherThreads) void gather_x_rows_kernel(LayerDesc d, const uint16_t* __restrict__ X,
+                                                                     int64_t M, int64_t ldx,
+                                                                     uint16_t* __restrict__ Xp, int tok) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t xr[];  // tok rows of K
+  const int64_t K = d.K, m0 = (int64_t)blockIdx.x * tok;
+  const int nt = (int)(M - m0 < tok ? M - m0 : tok);
+  const int tid = threadIdx.x;
+  for (int t = 0; t < nt; ++t) {
+    const uint16_t* x = X + (m0 + t) * ldx;
+    uint16_t* xs = xr + (int64_t)t * K;
+    if (((uintptr_t)x % 16) == 0 && K % 8 == 0) {
+      for (int64_t k0 = 8 * (int64_t)tid; k0 < K; k0 += 8 * 4 * kGatherThreads) {
+        u32x4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int64_t k = k0 + u * 8 * kGatherThreads;
+          v[u] = k < K ? *(const u32x4*)(x + k) : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int64_t k = k0 + u * 8 * kGatherThreads;
+          if (k < K) *(u32x4*)(xs + k) = v[u];
+        }
+      }
+    } else {
+      for (int64_t k = tid; k < K; k += kGatherThreads) xs[k] = x[k];
+    }
+  }
+  __syncthreads();
+  const int64_t pieces = d.K_p / 8;
+  for (int64_t q0 = tid; q0 < pieces; q0 += (int64_t)kGatherThreads * kGBatch) {
+    u32x4 i0[kGBatch], i1[kGBatch];
+#pragma unroll
+    for (int u = 0; u < kGBatch; ++u) {
+      const int64_t q = q0 + (int64_t)u * kGatherThreads;
+      const int64_t c = q < pieces ? 8 * q : 0;
+      i0[u] = *(const u32x4*)(d.pip + c);
+      i1[u] = *(const u32x4*)(d.pip + c + 4);
+    }
+    for (int t = 0; t < nt; ++t) {
+#pragma unroll
+      for (int u = 0; u < kGBatch; ++u) {
+        const int64_t q = q0 + (int64_t)u * kGatherThreads;
+        if (q < pieces)
+          *(u32x4*)(Xp + (m0 + t) * d.K_p + 8 * q) = gather8_from(xr + (int64_t)t * K, i0[u], i1[u]);
+      }
+    }
+  }
+}
+
 // Per-token e4m3 quantisation, one workgroup of 256 threads per token: the
 // largest magnitude of the row (a max reduction, exact in any order), the
 // scale max/448 as an fp32 quotient (1 for an all-zero row), then each code
@@ -1183,6 +1240,22 @@ hipError_t launch_pack(const LayerDesc& d, const void* W, int64_t ldw, hipStream
 }
 
 hipError_t launch_gather_x(const LayerDesc& d, const void* X, int64_t M, int64_t ldx, void* Xp, hipStream_t s) {
+  // large batches: rows staged in LDS, as many per workgroup as fit 112 KB
+  // (K = 5120: 8, 10240: 5, 27648: 2), when that still gives 128 workgroups
+  constexpr int64_t kGLds = 112 * 1024;
+  if (d.K * 2 <= kGLds) {
+    const int tok = (int)std::min<int64_t>(8, kGLds / (d.K * 2));
+    if ((M + tok - 1) / tok >= 128) {
+      const size_t lds = (size_t)tok * d.K * 2;
+      auto k = gather_x_rows_kernel;
+      if (lds > 64 * 1024) {
+        const hipError_t e = hipFuncSetAttribute((const void*)k, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+        if (e != hipSuccess) return e;
+      }
+      k<<<(unsigned)((M + tok - 1) / tok), kGatherThreads, lds, s>>>(d, (const uint16_t*)X, M, ldx, (uint16_t*)Xp, tok);
+      return hipGetLastError();
+    }
+  }
   gather_x_kernel<<<blocks_for(M * (d.K_p / 8), 256), 256, 0, s>>>(d, (const uint16_t*)X, M, ldx, (uint16_t*)Xp);
   return hipGetLastError();
 }

@@ -130,6 +130,34 @@ def test_gather_equals_contiguous_bitwise():
         sdg.spense_free(h2)
 
 
+@pytest.mark.parametrize("K,K_d,M,ldx_pad", [(1000, 248, 1100, 0), (1024, 256, 1030, 3), (7168, 1792, 1040, 0)])
+def test_large_batch_gather_equals_contiguous_bitwise(K, K_d, M, ldx_pad):
+    """Large batches gather X'p in a pre-pass that stages whole rows in LDS
+    (several rows per workgroup; K = 1000 and a leading dimension of K + 3
+    take the element-wise staging): the output equals the pre-permuted
+    contiguous call bit for bit."""
+    N = 64
+    W, s = _small(N, K, DT_FP8, 21)
+    D = synth.random_dense_set(K, K_d, 22)
+    X = synth.make_x(M, K, DT_BF16, np.random.default_rng(23))
+    pi, K_s, _ = oracle.resolve_dense_set(K, dense_cols=D)
+    sd = to_dev(s, DT_F32)
+    h1 = pack_dev(to_dev(W, DT_FP8), DT_FP8, sd, dense_cols=D)
+    h2 = pack_dev(to_dev(np.ascontiguousarray(W[:, pi]), DT_FP8), DT_FP8, sd, dense_fraction=K_d / K)
+    try:
+        Xd = to_dev(X, DT_BF16)
+        if ldx_pad:
+            buf = torch.zeros((M, K + ldx_pad), dtype=torch.bfloat16, device="cuda")
+            buf[:, :K].copy_(Xd)
+            Xd = buf[:, :K]
+        y1 = linear_dev(h1, Xd, N)
+        y2 = linear_dev(h2, to_dev(np.ascontiguousarray(X[:, pi]), DT_BF16), N)
+        assert torch.equal(y1, y2)
+    finally:
+        sdg.spense_free(h1)
+        sdg.spense_free(h2)
+
+
 def test_power_of_two_scaling_and_determinism():
     N, K, M = 80, 768, 12
     W, s = _small(N, K, DT_FP8, 14)
