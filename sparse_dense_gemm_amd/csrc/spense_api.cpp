@@ -607,8 +607,18 @@ static int plan_linear(const spense_layer* h, int64_t M, int32_t splits, int64_t
     const Preset& c = kPresets[i];
     return (NT_fill + c.nw * c.nr - 1) / (c.nw * c.nr) * ((M + 16 * c.mt - 1) / (16 * c.mt));
   };
+  // Down-projection-like layers (few output rows, long K) with bf16
+  // activations, 32 < M <= 64: four waves with two row tiles and two m-tiles
+  // (down 5120 x 25600 at M = 64, seven packed copies rotated: 45.4 -> 40.9
+  // us).  Eight single-row-tile waves with an eight-unit ring and one m-tile
+  // (preset 15) won a sweep at M = 32 with the layer's weights resident in the
+  // last-level cache but lost with them streamed from HBM (30.4 -> 34.5 us),
+  // and stays available as a forced preset.
+  const bool down_like = xbytes == 2 && d.NT * kRowTile <= 8192 && d.K_p >= 16384;
   int pre;
-  if (M <= 32) {
+  if (down_like && M > 32 && M <= 64) {
+    pre = 1;
+  } else if (M <= 32) {
     pre = workgroups(2) >= 150 ? 2 : 0;
   } else {
     // (preset, workgroups it needs before splits); e4m3 codes first try eight

@@ -134,7 +134,9 @@ hipError_t launch_linear_tile(const LayerDesc& d, const LinearArgs& a, const Lin
   X(11, 4, 4, 4, 4, 2)         \
   X(12, 8, 2, 4, 4, 4)         \
   X(13, 8, 4, 2, 2, 8)         \
-  X(14, 8, 4, 2, 4, 4)
+  X(14, 8, 4, 2, 4, 4)         \
+  X(15, 8, 1, 8, 8, 1)         \
+  X(16, 8, 1, 4, 4, 2)
 
 // Preset 13 runs on e4m3 activation codes only: with bf16 activations its
 // eight m-tiles of operand pairs do not fit the registers of two waves per SIMD.

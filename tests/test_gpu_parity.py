@@ -282,7 +282,7 @@ def test_single_shot_staging_beyond_64kb(wdtype, dense, monkeypatch):
         sdg.spense_free(h)
 
 
-TILE_PRESETS = list(range(15))
+TILE_PRESETS = list(range(17))
 
 
 @pytest.mark.parametrize("wdtype", [DT_FP8, DT_BF16])
