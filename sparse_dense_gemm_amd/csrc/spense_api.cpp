@@ -660,8 +660,27 @@ static int plan_linear(const spense_layer* h, int64_t M, int32_t splits, int64_t
     const int64_t resident = kCUs * std::max<int64_t>(1, kLdsPerCU / lds);
     S = units >= kCUs / 2 ? 1 : std::max<int64_t>(1, std::min<int64_t>(resident / units, max_splits));
     // each split writes and reads back fp32 partials of the whole output
-    // (8 M N bytes); keep that below half the packed weight bytes
-    S = std::max<int64_t>(1, std::min<int64_t>(S, d.tile_bytes / (256 * M)));
+    // (8 M N bytes); keep that below two thirds of the packed weight bytes
+    // (O 5120 x 8192 at M = 128: three splits 26.2 us, two 29.9 us)
+    S = std::max<int64_t>(1, std::min<int64_t>(S, d.tile_bytes / (192 * M)));
+    // Of the split counts up to that, take the one with the least work on the
+    // busiest CU: a CU whose share of the grid is more than eight waves runs
+    // the extra workgroups beside (or after) its first ones, so the launch
+    // lasts about ceil(waves / (8 per CU)) workgroup-lengths of K / S each.
+    // A grid just past one workgroup per CU is the costly case (QKV 12288 x
+    // 5120 at M = 64, weights streamed from HBM: three splits, 288
+    // eight-wave workgroups, 37.8 us; two splits, 192 workgroups, 30.1 us).
+    int64_t best = 1;
+    double best_cost = 1e30;
+    for (int64_t s = 1; s <= S; ++s) {
+      const int64_t rounds = (units * s * p.waves + kCUs * 8 - 1) / (kCUs * 8);
+      const double cost = (double)rounds / (double)s;
+      if (cost < best_cost * (1 - 1e-9)) {
+        best_cost = cost;
+        best = s;
+      }
+    }
+    S = best;
   }
   // the partials are addressed with 32-bit offsets
   if (S > 1 && S * M * d.NT * 64 >= (int64_t(1) << 31)) {
