@@ -67,18 +67,15 @@ __device__ __forceinline__ uint32_t bf16_rne(float f) {
 }
 
 // Eight e4m3 codes (little-endian in lo, hi) -> eight bf16.  Every e4m3 value
-// is exact in fp32 and in bf16, so keeping the upper half of the fp32 word is
-// exact.
+// is exact in bf16; the conversion with a unit scale widens two codes per
+// instruction (code 2j to the low half of word j, code 2j + 1 to the high
+// half).
 __device__ __forceinline__ bf16x8 fp8x8_to_bf16(uint32_t lo, uint32_t hi) {
-  auto f0 = __builtin_amdgcn_cvt_pk_f32_fp8(lo, false);
-  auto f1 = __builtin_amdgcn_cvt_pk_f32_fp8(lo, true);
-  auto f2 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, false);
-  auto f3 = __builtin_amdgcn_cvt_pk_f32_fp8(hi, true);
   u32x4 w;
-  w.x = __builtin_amdgcn_perm(__float_as_uint(f0[1]), __float_as_uint(f0[0]), 0x07060302u);
-  w.y = __builtin_amdgcn_perm(__float_as_uint(f1[1]), __float_as_uint(f1[0]), 0x07060302u);
-  w.z = __builtin_amdgcn_perm(__float_as_uint(f2[1]), __float_as_uint(f2[0]), 0x07060302u);
-  w.w = __builtin_amdgcn_perm(__float_as_uint(f3[1]), __float_as_uint(f3[0]), 0x07060302u);
+  w.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false));
+  w.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true));
+  w.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false));
+  w.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true));
   return __builtin_bit_cast(bf16x8, w);
 }
 
