@@ -444,11 +444,25 @@ __device__ __forceinline__ void decode_body(const LayerDesc& d, const LinearArgs
         return lds_b(xb + col);
       }
     };
-    auto consume = [&](int i, int k) {
+    // B operands of unit k (sparse: the unit-step's two 64-column halves;
+    // dense: one 64-column half, read twice: a select between loaded values
+    // would wait for them at once)
+    auto bload = [&](int k, bf16x16& B0, bf16x16& B1) {
       const bool sp = k < ns;
       const int col0 = sp ? 128 * k : 128 * ns + 64 * (k - ns);
-      const int col1 = sp ? col0 + 64 : col0;
-      mac_unit<WT>(acc0, acc1, wr[i], sp ? (int)wr[i].idx : (int)kDenseIdx, xread(col0), xread(col1));
+      B0 = xread(col0);
+      B1 = xread(sp ? col0 + 64 : col0);
+    };
+    // The B operands are read one unit ahead (the LDS round trip of the next
+    // unit overlaps this unit's products).
+    bf16x16 b0, b1;
+    bload(0, b0, b1);
+    auto consume = [&](int i, int k) {
+      bf16x16 n0, n1;
+      bload(k + 1 < total ? k + 1 : k, n0, n1);
+      mac_unit<WT>(acc0, acc1, wr[i], k < ns ? (int)wr[i].idx : (int)kDenseIdx, b0, b1);
+      b0 = n0;
+      b1 = n1;
     };
     // whole rings: every slot is consumed and refilled unconditionally, so
     // each slot waits for exactly its own loads
