@@ -607,25 +607,27 @@ static int plan_linear(const spense_layer* h, int64_t M, int32_t splits, int64_t
     const Preset& c = kPresets[i];
     return (NT_fill + c.nw * c.nr - 1) / (c.nw * c.nr) * ((M + 16 * c.mt - 1) / (16 * c.mt));
   };
-  // Down-projection-like layers (few output rows, long K) with bf16
-  // activations, 32 < M <= 64: four waves with two row tiles and two m-tiles
-  // (down 5120 x 25600 at M = 64, seven packed copies rotated: 45.4 -> 40.9
-  // us).  Eight single-row-tile waves with an eight-unit ring and one m-tile
+  // Layers with few output rows (O and down: 320 row tiles) take two row
+  // tiles and two m-tiles per wave from 40 workgroups before splits, which
+  // the splits then bring to one per CU (down 5120 x 25600 / 5120 x 27648,
+  // weights streamed from HBM: M = 64 36.3 / 45.1 us against 43.4 / 51.9
+  // with one row tile per wave; M = 96 with one row tile 58.6 / 66.3 us).
+  // Eight single-row-tile waves with an eight-unit ring and one m-tile
   // (preset 15) won a sweep at M = 32 with the layer's weights resident in the
   // last-level cache but lost with them streamed from HBM (30.4 -> 34.5 us),
   // and stays available as a forced preset.
-  const bool down_like = xbytes == 2 && d.NT * kRowTile <= 8192 && d.K_p >= 16384;
   int pre;
-  if (down_like && M > 32 && M <= 64) {
-    pre = 1;
-  } else if (M <= 32) {
+  if (M <= 32) {
     pre = workgroups(2) >= 150 ? 2 : 0;
   } else {
     // (preset, workgroups it needs before splits); e4m3 codes first try eight
     // m-tiles per wave (four row tiles), which halves the weight bytes loaded
-    // per product (gate/up 55296x5120 at M = 2048: 574 us vs 645 us)
+    // per product (gate/up 55296x5120 at M = 2048: 574 us vs 645 us).  For
+    // bf16 activations the two-row-tile, four-m-tile step takes the two-unit
+    // ring and chunk (gate/up 51200 / 55296 x 5120 at M = 64: 51.8 / 54.3 us
+    // against 53.7 / 56.3 with four-unit ring and chunk).
     const int64_t need_a8[4][2] = {{13, 150}, {6, 150}, {12, 120}, {2, 64}};
-    const int64_t need_a16[4][2] = {{14, 150}, {14, 150}, {12, 120}, {2, 64}};
+    const int64_t need_a16[4][2] = {{14, 150}, {14, 150}, {6, 120}, {2, 40}};
     pre = 0;
     for (const auto& c : xbytes == 1 ? need_a8 : need_a16)
       if (workgroups((int)c[0]) >= c[1]) {
