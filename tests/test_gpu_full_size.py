@@ -218,3 +218,39 @@ def test_glu_bench_shape():
             assert ry <= 1.0
     finally:
         sdg.spense_free(h)
+
+
+@pytest.mark.parametrize("a8", [False, True], ids=["w8a16", "w8a8"])
+def test_down_projection_between_benchmark_batches(a8):
+    """The 36B-class down projection (5120 x 27648, 6912 chosen dense
+    columns) at batch sizes between the benchmark's, where the launch planner
+    moves to larger tiles with split-K (M > 128) or to two-row-tile tiles with
+    splits (M = 96): automatic plan, a spread sample of row tiles for a sample
+    of tokens, against the oracle (W8A8: the exact W8A8 result of the oracle's
+    own per-token codes)."""
+    spec = next(x for x in WL["layer36b_fp8"].layers if x.name == "down")
+    Ms = (96, 192, 256, 384, 512)
+    W, s, X, D = synth.layer_inputs(spec, max(Ms))
+    rows = _spread_rows(spec.N)
+    pi, K_s, _ = oracle.resolve_dense_set(spec.K, dense_cols=D)
+    ref = oracle.pack(W[rows], DT_FP8, pi, K_s)
+    h = pack_dev(to_dev(W, DT_FP8), DT_FP8, to_dev(s, DT_F32), dense_cols=D)
+    try:
+        Xd = to_dev(X, DT_BF16)
+        for M in Ms:
+            sel = np.unique(np.concatenate([np.random.default_rng(7 + M).choice(M, 30, replace=False), [0, M - 1]]))
+            Y = torch.empty((M, spec.N), dtype=torch.float32, device="cuda")
+            if a8:
+                sdg.spense_linear_w8a8(h, Xd[:M], Y)
+                q, sx = oracle.quantize_tokens_ref(X[sel], DT_BF16)
+                Yref, B = oracle.linear_w8a8_ref(q, sx, ref, s[rows])
+            else:
+                sdg.spense_linear(h, Xd[:M], Y)
+                Yref, B = oracle.linear_ref(X[sel], DT_BF16, ref, s[rows])
+            torch.cuda.synchronize()
+            r = tol_ratio(Y.cpu().numpy()[np.ix_(sel, rows)], Yref, B)
+            log(f"[down between batches] {'w8a8' if a8 else 'w8a16'} M={M}: ratio {r:.3e} "
+                f"on {sel.size} tokens x {rows.size} rows")
+            assert r <= 1.0
+    finally:
+        sdg.spense_free(h)
