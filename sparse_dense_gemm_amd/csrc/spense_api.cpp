@@ -640,7 +640,10 @@ static int plan_linear(const spense_layer* h, int64_t M, int32_t splits, int64_t
     // bf16 activations M = 256 / 512 91.5 / 138.6 us against 128.3 / 213.8;
     // e4m3 codes 74.0 / 117.4 against 114.0 / 139.0; for e4m3 codes the
     // two-row-tile tile stays ahead up to M = 384: 95.8 against 103.9 us).
-    if (d.NT * kRowTile <= 8192 && d.K_p >= 16384 && M > 128) pre = xbytes == 1 && M <= 384 ? 6 : 14;
+    // Where the counts already reach the eight-m-tile tile of e4m3 codes
+    // (M = 2048) it stays: the four-m-tile one took that layer's pass from
+    // 1213 to 1334 us.
+    if (d.NT * kRowTile <= 8192 && d.K_p >= 16384 && M > 128 && pre != 13) pre = xbytes == 1 && M <= 384 ? 6 : 14;
   }
   if (const char* t = std::getenv("SPENSE_TILE")) {
     // a forced preset whose two staging buffers would not fit in one CU's LDS,
