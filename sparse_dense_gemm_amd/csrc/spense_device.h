@@ -320,6 +320,48 @@ __device__ __forceinline__ void mac_unit(f32x4& acc0, f32x4& acc1, const UnitFra
   acc1 = smfmac_bf16<1>(A1, B1, acc1, idx);
 }
 
+// Split, row group and m-group of workgroup `block` of `grid`.  Logical id
+// L = s * (rgroups * mgroups) + (position within the split).  Workgroups are
+// dealt to the 8 XCDs round-robin; with the XCD remap each XCD takes a
+// contiguous run of logical ids.  Within a split the order is m-group
+// fastest over one row group, or, with rblock > 1, blocks of rblock row
+// groups taken one m-group at a time (row group fastest), so that the
+// workgroups an XCD runs together share both weight slices and activation
+// rows in its L2: with R row groups x G m-groups resident, one stage moves
+// R weight slices and G activation slices into the L2 instead of one slice
+// and R G activation slices.
+__device__ __forceinline__ void tile_coords(int b, int grid, const LinearPlan& p, int& s, int& rg, int& mg) {
+  if (p.xcd_remap) b = (b % 8) * (grid / 8) + b / 8;
+  const int S = p.splits;
+  s = 0;
+  mg = 0;
+  rg = b;
+  if (p.mgroups > 1 && p.rblock > 1) {
+    const uint32_t per_split = (uint32_t)p.rgroups * (uint32_t)p.mgroups;
+    uint32_t L = (uint32_t)b;
+    if (S > 1) {
+      s = (int)(L / per_split);
+      L -= (uint32_t)s * per_split;
+    }
+    const uint32_t span = (uint32_t)p.rblock * (uint32_t)p.mgroups;
+    const uint32_t blk = L / span, base = blk * (uint32_t)p.rblock;
+    const uint32_t left = (uint32_t)p.rgroups - base;
+    const uint32_t gb = left < (uint32_t)p.rblock ? left : (uint32_t)p.rblock;
+    const uint32_t rem = L - blk * span;
+    mg = (int)(rem / gb);
+    rg = (int)(base + rem - (uint32_t)mg * gb);
+    return;
+  }
+  if (p.mgroups > 1) {
+    mg = (int)((uint32_t)b % (uint32_t)p.mgroups);
+    rg = (int)((uint32_t)b / (uint32_t)p.mgroups);
+  }
+  if (S > 1) {
+    s = (int)((uint32_t)rg / (uint32_t)p.rgroups);
+    rg = (int)((uint32_t)rg % (uint32_t)p.rgroups);
+  }
+}
+
 // Steps [n s / S, n (s + 1) / S) of split s of S.  Launch set-up runs before
 // a wave's first weight load, so it avoids 64-bit division: n < 2^16 (K_p <
 // 2^23) and S <= 64 keep n (s + 1) below 2^31, and one split needs none.

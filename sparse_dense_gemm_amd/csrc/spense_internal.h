@@ -99,22 +99,25 @@ struct LinearPlan {
   int nr;        // row tiles per wave (linear_stream_kernel)
   int preset;    // index into SPENSE_TILE_PRESETS, or -1 (one row tile and m-tile per wave)
   int xcd_remap; // 1: logical workgroup id = XCD-major remap of blockIdx (grid a multiple of 8)
-  int lds_preset = -1; // >= 0: linear_tile_kernel configuration (spense_tile.hip); waves, mt, nr (row
-                  // tiles per workgroup) and chunk (unit-steps per LDS stage) then describe it
+  int lds_preset = -1; // >= 0: linear_tile_kernel configuration (spense_tile.hip); waves, mt (m-tiles
+                  // per workgroup) and nr (row tiles per workgroup) then describe it, chunk is 1
   int swz = 0;    // linear_decode_kernel: unpadded, swizzled staged rows (taken where padded rows do not fit)
+  int rblock = 1; // > 1: several m-groups run their row groups in blocks of rblock (see tile_coords)
 };
 
-// Configurations of linear_tile_kernel (weight units staged through LDS,
-// consumer waves splitting the tokens): consumer waves, m-tiles per consumer,
-// row tiles per workgroup, unit-steps per stage, stages in the LDS ring,
-// producer waves.
+// Configurations of linear_tile_kernel (weight units and activation
+// fragments both staged through LDS): waves along output rows, waves along
+// tokens, row tiles per wave, m-tiles per wave, stages in the LDS ring.
 struct LdsPreset {
-  int nw, mt, rt, ch, ns, np;
+  int wr, wm, r, t, ns;
 };
 int lds_preset_count();
 LdsPreset lds_preset(int i);
-// LDS of configuration i (its stages of units and index blocks)
-int64_t lds_tile_bytes(int i, int32_t wdtype);
+// LDS of configuration i (its ring of stages) for weights of wdtype and bf16
+// activations, or e4m3 activation codes (a8)
+int64_t lds_tile_bytes(int i, int32_t wdtype, bool a8);
+// copies each wave issues per stage (they must fit the wait counter)
+int lds_tile_copies(int i, int32_t wdtype, bool a8);
 hipError_t launch_linear_tile(const LayerDesc& d, const LinearArgs& a, const LinearPlan& p, hipStream_t s);
 
 // Blocked configurations of linear_stream_kernel for batches above 16 rows:

@@ -558,24 +558,9 @@ __device__ __forceinline__ void stream_body(const LayerDesc& d, const LinearArgs
   int& last_flag = *last_flag_p;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // Workgroups are dealt to the 8 XCDs round-robin.  With several m-groups the
-  // order is remapped so that each XCD takes a contiguous run of logical ids,
-  // m-group fastest: the m-groups that share a weight slice run on one XCD at
-  // about the same time, and all but the first read it from that XCD's L2.
-  int b = block;
-  if (p.xcd_remap) b = (b % 8) * (grid / 8) + b / 8;
-  // logical id = (s * rgroups + rg) * mgroups + mg; one m-group or one split
-  // (every decode launch) skips its division
   const int S = p.splits;
-  int mg = 0, rg = b, s = 0;
-  if (p.mgroups > 1) {
-    mg = (int)((uint32_t)b % (uint32_t)p.mgroups);
-    rg = (int)((uint32_t)b / (uint32_t)p.mgroups);
-  }
-  if (S > 1) {
-    s = (int)((uint32_t)rg / (uint32_t)p.rgroups);
-    rg = (int)((uint32_t)rg % (uint32_t)p.rgroups);
-  }
+  int s, rg, mg;
+  tile_coords(block, grid, p, s, rg, mg);
   const int64_t rt0 = ((int64_t)rg * NW + wave) * NR;
   int ms0, ms1, md0, md1;
   split_range(d.n_sm, s, S, ms0, ms1);

@@ -319,7 +319,7 @@ def test_tile_presets(wdtype, dense, monkeypatch):
         sdg.spense_free(h)
 
 
-LDS_PRESETS = list(range(7))
+LDS_PRESETS = list(range(8))
 
 
 @pytest.mark.parametrize("wdtype", [DT_FP8, DT_BF16])

@@ -151,7 +151,7 @@ def test_w8a8_lds_tile_presets(dense, monkeypatch):
         for M in (17, 40, 64, 130, 300):
             q, sx = oracle.quantize_tokens_ref(X[:M], DT_BF16)
             Yref, B = oracle.linear_w8a8_ref(q, sx, ref, s)
-            for v in range(7):
+            for v in range(8):
                 monkeypatch.setenv("SPENSE_LDS", str(v))
                 for sp in (0, 1, 3):
                     Y = _w8a8_dev(h, Xd[:M], N, splits=sp).cpu().numpy()
