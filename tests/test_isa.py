@@ -106,10 +106,17 @@ def test_main_loops_keep_loads_in_flight(gfx950_asm):
         if not main or not main["vm"]:
             continue
         checked += 1
-        # the LDS-staged kernel consumes a unit-step's activations while the
-        # next step's (two loads per m-tile at least) are still in flight
-        least = 2 if "linear_tile" in name else 4
-        assert min(main["vm"]) >= least, (name[:90], sorted(set(main["vm"])))
+        if "linear_tile" in name:
+            # the LDS-staged kernel waits once per stage, for its own copies of
+            # that stage only: the copies of the NS - 2 later stages stay in
+            # flight (none with a two-stage ring)
+            m = re.search(r"I([ht])Lb([01])ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELi(\d+)ELb[01]E", name)
+            wt, a8, wr, wm, r, t, ns = m.group(1), int(m.group(2)), *map(int, m.groups()[2:])
+            nwv = wr * wm
+            copies = (wr * r // nwv) * (2 if wt == "h" else 3) + (wm * t // nwv) * (2 if a8 else 4)
+            assert set(main["vm"]) == {(ns - 2) * copies}, (name[:90], sorted(set(main["vm"])))
+        else:
+            assert min(main["vm"]) >= 4, (name[:90], sorted(set(main["vm"])))
     assert checked > 40
 
 
@@ -141,11 +148,12 @@ def test_weights_read_once_stream_non_temporally(gfx950_asm):
             assert loads and all(x.rstrip().endswith(" nt") for x in loads), (name[:90], loads[:3])
             seen["decode"] += 1
         elif "linear_tile" in name:
-            # the weight units go to LDS from the producer waves' own loop
+            # weight units and index blocks are copied into LDS with the
+            # non-temporal hint in the one-m-group build, activations never
             loads = [x for x in body.splitlines() if re.search(r"\sbuffer_load_dword\S*\s.*\slds\b", x)]
             nt = [x for x in loads if re.search(r"\snt\b", x)]
             if "Lb1EEEv" in name:
-                assert loads and len(nt) == len(loads), name[:90]
+                assert loads and nt and len(nt) < len(loads), name[:90]
                 seen["nt"] += 1
             else:
                 assert loads and not nt, (name[:90], nt[:3])
