@@ -383,3 +383,35 @@ def test_lds_tile_equals_streaming_bitwise_on_one_split():
         assert torch.equal(y_lds, y_str)
     finally:
         sdg.spense_free(h)
+
+
+@pytest.mark.parametrize("kernel", [("SPENSE_TILE", "0"), ("SPENSE_LDS", "4")])
+def test_workgroup_order_blocks_bitwise(kernel, monkeypatch):
+    """The workgroup order with several m-groups (blocks of row groups, one
+    m-group at a time) only decides which workgroup computes which tile: every
+    block size, including blocks that do not divide the row groups and a last
+    partial block, gives the same output bit for bit, with one split and with
+    several, and within tolerance of the oracle."""
+    N, K = 648, 1024  # 40.5 row tiles: several row groups of either kernel, the last one partial
+    W, s = _small(N, K, DT_FP8, 41)
+    sd = to_dev(s, DT_F32)
+    D = synth.random_dense_set(K, 256, 42)
+    h = pack_dev(to_dev(W, DT_FP8), DT_FP8, sd, dense_cols=D)
+    try:
+        X = synth.make_x(300, K, DT_BF16, np.random.default_rng(43))
+        Xd = to_dev(X, DT_BF16)
+        ref = oracle_pack_rows(W, DT_FP8, D)
+        monkeypatch.setenv(*kernel)
+        for M in (100, 300):
+            Yref, B = oracle.linear_ref(X[:M], DT_BF16, ref, s)
+            for sp in (1, 3):
+                ys = []
+                for rb in ("1", "2", "3", "4", "5", "16"):
+                    monkeypatch.setenv("SPENSE_RBLOCK", rb)
+                    ys.append(linear_dev(h, Xd[:M], N, splits=sp))
+                for y in ys[1:]:
+                    assert torch.equal(y, ys[0]), (kernel, M, sp)
+                assert tol_ratio(ys[0].cpu().numpy(), Yref, B) <= 1.0, (kernel, M, sp)
+        log(f"[workgroup order] {kernel}: block sizes 1-5, 16 bitwise equal")
+    finally:
+        sdg.spense_free(h)
