@@ -91,6 +91,15 @@ __device__ __forceinline__ void copy4(const i32x4& r, uint32_t lds, uint32_t vof
     asm volatile("buffer_load_dword %0, %1, %2 offen lds" ::"v"(voff), "s"(r), "s"(soff), "{m0}"(lds) : "memory");
 }
 
+// f(integral_constant<A>), ..., f(integral_constant<B - 1>), in order
+template <int A, int B, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (A < B) {
+    f(std::integral_constant<int, A>{});
+    static_for<A + 1, B>(f);
+  }
+}
+
 template <typename WT, bool A8, int WR, int WM, int R, int T>
 struct TileShape {
   static constexpr int NWV = WR * WM;                       // waves per workgroup
@@ -173,40 +182,44 @@ __global__ __launch_bounds__(WR * WM * 64) void linear_tile_kernel(LayerDesc d, 
   // 128 (ms0 + k), dense unit 2 md0 + k - ns at K_sp + 64 (2 md0 + k - ns)
   const uint32_t s_col = (uint32_t)(128 * ms0) * XB, d_col = (uint32_t)(d.K_sp + 128 * md0 - 64 * ns) * XB;
 
-  auto issue = [&](int k, uint8_t* buf) __attribute__((always_inline)) {
+  // Copy number i (0 .. kCopies - 1, a compile-time index) of this wave's
+  // share of unit-step k into buf: first its weight units (each unit's 1 KB
+  // pieces, then its index block), then its m-tiles' activation blocks.
+  constexpr int kWC = S_::kWU * (int)(UB / 1024 + 1);  // weight copies per wave and stage
+  auto issue_one = [&](int k, uint8_t* buf, auto ic) __attribute__((always_inline)) {
+    constexpr int i = decltype(ic)::value;
     const bool in = k < total, sp = k < ns;
-#pragma unroll
-    for (int i = 0; i < S_::kWU; ++i) {
-      const int r = wave + NWV * i;
-      const uint32_t uoff = in ? (uint32_t)r * tb + (sp ? s_unit0 : d_unit0) + (uint32_t)k * UB : kOutOfRange;
-      const uint32_t ioff = in && sp ? (uint32_t)r * tb + s_idx0 + (uint32_t)k * 256u : kOutOfRange;
-#pragma unroll
-      for (int h = 0; h < (int)(UB / 1024); ++h)
-        copy16<NTW>(wres, lds_addr(buf + r * RS + 1024 * h), 16 * lane, uoff + 1024u * h);
-      copy4<NTW>(wres, lds_addr(buf + r * RS + UB), 4 * lane, ioff);
-    }
-    const uint32_t col = !in ? kOutOfRange : sp ? s_col + (uint32_t)(128 * XB) * k : d_col + (uint32_t)(64 * XB) * k;
-    const uint32_t xl = sp ? xl_s : xl_d;
-#pragma unroll
-    for (int i = 0; i < S_::kXT; ++i) {
-      const int t = wave + NWV * i;
-      uint8_t* xb = buf + S_::kX + t * XU;
-      const uint32_t v = (uint32_t)t * xtile + xl;
-      if constexpr (A8) {
-#pragma unroll
-        for (int rh = 0; rh < 2; ++rh) copy16<false>(xres, lds_addr(xb + 1024 * rh), v + xhalf * rh, col);
+    if constexpr (i < kWC) {
+      constexpr int iu = i / (int)(UB / 1024 + 1), part = i % (int)(UB / 1024 + 1);
+      const int r = wave + NWV * iu;
+      if constexpr (part < (int)(UB / 1024)) {
+        const uint32_t uoff = in ? (uint32_t)r * tb + (sp ? s_unit0 : d_unit0) + (uint32_t)k * UB : kOutOfRange;
+        copy16<NTW>(wres, lds_addr(buf + r * RS + 1024 * part), 16 * lane, uoff + 1024u * part);
       } else {
-        // a dense unit uses its one 64-column step for both products: its
-        // second step's blocks take the same columns (so that the reads of a
-        // stage have fixed LDS offsets)
-        const uint32_t col1 = !in ? kOutOfRange : sp ? col + 128u : col;
-#pragma unroll
-        for (int rh = 0; rh < 2; ++rh) {
-          copy16<false>(xres, lds_addr(xb + 1024 * rh), v + xhalf * rh, col);
-          copy16<false>(xres, lds_addr(xb + 2048 + 1024 * rh), v + xhalf * rh, col1);
-        }
+        const uint32_t ioff = in && sp ? (uint32_t)r * tb + s_idx0 + (uint32_t)k * 256u : kOutOfRange;
+        copy4<NTW>(wres, lds_addr(buf + r * RS + UB), 4 * lane, ioff);
+      }
+    } else {
+      constexpr int jx = i - kWC, it = jx / S_::kXB, blk = jx % S_::kXB;
+      const int t = wave + NWV * it;
+      uint8_t* xb = buf + S_::kX + t * XU;
+      const uint32_t col = !in ? kOutOfRange : sp ? s_col + (uint32_t)(128 * XB) * k : d_col + (uint32_t)(64 * XB) * k;
+      const uint32_t v = (uint32_t)t * xtile + (sp ? xl_s : xl_d);
+      if constexpr (A8) {
+        copy16<false>(xres, lds_addr(xb + 1024 * blk), v + xhalf * blk, col);
+      } else {
+        // blocks (step q, row half rh) at 2048 q + 1024 rh; a dense unit uses
+        // its one 64-column step for both products: its second step's blocks
+        // take the same columns (so that the reads of a stage have fixed LDS
+        // offsets)
+        constexpr int q = blk & 1, rh = blk >> 1;
+        const uint32_t cq = q == 0 || !in ? col : sp ? col + 128u : col;
+        copy16<false>(xres, lds_addr(xb + 2048 * q + 1024 * rh), v + xhalf * rh, cq);
       }
     }
+  };
+  auto issue = [&](int k, uint8_t* buf) __attribute__((always_inline)) {
+    static_for<0, S_::kCopies>([&](auto ic) { issue_one(k, buf, ic); });
   };
 
   // this lane's two 16-byte fragment pieces within an m-tile's block pair:
@@ -222,14 +235,20 @@ __global__ __launch_bounds__(WR * WM * 64) void linear_tile_kernel(LayerDesc d, 
 #pragma unroll
   for (int i = 0; i < R * T; ++i) acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // products of the unit-step k staged in buf
-  auto consume = [&](const uint8_t* buf, int k) __attribute__((always_inline)) {
+  // Products of the unit-step k staged in buf, in groups (a row tile, or a
+  // row tile and step); after group g, between(g) issues the share of the
+  // next stage's copies that belongs to it, so that the copies are spread
+  // over the products instead of queueing at the stage's start.  Every LDS
+  // read of the stage is issued before the first copy (the copies are
+  // ordered with memory accesses and may not pass them).
+  constexpr int kGroups = A8 ? R : 2 * R;
+  auto consume = [&](const uint8_t* buf, int k, auto&& between) __attribute__((always_inline)) {
     const bool sp = k < ns;
     const uint8_t* Wb = buf + (wr * R) * RS + 16 * lane;
     const uint8_t* Ib = buf + (wr * R) * RS + UB + 4 * lane;
     const uint8_t* Xb = buf + S_::kX + (wm * T) * XU;
     // index words are read for dense units too (their blocks hold zeros) and
-    // replaced by the dense word, so a stage's reads do not depend on its kind.
+    // replaced by the dense word, so a stage's reads do not depend on its kind
     int idx[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
@@ -238,6 +257,7 @@ __global__ __launch_bounds__(WR * WM * 64) void linear_tile_kernel(LayerDesc d, 
     }
     if constexpr (A8) {
       i32x8 B[T];
+      u32x4 A[R];
 #pragma unroll
       for (int t = 0; t < T; ++t) {
         // the instruction pairs byte quarters (0, 2, 1, 3) of the 32 codes
@@ -245,36 +265,43 @@ __global__ __launch_bounds__(WR * WM * 64) void linear_tile_kernel(LayerDesc d, 
         B[t] = __builtin_shufflevector(lo, hi, 0, 1, 4, 5, 2, 3, 6, 7);
       }
 #pragma unroll
-      for (int r = 0; r < R; ++r) {
-        const u32x4 A = *(const u32x4*)(Wb + r * RS);
+      for (int r = 0; r < R; ++r) A[r] = *(const u32x4*)(Wb + r * RS);
+      static_for<0, kGroups>([&](auto gc) {
+        constexpr int r = decltype(gc)::value;
 #pragma unroll
-        for (int t = 0; t < T; ++t) acc[r * T + t] = smfmac_fp8(A, B[t], acc[r * T + t], idx[r]);
-      }
+        for (int t = 0; t < T; ++t) acc[r * T + t] = smfmac_fp8(A[r], B[t], acc[r * T + t], idx[r]);
+        between(gc);
+      });
     } else {
-      u32x4 w[R];
+      bf16x16 B[2][T];
+      u32x4 w[sizeof(WT) == 1 ? R : 2 * R];
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+          B[q][t] = as_bf16x16(*(const u32x4*)(Xb + t * XU + 2048 * q + xo0),
+                               *(const u32x4*)(Xb + t * XU + 2048 * q + xo1));
       if constexpr (sizeof(WT) == 1) {
 #pragma unroll
         for (int r = 0; r < R; ++r) w[r] = *(const u32x4*)(Wb + r * RS);
-      }
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const uint32_t xq = 2048u * q;
-        bf16x16 B[T];
-#pragma unroll
-        for (int t = 0; t < T; ++t)
-          B[t] = as_bf16x16(*(const u32x4*)(Xb + t * XU + xq + xo0), *(const u32x4*)(Xb + t * XU + xq + xo1));
+      } else {
 #pragma unroll
         for (int r = 0; r < R; ++r) {
-          bf16x8 A;
-          if constexpr (sizeof(WT) == 1) A = q == 0 ? fp8x8_to_bf16(w[r].x, w[r].y) : fp8x8_to_bf16(w[r].z, w[r].w);
-          else A = as_bf16x8(*(const u32x4*)(Wb + r * RS + 1024 * q));
-#pragma unroll
-          for (int t = 0; t < T; ++t) {
-            if (q == 0) acc[r * T + t] = smfmac_bf16<0>(A, B[t], acc[r * T + t], idx[r]);
-            else acc[r * T + t] = smfmac_bf16<1>(A, B[t], acc[r * T + t], idx[r]);
-          }
+          w[2 * r] = *(const u32x4*)(Wb + r * RS);
+          w[2 * r + 1] = *(const u32x4*)(Wb + r * RS + 1024);
         }
       }
+      // group g: step q = g / R of row tile r = g % R (both steps of a row
+      // tile add into its accumulators in the order q = 0, 1)
+      static_for<0, kGroups>([&](auto gc) {
+        constexpr int g = decltype(gc)::value, q = g / R, r = g % R;
+        bf16x8 A;
+        if constexpr (sizeof(WT) == 1) A = q == 0 ? fp8x8_to_bf16(w[r].x, w[r].y) : fp8x8_to_bf16(w[r].z, w[r].w);
+        else A = as_bf16x8(w[2 * r + q]);
+#pragma unroll
+        for (int t = 0; t < T; ++t) acc[r * T + t] = smfmac_bf16<q>(A, B[q][t], acc[r * T + t], idx[r]);
+        between(gc);
+      });
     }
   };
 
@@ -291,8 +318,13 @@ __global__ __launch_bounds__(WR * WM * 64) void linear_tile_kernel(LayerDesc d, 
       // the barrier stage c is complete and buffer (c - 1) % NS is free
       __builtin_amdgcn_s_waitcnt((int)((kWait & 15) | ((kWait >> 4) << 14) | (7 << 4) | (0 << 8)));
       barrier_no_fence();
-      issue(c + NS - 1, bufs[(j + NS - 1) % NS]);
-      consume(bufs[j], c);
+      uint8_t* nb = bufs[(j + NS - 1) % NS];
+      consume(bufs[j], c, [&](auto gc) __attribute__((always_inline)) {
+        constexpr int g = decltype(gc)::value;
+        static_for<g * S_::kCopies / kGroups, (g + 1) * S_::kCopies / kGroups>(
+            [&](auto ic) { issue_one(c + NS - 1, nb, ic); });
+        __builtin_amdgcn_sched_barrier(0);
+      });
     }
   }
   SPENSE_WAIT_VM(0);
