@@ -550,8 +550,17 @@ static int plan_linear(const spense_layer* h, int64_t M, int32_t splits, int64_t
   // More than 16 rows, one layer per launch, on request: weight units and
   // activation fragments both staged through LDS, each wave multiplying a
   // block of row tiles by a block of m-tiles (linear_tile_kernel).
-  if (NT_fill == d.NT && lds_enabled() && lds_forced() < lds_preset_count()) {
-    const int pre = lds_forced();
+  // Without a request the planner takes it where it measured faster than the
+  // streaming kernels: e4m3 weights, 64 < M <= 256, and at least 3200 row
+  // tiles (the gate/up projections of the 32B- and 36B-class layers; 36B-class
+  // 55296 x 5120: M = 128 72.1 vs 77.8 us with bf16 activations and 60.7 vs
+  // 73.3 us with e4m3 codes, M = 256 132 vs 138 / 107 vs 110 us).  Layers with
+  // fewer row tiles, and smaller or larger batches, ran slower on it.
+  const char* tile_forced = std::getenv("SPENSE_TILE");
+  const bool lds_auto = !lds_enabled() && !(tile_forced && *tile_forced) && d.wdtype == DT_FP8 && M > 64 &&
+                        M <= 256 && d.NT >= 3200;
+  if (NT_fill == d.NT && (lds_auto || (lds_enabled() && lds_forced() < lds_preset_count()))) {
+    const int pre = lds_auto ? (xbytes == 1 ? 5 : 4) : lds_forced();
     const LdsPreset c = lds_preset(pre);
     const bool a8 = xbytes == 1;
     const int64_t rt = (int64_t)c.wr * c.r, mg = (int64_t)c.wm * c.t;
@@ -572,11 +581,24 @@ static int plan_linear(const spense_layer* h, int64_t M, int32_t splits, int64_t
       p.lds_bytes = (int)lds;
       int64_t S = splits;
       if (S == 0) {
+        // as for the streaming kernels: splits to fill the CUs when the tiles
+        // alone do not, fp32 partials below two thirds of the packed weight
+        // bytes, and of those split counts the one with the least work on the
+        // busiest CU (rounds of resident workgroups, each K / S long)
         const int64_t units = (int64_t)p.rgroups * p.mgroups;
-        const int64_t per_cu = std::max<int64_t>(1, kLdsPerCU / lds);
-        const int64_t resident = kCUs * per_cu;
+        const int64_t resident = kCUs * std::max<int64_t>(1, kLdsPerCU / lds);
         S = units >= resident / 2 ? 1 : std::max<int64_t>(1, std::min<int64_t>(resident / units, max_splits));
-        S = std::max<int64_t>(1, std::min<int64_t>(S, d.tile_bytes / (256 * M)));
+        S = std::max<int64_t>(1, std::min<int64_t>(S, d.tile_bytes / (192 * M)));
+        int64_t best = 1;
+        double best_cost = 1e30;
+        for (int64_t sc = 1; sc <= S; ++sc) {
+          const double cost = (double)((units * sc + resident - 1) / resident) / (double)sc;
+          if (cost < best_cost * (1 - 1e-9)) {
+            best_cost = cost;
+            best = sc;
+          }
+        }
+        S = best;
       }
       if (S > 1 && S * M * d.NT * 64 >= (int64_t(1) << 31)) {
         if (splits != 0) return SPENSE_EUNSUPPORTED;
