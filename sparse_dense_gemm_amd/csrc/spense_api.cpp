@@ -736,9 +736,11 @@ static int plan_linear(const spense_layer* h, int64_t M, int32_t splits, int64_t
   const int64_t grid = (int64_t)p.rgroups * p.mgroups * S;
   p.xcd_remap = (p.mgroups > 1 && grid % 8 == 0) ? 1 : 0;  // decided per layer (the remap stays inside it)
   if (const char* x = std::getenv("SPENSE_XCD")) p.xcd_remap = (std::atoi(x) != 0 && grid % 8 == 0) ? 1 : 0;
-  // blocks of four row groups when several m-groups share the weights (the
-  // 36B-class e4m3 set at M = 2048: 1931 -> 1837 us; no change at M = 128)
-  p.rblock = p.mgroups > 1 ? rblock_choice(4) : 1;
+  // blocks of four row groups when eight or more m-groups share the weights
+  // (the 36B-class e4m3 set at M = 2048, 32 m-groups: 1931 -> 1837 us, HBM
+  // bytes 5.85 -> 4.07 GB per pass; at M = 128, four m-groups, the blocks
+  // read about 20% more bytes for the same time)
+  p.rblock = p.mgroups >= 8 ? rblock_choice(4) : 1;
   return SPENSE_OK;
 }
 

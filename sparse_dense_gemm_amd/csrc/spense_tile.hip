@@ -18,15 +18,16 @@
 // copy of 64 lanes lands as one contiguous 1 KB block and a wave reads it back
 // without bank conflicts).  Every wave issues the same copies per stage
 // (buffer loads with an LDS destination): its share of the weight units and
-// of the m-tiles.  The ring has NS stage buffers, declared as separate arrays
-// and indexed with compile-time constants (the loop is unrolled by NS), so
-// that the compiler's waits before an LDS read cover only the copies into
-// that buffer; NS - 1 stages are in flight.  One barrier per stage: before
-// it each wave waits for its own copies of the stage (the copies of the
-// later stages stay in flight) and for its LDS reads of the previous stage;
-// after it the stage is complete in LDS and the previous stage's buffer may
-// be refilled.  Each weight byte fetched into the CU feeds 16 MG tokens and
-// each activation byte 16 RT output rows.
+// of the m-tiles, spread over the product groups of the stage before.  The
+// ring has NS stage buffers, declared as separate arrays and indexed with
+// compile-time constants (the loop is unrolled by NS); NS - 1 stages are in
+// flight.  The copies are assembly that the compiler does not track, so the
+// kernel counts them itself.  One barrier per stage: before it each wave
+// waits for its own copies of the stage (the copies of the later stages stay
+// in flight) and for its LDS reads of the previous stage; after it the stage
+// is complete in LDS and the previous stage's buffer may be refilled.  Each
+// weight byte fetched into the CU feeds 16 MG tokens and each activation byte
+// 16 RT output rows.
 //
 // Activations are read from the contiguous X'p (gathered or quantised
 // beforehand for a chosen dense set).  Every copy is issued unconditionally:
